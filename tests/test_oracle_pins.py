@@ -1,0 +1,401 @@
+"""Pins of the float64 oracle to things other than itself (CPU only).
+
+Each test checks the oracle against what the pages and the mathematics fix: brute
+force on tiny inputs, torch's float64 SDPA (an independent implementation of the same
+definition), closed forms, invariances, torch's own float8 decode, the OCP MX E2M1
+table and quantisation error bounds.  ``test_pins_catch_planted_mistakes`` plants
+plausible mistakes in copies of the oracle's attention and checks that a pin fails.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+# ----------------------------------------------------------------------------------
+# number formats
+# ----------------------------------------------------------------------------------
+
+def test_e4m3_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.decode_e4m3fn(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    assert np.array_equal(np.signbit(ours[fin]), np.signbit(ref[fin]))
+    assert np.nanmax(ours) == 448.0
+
+
+def test_e2m1_matches_ocp_table():
+    rows = [ln.split() for ln in open(os.path.join(GOLDEN, "e2m1_ocp_mx.txt")) if ln[0] != "#"]
+    table = {int(a): float(b) for a, b in rows}
+    ours = oracle.decode_e2m1(np.arange(16))
+    for c in range(16):
+        assert ours[c] == table[c], c
+        assert np.signbit(ours[c]) == np.signbit(table[c]), c
+
+
+def test_bf16_bits_decode_matches_torch():
+    rng = np.random.default_rng(5)
+    bits = rng.integers(0, 1 << 16, size=4096, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.decode_bf16_bits(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    same = (ours == ref) | (np.isnan(ours) & np.isnan(ref))
+    assert same.all()
+
+
+def test_nvfp4_products_exact_in_bf16():
+    """Every E2M1 value times every finite E4M3 scale is exactly a bf16 value, so a
+    bf16 tile holds the dequantised NVFP4 cache without rounding."""
+    v = oracle.decode_e2m1(np.arange(16))
+    s = oracle.decode_e4m3fn(np.arange(256, dtype=np.uint8))
+    s = s[np.isfinite(s)]
+    prod = (v[:, None] * s[None, :]).ravel()
+    back = torch.from_numpy(prod).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(back, prod)
+
+
+def test_fp8_values_exact_in_bf16():
+    s = oracle.decode_e4m3fn(np.arange(256, dtype=np.uint8))
+    s = s[np.isfinite(s)]
+    back = torch.from_numpy(s).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(back, s)
+
+
+def test_fp8_page_decode_within_quantisation_bound():
+    rng = np.random.default_rng(11)
+    P = 32
+    x = rng.standard_normal((P, oracle.ROW), dtype=np.float32)
+    scale = float(np.float32(np.abs(x).max()) / np.float32(448))
+    page = gen.encode_pages(x, gen.FMT_FP8, P, P * oracle.ROW, scale)[0]
+    dec = oracle.decode_page(page, oracle.FMT_FP8, P, scale)
+    # E4M3: relative half-ulp 2^-4 for normals, absolute 2^-10 below 2^-6
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale)
+    assert (np.abs(dec - x) <= bound * 1.0000001 + 1e-12).all()
+    # codes come from torch's cast, so the decode must equal torch's decode exactly
+    ref = torch.from_numpy(page[:P * oracle.ROW].copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(dec.ravel(), scale * ref)
+
+
+def test_nvfp4_page_decode_within_quantisation_bound():
+    """The generator's encoder writes the reading of the NVFP4 page independently of the
+    oracle's decoder; a wrong nibble order, group or section offset in either breaks the
+    E2M1 error bound |x - deq| <= s_g (largest grid gap 2, times half, plus saturation)."""
+    rng = np.random.default_rng(12)
+    P = 16
+    x = rng.standard_normal((P, oracle.ROW), dtype=np.float32)
+    stride = P * (oracle.ROW // 2 + oracle.ROW // 16)
+    page = gen.encode_pages(x, gen.FMT_NVFP4, P, stride, 1.0)[0]
+    dec = oracle.decode_page(page, oracle.FMT_NVFP4, P)
+    sc = oracle.decode_e4m3fn(page[P * 288:P * 324].reshape(P, 36))
+    bound = np.repeat(sc, 16, axis=1)
+    assert (np.abs(dec - x) <= bound + 1e-12).all()
+    # and the decode is far better than the bound on average
+    assert np.mean(np.abs(dec - x) / bound) < 0.3
+
+
+# ----------------------------------------------------------------------------------
+# attention: brute force, library routine, closed forms
+# ----------------------------------------------------------------------------------
+
+def brute_force_attend(qfull, kv, visible, sm_scale):
+    """Pure-Python loops over the definition (no numpy reductions)."""
+    R, n = len(qfull), len(kv)
+    O = [[0.0] * 512 for _ in range(R)]
+    L = [-math.inf] * R
+    for r in range(R):
+        v = min(max(int(visible[r]), 0), n)
+        if v == 0:
+            continue
+        s = []
+        for t in range(v):
+            acc = 0.0
+            for d in range(576):
+                acc += float(qfull[r][d]) * float(kv[t][d])
+            s.append(sm_scale * acc)
+        m = max(s)
+        z = sum(math.exp(x - m) for x in s)
+        L[r] = m + math.log(z)
+        for t in range(v):
+            w = math.exp(s[t] - L[r])
+            for d in range(512):
+                O[r][d] += w * float(kv[t][d])
+    return np.array(O), np.array(L)
+
+
+def test_attend_matches_brute_force():
+    rng = np.random.default_rng(1)
+    qf = _rand(rng, 3, 576)
+    kv = _rand(rng, 23, 576)
+    vis = np.array([23, 7, 1])
+    O, L = oracle.attend(qf, kv, vis, 0.07)
+    Ob, Lb = brute_force_attend(qf, kv, vis, 0.07)
+    assert np.abs(O - Ob).max() < 1e-12
+    assert np.abs(L - Lb).max() < 1e-12
+
+
+def sdpa_reference(qfull, kv, visible, sm_scale):
+    q = torch.from_numpy(qfull)[None, None]           # [1,1,R,576]
+    k = torch.from_numpy(kv)[None, None]              # [1,1,n,576]
+    v = torch.from_numpy(kv[:, :512].copy())[None, None]
+    mask = torch.arange(kv.shape[0])[None, :] < torch.from_numpy(np.asarray(visible))[:, None]
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=sm_scale)
+    scores = (q @ k.transpose(-1, -2))[0, 0] * sm_scale
+    lse = torch.logsumexp(scores.masked_fill(~mask, -math.inf), dim=-1)
+    return o[0, 0].numpy(), lse.numpy()
+
+
+def _attend_vs_sdpa(attend_fn, seed=2):
+    rng = np.random.default_rng(seed)
+    qf = _rand(rng, 8, 576)
+    kv = _rand(rng, 300, 576)
+    vis = np.array([300, 299, 150, 1, 64, 65, 2, 300])
+    O, L = attend_fn(qf, kv, vis, 1.0 / math.sqrt(192))
+    Or, Lr = sdpa_reference(qf, kv, vis, 1.0 / math.sqrt(192))
+    return max(np.abs(O - Or).max(), np.abs(L - Lr).max())
+
+
+def test_attend_matches_torch_sdpa_float64():
+    assert _attend_vs_sdpa(oracle.attend) < 1e-10
+
+
+def test_closed_form_zero_query_is_mean():
+    rng = np.random.default_rng(3)
+    kv = _rand(rng, 100, 576)
+    qf = np.zeros((2, 576))
+    O, L = oracle.attend(qf, kv, np.array([100, 37]), 0.1)
+    assert np.abs(O[0] - kv[:100, :512].mean(0)).max() < 1e-13
+    assert np.abs(O[1] - kv[:37, :512].mean(0)).max() < 1e-13
+    assert abs(L[0] - math.log(100)) < 1e-13 and abs(L[1] - math.log(37)) < 1e-13
+    # sm_scale = 0 gives the same with any query
+    O2, L2 = oracle.attend(_rand(rng, 2, 576), kv, np.array([100, 37]), 0.0)
+    assert np.abs(O2 - O).max() < 1e-13 and np.abs(L2 - L).max() < 1e-13
+
+
+def test_closed_form_single_token_and_dominant_token():
+    rng = np.random.default_rng(4)
+    kv = _rand(rng, 50, 576)
+    qf = _rand(rng, 1, 576)
+    O, L = oracle.attend(qf, kv, np.array([1]), 0.3)
+    assert np.array_equal(O[0], kv[0, :512])
+    assert abs(L[0] - 0.3 * float(qf[0] @ kv[0])) < 1e-12
+    tstar = 17
+    qd = (40.0 * kv[tstar])[None]
+    Od, _ = oracle.attend(qd, kv, np.array([50]), 1.0)
+    assert np.abs(Od[0] - kv[tstar, :512]).max() < 1e-9
+
+
+def test_empty_rows():
+    kv = np.ones((5, 576))
+    O, L = oracle.attend(np.ones((2, 576)), kv, np.array([0, -3]), 1.0)
+    assert (O == 0).all() and np.isneginf(L).all()
+    O, L = oracle.attend(np.ones((2, 576)), np.zeros((0, 576)), np.array([0, 0]), 1.0)
+    assert (O == 0).all() and np.isneginf(L).all()
+
+
+# ----------------------------------------------------------------------------------
+# split-KV: invariance and merge identity
+# ----------------------------------------------------------------------------------
+
+def test_split_invariance_contig():
+    rng = np.random.default_rng(6)
+    B, H, S = 2, 4, 300
+    q, qpe = _rand(rng, B, H, 512), _rand(rng, B, H, 64)
+    kv, kpe = _rand(rng, B, S, 512), _rand(rng, B, S, 64)
+    O, L = oracle.contig_decode(q, qpe, kv, kpe, 0.05)
+    for Ls in (1, 7, 64, 128, S):
+        op, lp = oracle.contig_decode_splitkv(q, qpe, kv, kpe, 0.05, Ls)
+        assert op.shape == (B, H, oracle.cdiv(S, Ls), 512)
+        Oc, Lc = oracle.combine(op.reshape(B * H, -1, 512), lp.reshape(B * H, -1))
+        assert np.abs(Oc.reshape(B, H, 512) - O).max() < 1e-12, Ls
+        assert np.abs(Lc.reshape(B, H) - L).max() < 1e-12, Ls
+
+
+def test_lse_merge_identity():
+    rng = np.random.default_rng(7)
+    qf = _rand(rng, 3, 576)
+    kv = _rand(rng, 90, 576)
+    vis = np.full(3, 90)
+    for a, b in ((0, 90), (13, 90), (0, 1), (45, 46)):
+        oa, la = oracle.attend_range(qf, kv, vis, 0.2, 0, a)
+        ob, lb = oracle.attend_range(qf, kv, vis, 0.2, a, b)
+        oab, lab = oracle.attend_range(qf, kv, vis, 0.2, 0, b)
+        Om, Lm = oracle.combine(np.stack([oa, ob], 1), np.stack([la, lb], 1))
+        assert np.abs(Om - oab).max() < 1e-12 and np.abs(Lm - lab).max() < 1e-12
+    # an empty part (lse = -inf, O = 0) is the identity
+    o1, l1 = oracle.attend_range(qf, kv, vis, 0.2, 0, 90)
+    Om, Lm = oracle.combine(np.stack([o1, np.zeros_like(o1)], 1), np.stack([l1, np.full(3, -np.inf)], 1))
+    assert np.array_equal(Om, o1) and np.array_equal(Lm, l1)
+    # all parts empty -> O = 0, LSE = -inf
+    Oe, Le = oracle.combine(np.zeros((2, 3, 512)), np.full((2, 3), -np.inf))
+    assert (Oe == 0).all() and np.isneginf(Le).all()
+
+
+# ----------------------------------------------------------------------------------
+# paged: gather, permutation invariance, causal verify
+# ----------------------------------------------------------------------------------
+
+def test_paged_equals_contig_on_same_rows():
+    """A bf16 page pool holding the contiguous rows in a shuffled page order gives the
+    same result as the contiguous op: pins the gather (page = table[t // P], row t % P)."""
+    rng = np.random.default_rng(8)
+    B, H, S, P = 2, 4, 200, 32
+    c = gen.make_contig(B, H, S, seed=99)
+    q, qpe, kv, kpe = c.f64()
+    O, L = oracle.contig_decode(q, qpe, kv, kpe, 0.1)
+    npg = oracle.cdiv(S, P)
+    perm = rng.permutation(B * npg)
+    stride = P * 1152
+    cache = np.zeros((B * npg, stride), np.uint8)
+    rows = np.concatenate([c.kv, c.kpe], axis=-1)  # bf16 bits [B,S,576]
+    bt = np.zeros((B, npg), np.int32)
+    for b in range(B):
+        for i in range(npg):
+            blk = np.zeros((P, 576), np.uint16)
+            part = rows[b, i * P:(i + 1) * P]
+            blk[:len(part)] = part
+            cache[perm[b * npg + i]] = blk.view(np.uint8).ravel()
+            bt[b, i] = perm[b * npg + i]
+    Op, Lp = oracle.paged_decode(q[:, None], qpe[:, None], cache.ravel(), oracle.FMT_BF16, 1.0, P, stride, bt,
+                                 np.full(B, S), 0.1)
+    assert np.array_equal(Op[:, 0], O) and np.array_equal(Lp[:, 0], L)
+
+
+def test_page_permutation_invariance():
+    w = gen.make_paged(B=3, H=4, q_len=2, lo=70, hi=300, page_size=32, fmt=gen.FMT_FP8, seed=21)
+    q, qpe = w.q_f64()
+    O, L = oracle.paged_decode(q, qpe, w.cache, w.fmt, w.kv_scale, w.page_size, w.page_stride,
+                               w.block_tables, w.seq_lens, w.sm_scale)
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(w.num_pages)
+    pages = w.cache.reshape(w.num_pages, w.page_stride)
+    moved = np.empty_like(pages)
+    moved[perm] = pages
+    bt2 = perm[w.block_tables]
+    O2, L2 = oracle.paged_decode(q, qpe, moved.ravel(), w.fmt, w.kv_scale, w.page_size, w.page_stride,
+                                 bt2, w.seq_lens, w.sm_scale)
+    assert np.array_equal(O, O2) and np.array_equal(L, L2)
+    assert np.isfinite(O).all()
+
+
+def test_causal_verify_rows():
+    """q_len = 2: query 0 sees n-1 tokens and equals a one-token decode over n-1 tokens;
+    query 1 sees all n; zero queries give ln(n-1) and ln(n)."""
+    w = gen.make_paged(B=2, H=4, q_len=2, lo=65, hi=130, page_size=64, fmt=gen.FMT_BF16, seed=22)
+    q, qpe = w.q_f64()
+    O, L = oracle.paged_decode(q, qpe, w.cache, w.fmt, 1.0, w.page_size, w.page_stride,
+                               w.block_tables, w.seq_lens, w.sm_scale)
+    for b in range(2):
+        n = int(w.seq_lens[b])
+        o0, l0 = oracle.paged_decode_request(q[b, :1], qpe[b, :1], w.cache, w.fmt, 1.0, w.page_size,
+                                             w.page_stride, w.block_tables[b], n - 1, w.sm_scale)
+        assert np.array_equal(o0[0], O[b, 0]) and np.array_equal(l0[0], L[b, 0])
+    Oz, Lz = oracle.paged_decode(np.zeros_like(q), np.zeros_like(qpe), w.cache, w.fmt, 1.0, w.page_size,
+                                 w.page_stride, w.block_tables, w.seq_lens, w.sm_scale)
+    for b in range(2):
+        n = int(w.seq_lens[b])
+        assert np.abs(Lz[b, 0] - math.log(n - 1)).max() < 1e-12
+        assert np.abs(Lz[b, 1] - math.log(n)).max() < 1e-12
+
+
+def test_seq_len_below_q_len_gives_empty_row():
+    w = gen.make_paged(B=2, H=2, q_len=2, lo=1, hi=1, page_size=32, fmt=gen.FMT_BF16, seed=23,
+                       seq_lens=[1, 0])
+    q, qpe = w.q_f64()
+    O, L = oracle.paged_decode(q, qpe, w.cache, w.fmt, 1.0, w.page_size, w.page_stride,
+                               w.block_tables, w.seq_lens, w.sm_scale)
+    assert np.isneginf(L[0, 0]).all() and (O[0, 0] == 0).all()
+    assert np.isfinite(L[0, 1]).all()
+    assert np.isneginf(L[1]).all() and (O[1] == 0).all()
+
+
+def test_poisoned_table_entries_are_never_read():
+    w = gen.make_paged(B=3, H=2, q_len=1, lo=40, hi=200, page_size=32, fmt=gen.FMT_NVFP4, seed=24,
+                       max_blocks=16, poison_tail=True)
+    q, qpe = w.q_f64()
+    O, L = oracle.paged_decode(q, qpe, w.cache, w.fmt, 1.0, w.page_size, w.page_stride,
+                               w.block_tables, w.seq_lens, w.sm_scale)
+    assert np.isfinite(O).all() and np.isfinite(L).all()
+    assert (w.block_tables == w.poison_page).any()
+
+
+# ----------------------------------------------------------------------------------
+# planner
+# ----------------------------------------------------------------------------------
+
+def test_next_power_of_2_definition():
+    assert oracle.next_power_of_2(0) == 1 and oracle.next_power_of_2(-5) == 1
+    for n in list(range(1, 5000)) + [2 ** 20 - 1, 2 ** 20, 2 ** 20 + 1]:
+        assert oracle.next_power_of_2(n) == 2 ** math.ceil(math.log2(n)), n
+
+
+def test_contig_planner_worked_examples():
+    rows = [ln.split() for ln in open(os.path.join(GOLDEN, "planner_tilegym.txt")) if ln[0] != "#"]
+    for cus, B, S, L, NS in (map(int, r) for r in rows):
+        assert oracle.plan_contig(cus, B, S) == (L, NS), (cus, B, S)
+
+
+def test_contig_planner_invariants():
+    for B in (1, 2, 3, 7, 64, 255, 256, 1000):
+        for S in (1, 127, 128, 129, 4096, 8191, 100000):
+            L, NS = oracle.plan_contig(256, B, S)
+            assert L >= 128 and L & (L - 1) == 0
+            assert (NS - 1) * L < S <= NS * L
+
+
+# ----------------------------------------------------------------------------------
+# planted mistakes: each must fail at least one pin
+# ----------------------------------------------------------------------------------
+
+def _mutant(kind):
+    def attend(qfull, kv, visible, sm_scale):
+        qfull = np.asarray(qfull, np.float64)
+        kv = np.asarray(kv, np.float64)
+        R, n = qfull.shape[0], kv.shape[0]
+        O = np.zeros((R, 512))
+        lse = np.full(R, -np.inf)
+        nope = qfull[:, :512] @ kv[:, :512].T
+        rope = qfull[:, 512:] @ kv[:, 512:].T
+        if kind == "drop_rope":
+            s = sm_scale * nope
+        elif kind == "rope_sign":
+            s = sm_scale * (nope - rope)
+        elif kind == "scale_sqrt":
+            s = math.sqrt(sm_scale) * (nope + rope)
+        else:
+            s = sm_scale * (nope + rope)
+        for r in range(R):
+            v = int(min(max(visible[r], 0), n))
+            if kind == "off_by_one_visible":
+                v = max(v - 1, 0)
+            if v == 0:
+                continue
+            sr = s[r, :v]
+            m = sr.max()
+            lse[r] = m + math.log(np.exp(sr - m).sum())
+            vals = kv[:v, 64:576] if kind == "v_from_wrong_columns" else kv[:v, :512]
+            O[r] = np.exp(sr - lse[r]) @ vals
+            if kind == "lse_base2":
+                lse[r] = lse[r] / math.log(2)
+        return O, lse
+    return attend
+
+
+@pytest.mark.parametrize("kind", ["drop_rope", "rope_sign", "scale_sqrt", "off_by_one_visible",
+                                  "v_from_wrong_columns", "lse_base2"])
+def test_pins_catch_planted_mistakes(kind):
+    assert _attend_vs_sdpa(_mutant("none")) < 1e-10
+    assert _attend_vs_sdpa(_mutant(kind)) > 1e-3
