@@ -1,0 +1,78 @@
+// Internal interface between the C-ABI host code (mla_api.cpp) and the gfx950 kernels
+// (mla_kernels.hip).  Not installed; the public interface is include/mla_decode.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kLatent = 512;  // latent width (V aliases it)
+constexpr int kRope = 64;     // rope key width
+constexpr int kRow = 576;     // one cache token
+
+constexpr int kTileTokens = 32;    // tokens per KV tile streamed through LDS
+constexpr int kRowsPerWave = 32;   // query rows (query x head) one wavefront owns
+constexpr int kWaves = 4;          // wavefronts per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerGroup = kRowsPerWave * kWaves;  // rows per workgroup
+constexpr int kMaxBatch = 4096;
+
+constexpr int kFmtBf16 = 0;
+constexpr int kFmtFp8 = 1;
+constexpr int kFmtNvfp4 = 2;
+
+// Everything one decode launch needs; passed by value as the kernel argument.
+struct DecodeParams {
+  const uint16_t* q;    // [B, q_len, H, 512] bf16 bits
+  const uint16_t* qpe;  // [B, q_len, H, 64]
+  // contiguous cache
+  const uint16_t* kv;   // [B, S, 512]
+  const uint16_t* kpe;  // [B, S, 64]
+  int S;
+  int kv_len_per_split;
+  // paged cache
+  const uint8_t* cache;
+  int64_t page_stride;
+  const int32_t* block_tables;
+  int max_blocks;
+  const int32_t* seq_lens;
+  int page_size;
+  int num_pages;
+  // problem
+  int B, q_len, H;
+  int rows;           // q_len * H
+  int row_groups;     // ceil(rows / kRowsPerGroup)
+  int num_splits;     // contiguous: splits per request; paged: token-balanced ranges
+  float score_scale;  // sm_scale * kv_scale * log2(e)
+  float v_scale;      // kv_scale (FP8) or 1
+  // partial outputs: element (slot, row, d) at o_part[slot*o_slot + row*o_row + d]
+  float* o_part;
+  float* lse_part;
+  int64_t o_slot, o_row, l_slot, l_row;
+  int32_t* seg_first;  // paged: first / last range index that covers request b
+  int32_t* seg_last;
+  int32_t* info;       // paged: info[0] = total tile count of the batch
+};
+
+struct CombineParams {
+  const float* o_part;
+  const float* lse_part;
+  uint16_t* o;
+  float* lse;
+  int rows;        // generic: total rows; paged: rows per request (q_len * H)
+  int num_splits;  // generic: splits per row; paged: token-balanced ranges
+  int B;           // paged only
+  const int32_t* seq_lens;
+  const int32_t* seg_first;
+  const int32_t* seg_last;
+  const int32_t* info;
+  int max_len;     // paged: max_blocks * page_size (clamp for seq_lens)
+};
+
+hipError_t launch_decode_contig(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_paged(int fmt, const DecodeParams& p, hipStream_t stream);
+hipError_t launch_combine_generic(const CombineParams& p, hipStream_t stream);
+hipError_t launch_combine_paged(const CombineParams& p, hipStream_t stream);
+
+}  // namespace mla

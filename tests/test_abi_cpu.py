@@ -1,0 +1,163 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol, the
+planners match the oracle's planner, and every invalid-argument path returns its status
+before touching the GPU (these calls pass fake, aligned device addresses, which the
+library never dereferences on the host)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import mla_split_kv_02_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(mla.LIB_PATH), reason="library not built")
+
+F = 0x10000000  # fake 256-aligned device address (never dereferenced by failing calls)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = mla.lib()
+    decl = declared_functions()
+    assert decl == sorted(mla.EXPORTED_SYMBOLS)
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4):
+        assert mla.status_string(s).startswith("MLA_")
+    assert mla.status_string(7) == "unknown mla_status"
+
+
+def test_plan_contig_matches_oracle():
+    for cus in (1, 80, 256, 304):
+        for B in (1, 2, 3, 4, 32, 64, 255, 256, 1000):
+            for S in (1, 100, 128, 129, 256, 4096, 8192, 65537):
+                assert mla.plan_contig(cus, B, S) == oracle.plan_contig(cus, B, S), (cus, B, S)
+
+
+def test_plan_paged_and_workspace():
+    assert mla.plan_paged(256, 64, 1, 128) == 256
+    assert mla.plan_paged(256, 128, 2, 128) == 128
+    assert mla.plan_paged(256, 4, 1, 16) == 256
+    assert mla.plan_paged(1, 4, 8, 128) == 1
+    ws = mla.paged_workspace_bytes(64, 1, 128, 256)
+    per_split = oracle.workspace_floats_per_split(1, 128) * 4
+    assert ws >= (256 + 63) * per_split
+    assert ws < (256 + 63) * per_split + 4096
+    assert mla.paged_workspace_bytes(0, 1, 128, 256) == 0
+    assert mla.paged_workspace_bytes(4, 9, 128, 256) == 0
+    assert mla.paged_workspace_bytes(4, 1, 24, 256) == 0
+
+
+def _paged(**kw):
+    a = dict(q=F, qpe=F, cache=F, fmt=1, kv_scale=1.0, num_pages=10, page_size=64, stride=64 * 576, bt=F, mb=4,
+             sl=F, B=2, q_len=1, H=128, sm=0.07, ns=8, ws=F, ws_bytes=1 << 30, o=F, lse=F)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return mla.lib().mla_paged_decode(vp(a["q"]), vp(a["qpe"]), vp(a["cache"]), a["fmt"], a["kv_scale"],
+                                      a["num_pages"], a["page_size"], a["stride"], vp(a["bt"]), a["mb"],
+                                      vp(a["sl"]), a["B"], a["q_len"], a["H"], a["sm"], a["ns"], vp(a["ws"]),
+                                      a["ws_bytes"], vp(a["o"]), vp(a["lse"]), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(cache=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(bt=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(sl=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(ws=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(o=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(q=F + 8), mla.MLA_ERR_INVALID_ARG),
+    (dict(ws=F + 16), mla.MLA_ERR_INVALID_ARG),
+    (dict(fmt=3), mla.MLA_ERR_UNSUPPORTED),
+    (dict(page_size=16), mla.MLA_ERR_UNSUPPORTED),
+    (dict(page_size=128), mla.MLA_ERR_UNSUPPORTED),
+    (dict(q_len=0), mla.MLA_ERR_UNSUPPORTED),
+    (dict(q_len=9), mla.MLA_ERR_UNSUPPORTED),
+    (dict(H=24), mla.MLA_ERR_UNSUPPORTED),
+    (dict(H=144), mla.MLA_ERR_UNSUPPORTED),
+    (dict(B=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(B=4097), mla.MLA_ERR_INVALID_ARG),
+    (dict(ns=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(ns=65537), mla.MLA_ERR_INVALID_ARG),
+    (dict(stride=64 * 576 - 16), mla.MLA_ERR_INVALID_ARG),
+    (dict(stride=64 * 576 + 8), mla.MLA_ERR_INVALID_ARG),
+    (dict(fmt=0, stride=64 * 576), mla.MLA_ERR_INVALID_ARG),
+    (dict(fmt=2, stride=64 * 324 - 16), mla.MLA_ERR_INVALID_ARG),
+    (dict(num_pages=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(mb=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(B=4096, mb=1 << 14), mla.MLA_ERR_INVALID_ARG),
+    (dict(kv_scale=0.0), mla.MLA_ERR_INVALID_ARG),
+    (dict(kv_scale=float("nan")), mla.MLA_ERR_INVALID_ARG),
+    (dict(sm=float("inf")), mla.MLA_ERR_INVALID_ARG),
+    (dict(ws_bytes=1000), mla.MLA_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_paged_decode_rejects(kw, status):
+    assert _paged(**kw) == status
+
+
+def test_paged_workspace_boundary():
+    need = mla.paged_workspace_bytes(2, 1, 128, 8)
+    assert _paged(ws_bytes=need - 1) == mla.MLA_ERR_WORKSPACE_TOO_SMALL
+
+
+def _contig(**kw):
+    a = dict(q=F, qpe=F, kv=F, kpe=F, B=2, H=16, S=256, sm=0.07, L=128, op=F, lp=F)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return mla.lib().mla_decode_splitkv(vp(a["q"]), vp(a["qpe"]), vp(a["kv"]), vp(a["kpe"]), a["B"], a["H"],
+                                        a["S"], a["sm"], a["L"], vp(a["op"]), vp(a["lp"]), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(kpe=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(op=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(lp=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(kv=F + 2), mla.MLA_ERR_INVALID_ARG),
+    (dict(L=100), mla.MLA_ERR_INVALID_ARG),
+    (dict(L=64), mla.MLA_ERR_INVALID_ARG),
+    (dict(L=384), mla.MLA_ERR_INVALID_ARG),
+    (dict(B=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(S=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(H=8), mla.MLA_ERR_UNSUPPORTED),
+    (dict(H=136), mla.MLA_ERR_UNSUPPORTED),
+    (dict(sm=float("nan")), mla.MLA_ERR_INVALID_ARG),
+])
+def test_decode_splitkv_rejects(kw, status):
+    assert _contig(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(op=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(o=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(rows=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(ns=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(ns=65537), mla.MLA_ERR_INVALID_ARG),
+    (dict(o=F + 4), mla.MLA_ERR_INVALID_ARG),
+])
+def test_combine_rejects(kw, status):
+    a = dict(op=F, lp=F, rows=4, ns=2, o=F, lse=F)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    assert mla.lib().mla_splitkv_combine(vp(a["op"]), vp(a["lp"]), a["rows"], a["ns"], vp(a["o"]), vp(a["lse"]),
+                                         None) == status
+
+
+def test_planner_null_outputs():
+    L = mla.lib()
+    assert L.mla_plan_contig(256, 1, 256, None, None) == mla.MLA_ERR_INVALID_ARG
+    assert L.mla_plan_paged(256, 1, 1, 16, None) == mla.MLA_ERR_INVALID_ARG
+    assert L.mla_device_num_cus(0, None) == mla.MLA_ERR_INVALID_ARG

@@ -1,0 +1,257 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle, element by
+element on the same seeded inputs.  Small cases span several tiles and ragged tails;
+the full-size workloads compare sampled requests (every head and query of each sampled
+request) that the oracle computes one by one."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mla_split_kv_02_amd as mla
+from workloads import gen
+from gpu_util import (TOL_LSE, TOL_O_BF16, TOL_O_QUANT, bf16_dev, host, i32_dev, max_err,
+                      paged_device_inputs, say, u8_dev)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _contig_run(c, L):
+    q, qpe, kv, kpe = (bf16_dev(a) for a in (c.q, c.qpe, c.kv, c.kpe))
+    op, lp, L = mla.decode_splitkv(q, qpe, kv, kpe, c.sm_scale, L)
+    o, lse = mla.splitkv_combine(op, lp)
+    torch.cuda.synchronize()
+    return host(op), host(lp), host(o), host(lse), L
+
+
+@pytest.mark.parametrize("B,H,S,L", [
+    (1, 16, 256, 128),     # tiny contiguous workload: 2 splits
+    (2, 32, 300, 128),     # ragged last split (44 tokens, partial tile)
+    (1, 48, 200, 128),     # rows not a multiple of 32: one wave half idle, two waves idle
+    (2, 128, 1000, 256),   # full head group, 4 splits, ragged
+    (3, 64, 129, 128),     # one token in the last split
+])
+def test_contig_splitkv_matches_oracle(B, H, S, L):
+    say(f"contig B={B} H={H} S={S} L={L}")
+    c = gen.make_contig(B, H, S, seed=7 + B + H + S)
+    op, lp, o, lse, _ = _contig_run(c, L)
+    q, qpe, kv, kpe = c.f64()
+    rop, rlp = oracle.contig_decode_splitkv(q, qpe, kv, kpe, c.sm_scale, L)
+    ro, rl = oracle.contig_decode(q, qpe, kv, kpe, c.sm_scale)
+    assert max_err(op, rop) <= TOL_O_BF16
+    assert max_err(lp, rlp) <= TOL_LSE
+    assert max_err(o, ro) <= TOL_O_BF16
+    assert max_err(lse, rl) <= TOL_LSE
+
+
+def test_contig_b4_h16_s4096_full_size():
+    say("contig_b4_h16_s4096 full size")
+    c = gen.make_workload("contig_b4_h16_s4096")
+    L, ns = mla.plan_contig(256, c.B, c.S)
+    assert (L, ns) == (128, 32)
+    op, lp, o, lse, _ = _contig_run(c, L)
+    q, qpe, kv, kpe = c.f64()
+    ro, rl = oracle.contig_decode(q, qpe, kv, kpe, c.sm_scale)
+    assert max_err(o, ro) <= TOL_O_BF16
+    assert max_err(lse, rl) <= TOL_LSE
+    rop, rlp = oracle.contig_decode_splitkv(q[:1], qpe[:1], kv[:1], kpe[:1], c.sm_scale, L)
+    assert max_err(op[:1], rop) <= TOL_O_BF16 and max_err(lp[:1], rlp) <= TOL_LSE
+
+
+def test_contig_b32_h128_s8192_full_size_sampled():
+    say("contig_b32_h128_s8192 full size, requests 0 and 31")
+    c = gen.make_workload("contig_b32_h128_s8192")
+    L, ns = mla.plan_contig(256, c.B, c.S)
+    assert (L, ns) == (1024, 8)
+    op, lp, o, lse, _ = _contig_run(c, L)
+    q, qpe, kv, kpe = c.f64()
+    for b in (0, 31):
+        ro, rl = oracle.contig_decode(q[b:b + 1], qpe[b:b + 1], kv[b:b + 1], kpe[b:b + 1], c.sm_scale)
+        assert max_err(o[b:b + 1], ro) <= TOL_O_BF16
+        assert max_err(lse[b:b + 1], rl) <= TOL_LSE
+        rop, rlp = oracle.contig_decode_splitkv(q[b:b + 1], qpe[b:b + 1], kv[b:b + 1], kpe[b:b + 1], c.sm_scale, L)
+        assert max_err(op[b:b + 1], rop) <= TOL_O_BF16 and max_err(lp[b:b + 1], rlp) <= TOL_LSE
+
+
+def test_contig_zero_query_is_mean_of_latent():
+    say("contig zero query")
+    c = gen.make_contig(2, 16, 333, seed=3, zero_q=True)
+    _, _, o, lse, _ = _contig_run(c, 128)
+    kv = gen.bf16_bits_to_f32(c.kv).astype(np.float64)
+    mean = kv.mean(axis=1)  # [B, 512]
+    assert np.abs(o - mean[:, None, :]).max() <= TOL_O_BF16
+    assert np.abs(lse - math.log(333)).max() <= TOL_LSE
+
+
+def test_contig_run_to_run_bitwise_stable():
+    say("contig determinism")
+    c = gen.make_contig(2, 128, 700, seed=5)
+    a = _contig_run(c, 256)
+    b = _contig_run(c, 256)
+    for x, y in zip(a[:4], b[:4]):
+        assert np.array_equal(x, y)
+
+
+def test_combine_matches_oracle_with_empty_splits():
+    say("combine generic")
+    rng = np.random.default_rng(4)
+    R, NS = 37, 9
+    op = rng.standard_normal((R, NS, 512)).astype(np.float32)
+    lp = (rng.standard_normal((R, NS)) * 3).astype(np.float32)
+    lp[3, 2] = -np.inf
+    lp[5, :] = -np.inf
+    lp[7, :8] = -np.inf
+    op[3, 2] = np.nan   # a skipped split must not be read
+    op[5, :] = np.nan
+    top = torch.from_numpy(op).to(DEV)
+    tlp = torch.from_numpy(lp).to(DEV)
+    o, lse = mla.splitkv_combine(top, tlp)
+    torch.cuda.synchronize()
+    ro, rl = oracle.combine(np.nan_to_num(op.astype(np.float64)), lp.astype(np.float64))
+    assert max_err(host(lse), rl) <= 1e-5
+    assert max_err(host(o), ro) <= 8e-3  # bf16 rounding of |O| < 4
+    assert (host(o)[5] == 0).all() and np.isneginf(host(lse)[5])
+
+
+# ----------------------------------------------------------------------------------
+# paged
+# ----------------------------------------------------------------------------------
+
+def _paged_run(w, num_splits=None, want_lse=True):
+    d = paged_device_inputs(w)
+    o, lse = mla.paged_decode(d["q"], d["qpe"], d["cache"], w.fmt, d["bt"], d["sl"], w.page_size, w.page_stride,
+                              w.kv_scale, w.sm_scale, num_splits=num_splits, want_lse=want_lse)
+    torch.cuda.synchronize()
+    return host(o), (host(lse) if lse is not None else None)
+
+
+def _paged_ref(w, requests=None):
+    q, qpe = w.q_f64()
+    return oracle.paged_decode(q, qpe, w.cache, w.fmt, w.kv_scale, w.page_size, w.page_stride, w.block_tables,
+                               w.seq_lens, w.sm_scale, requests=requests)
+
+
+def _tol_o(fmt):
+    return TOL_O_BF16 if fmt == gen.FMT_BF16 else TOL_O_QUANT
+
+
+@pytest.mark.parametrize("fmt", [gen.FMT_BF16, gen.FMT_FP8, gen.FMT_NVFP4])
+@pytest.mark.parametrize("q_len", [1, 2])
+@pytest.mark.parametrize("page_size", [32, 64])
+def test_paged_matches_oracle(fmt, q_len, page_size):
+    say(f"paged fmt={gen.FMT_NAMES[fmt]} q_len={q_len} page={page_size}")
+    w = gen.make_paged(B=4, H=128, q_len=q_len, lo=1, hi=400, page_size=page_size, fmt=fmt, seed=40 + fmt,
+                       seq_lens=[1, 63, 290, 97], max_blocks=16, poison_tail=True)
+    ro, rl = _paged_ref(w)
+    for ns in (None, 1, 5):
+        o, lse = _paged_run(w, ns)
+        assert max_err(o, ro) <= _tol_o(fmt), ns
+        assert max_err(lse, rl) <= TOL_LSE, ns
+
+
+@pytest.mark.parametrize("H,q_len", [(16, 1), (16, 2), (48, 1), (64, 4), (128, 8)])
+def test_paged_head_and_query_counts(H, q_len):
+    say(f"paged H={H} q_len={q_len}")
+    w = gen.make_paged(B=3, H=H, q_len=q_len, lo=8, hi=200, page_size=64, fmt=gen.FMT_FP8, seed=50 + H + q_len,
+                       max_blocks=4)
+    ro, rl = _paged_ref(w)
+    o, lse = _paged_run(w)
+    assert max_err(o, ro) <= TOL_O_QUANT
+    assert max_err(lse, rl) <= TOL_LSE
+
+
+def test_paged_empty_and_short_requests():
+    say("paged empty/short requests")
+    w = gen.make_paged(B=5, H=32, q_len=2, lo=1, hi=1, page_size=32, fmt=gen.FMT_BF16, seed=60,
+                       seq_lens=[0, 1, 2, 0, 33], max_blocks=3)
+    ro, rl = _paged_ref(w)
+    for ns in (None, 1, 2, 3):
+        o, lse = _paged_run(w, ns)
+        assert max_err(o, ro) <= TOL_O_BF16, ns
+        assert max_err(lse, rl) <= TOL_LSE, ns
+        assert (o[0] == 0).all() and np.isneginf(lse[0]).all()
+        assert np.isneginf(lse[1, 0]).all() and (o[1, 0] == 0).all()
+
+
+def test_paged_page_permutation_is_bitwise_invariant():
+    say("paged page permutation")
+    w = gen.make_paged(B=3, H=128, q_len=1, lo=100, hi=700, page_size=64, fmt=gen.FMT_FP8, seed=61)
+    o1, l1 = _paged_run(w)
+    rng = np.random.default_rng(1)
+    perm = rng.permutation(w.num_pages)
+    pages = w.cache.reshape(w.num_pages, w.page_stride)
+    moved = np.empty_like(pages)
+    moved[perm] = pages
+    w.cache = moved.reshape(-1)
+    w.block_tables = perm[w.block_tables].astype(np.int32)
+    o2, l2 = _paged_run(w)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_paged_padded_page_stride():
+    say("paged padded stride")
+    w = gen.make_paged(B=2, H=32, q_len=1, lo=50, hi=300, page_size=64, fmt=gen.FMT_NVFP4, seed=62,
+                       page_stride=64 * 324 + 48)
+    ro, rl = _paged_ref(w)
+    o, lse = _paged_run(w)
+    assert max_err(o, ro) <= TOL_O_QUANT and max_err(lse, rl) <= TOL_LSE
+
+
+def test_paged_fp8_every_code():
+    """A cache holding every E4M3 code (NaN codes excluded) decodes as the oracle does."""
+    say("paged fp8 every code")
+    w = gen.make_paged(B=1, H=16, q_len=1, lo=64, hi=64, page_size=64, fmt=gen.FMT_FP8, seed=63)
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    rows = np.resize(codes, 64 * 576).reshape(64, 576)
+    w.cache[:64 * 576] = rows.ravel()
+    w.block_tables[:] = 0
+    w.kv_scale = 1.0 / 128  # |values| <= 3.5 keeps the bf16 rounding of O inside the tolerance
+    ro, rl = _paged_ref(w)
+    o, lse = _paged_run(w)
+    assert max_err(o, ro) <= TOL_O_QUANT and max_err(lse, rl) <= TOL_LSE
+
+
+def test_paged_nvfp4_every_code_and_scale():
+    say("paged nvfp4 every code")
+    w = gen.make_paged(B=1, H=16, q_len=1, lo=64, hi=64, page_size=64, fmt=gen.FMT_NVFP4, seed=64)
+    rng = np.random.default_rng(2)
+    page = w.cache[:64 * 324]
+    page[:64 * 288] = np.resize(np.arange(256, dtype=np.uint8), 64 * 288)
+    # scales up to 0.5 (codes 0x00..0x30 with either sign) keep |values| <= 3
+    sc = np.array([c for c in range(256) if (c & 0x7F) <= 0x30], dtype=np.uint8)
+    page[64 * 288:] = rng.choice(sc, 64 * 36)
+    w.block_tables[:] = 0
+    ro, rl = _paged_ref(w)
+    o, lse = _paged_run(w)
+    assert max_err(o, ro) <= TOL_O_QUANT and max_err(lse, rl) <= TOL_LSE
+
+
+def test_paged_fp8_b64_h128_full_size_sampled():
+    """The benchmark workload at full size and in its benchmark launch configuration;
+    the shortest, the longest and a middle request are compared in full."""
+    say("paged_fp8_b64_h128 full size")
+    w = gen.make_workload("paged_fp8_b64_h128_s1k_32k")
+    o, lse = _paged_run(w, mla.plan_paged(256, w.B, w.q_len, w.H))
+    assert np.isfinite(o).all()
+    order = np.argsort(w.seq_lens)
+    pick = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
+    ro, rl = _paged_ref(w, requests=pick)
+    assert max_err(o[pick], ro) <= TOL_O_QUANT
+    assert max_err(lse[pick], rl) <= TOL_LSE
+
+
+@pytest.mark.slow
+def test_paged_nvfp4_b128_h128_q2_full_size_sampled():
+    say("paged_nvfp4_b128_h128_q2 full size")
+    w = gen.make_workload("paged_nvfp4_b128_h128_q2_s2k_64k")
+    o, lse = _paged_run(w, mla.plan_paged(256, w.B, w.q_len, w.H))
+    assert np.isfinite(o).all()
+    order = np.argsort(w.seq_lens)
+    pick = [int(order[0]), int(order[-1])]
+    ro, rl = _paged_ref(w, requests=pick)
+    assert max_err(o[pick], ro) <= TOL_O_QUANT
+    assert max_err(lse[pick], rl) <= TOL_LSE
