@@ -194,14 +194,14 @@ int paged_partials(const uint16_t* q, const uint16_t* qpe, const void* kv_cache,
   const int64_t rb = row_bytes(fmt);
   if (rb < 0) return MLA_ERR_UNSUPPORTED;
   if (page_size != 32 && page_size != 64) return MLA_ERR_UNSUPPORTED;
-  PagedLayout L;
-  const int st = check_paged_shape(B, q_len, H, num_splits, workspace, workspace_bytes, &L);
-  if (st != MLA_OK) return st;
   if (num_pages < 1 || max_blocks_per_seq < 1) return MLA_ERR_INVALID_ARG;
   if (page_stride_bytes < page_size * rb || page_stride_bytes % 16 != 0) return MLA_ERR_INVALID_ARG;
   if ((int64_t)B * max_blocks_per_seq * page_size >= ((int64_t)1 << 31)) return MLA_ERR_INVALID_ARG;
   if (!isfinite(sm_scale)) return MLA_ERR_INVALID_ARG;
   if (fmt == MLA_KV_FP8_E4M3 && !(isfinite(kv_scale) && kv_scale > 0.f)) return MLA_ERR_INVALID_ARG;
+  PagedLayout L;
+  const int st = check_paged_shape(B, q_len, H, num_splits, workspace, workspace_bytes, &L);
+  if (st != MLA_OK) return st;
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const float vs = (fmt == MLA_KV_FP8_E4M3) ? kv_scale : 1.f;

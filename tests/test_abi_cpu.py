@@ -161,3 +161,24 @@ def test_planner_null_outputs():
     assert L.mla_plan_contig(256, 1, 256, None, None) == mla.MLA_ERR_INVALID_ARG
     assert L.mla_plan_paged(256, 1, 1, 16, None) == mla.MLA_ERR_INVALID_ARG
     assert L.mla_device_num_cus(0, None) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_paged_partials_and_combine_reject():
+    L = mla.lib()
+    vp = ctypes.c_void_p
+    ws = mla.paged_workspace_bytes(2, 1, 128, 8)
+    ok = (vp(F), vp(F), vp(F), 1, 1.0, 10, 64, 64 * 576, vp(F), 4, vp(F), 2, 1, 128, 0.07, 8, vp(F), ws, None)
+    bad_fmt = ok[:3] + (5,) + ok[4:]
+    assert L.mla_paged_decode_partials(*bad_fmt) == mla.MLA_ERR_UNSUPPORTED
+    small_ws = ok[:17] + (ws - 1, None)
+    assert L.mla_paged_decode_partials(*small_ws) == mla.MLA_ERR_WORKSPACE_TOO_SMALL
+    null_q = (None,) + ok[1:]
+    assert L.mla_paged_decode_partials(*null_q) == mla.MLA_ERR_INVALID_ARG
+    c_ok = [vp(F), ws, vp(F), 2, 1, 128, 8, 4, 64, vp(F), vp(F), None]
+    for i, v, st in ((0, None, mla.MLA_ERR_INVALID_ARG), (1, ws - 1, mla.MLA_ERR_WORKSPACE_TOO_SMALL),
+                     (2, None, mla.MLA_ERR_INVALID_ARG), (5, 40, mla.MLA_ERR_UNSUPPORTED),
+                     (8, 48, mla.MLA_ERR_UNSUPPORTED), (7, 0, mla.MLA_ERR_INVALID_ARG),
+                     (9, None, mla.MLA_ERR_INVALID_ARG), (9, vp(F + 2), mla.MLA_ERR_INVALID_ARG)):
+        args = list(c_ok)
+        args[i] = v
+        assert L.mla_paged_combine(*args) == st, (i, v)
