@@ -1,0 +1,194 @@
+"""Benchmark of the absorbed-MLA paged decode on one MI355X.
+
+One step = the whole hot path on one batch: the split-KV decode launch (partials) and
+the LSE combine launch, through the C ABI, on inputs already resident in HBM.  The
+default workload is the paged FP8 batch B=64, H=128, q_len=1, seq_len uniform in
+[1024, 32768], page size 64 (seeded, synthetic).  Prints ONE JSON line on stdout.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Algorithmic counts (per step): flops = 2 * (576 + 512) * H * sum over requests and
+queries of the tokens each query sees; bytes = visible cache rows (576 FP8 bytes per
+token) + Q + QPE + O (bf16) + LSE (fp32) + one int32 block-table entry per page read.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "MLA decode KV GB/s + TFLOP/s (% roofline), B=64 H=128 paged fp8"
+KERNEL_SOURCES = ("mla_split_kv_02_amd/csrc/mla_kernels.hip", "mla_split_kv_02_amd/csrc/mla_internal.h")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_counts(w):
+    import numpy as np
+    n = w.seq_lens.astype(np.int64)
+    vis = sum(np.maximum(n - w.q_len + i + 1, 0) for i in range(w.q_len))  # per request
+    flops = 2.0 * (576 + 512) * w.H * float(vis.sum())
+    from workloads.gen import row_bytes
+    kv = float(n.sum()) * row_bytes(w.fmt)
+    rows = w.B * w.q_len * w.H
+    qbytes = rows * (512 + 64) * 2
+    obytes = rows * 512 * 2 + rows * 4
+    tbytes = 4.0 * float(((n + w.page_size - 1) // w.page_size).sum())
+    return flops, kv + qbytes + obytes + tbytes, kv
+
+
+def traffic_from_profiles(workload: str, src_hash: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_paged_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha") != src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    """The float64 oracle, as it stands, on requests of the same batch taken in order
+    until about budget_s seconds of CPU work."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    q, qpe = w.q_f64()
+    done_flops, used, t0 = 0.0, 0, time.perf_counter()
+    for b in range(w.B):
+        if time.perf_counter() - t0 > budget_s and used > 0:
+            break
+        oracle.paged_decode_request(q[b], qpe[b], w.cache, w.fmt, w.kv_scale, w.page_size, w.page_stride,
+                                    w.block_tables[b], int(w.seq_lens[b]), w.sm_scale)
+        n = int(w.seq_lens[b])
+        done_flops += 2.0 * (576 + 512) * w.H * sum(max(n - w.q_len + i + 1, 0) for i in range(w.q_len))
+        used += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(done_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"requests 0..{used - 1} of the same batch ({used} of {w.B}), float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="paged_fp8_b64_h128_s1k_32k")
+    ap.add_argument("--num-splits", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this decode path is built and measured on a single MI355X "
+              f"(--gpus {args.gpus} was asked for); see the design notes for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mla_split_kv_02_amd as mla
+    from workloads import gen
+
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {args.workload}")
+    w = gen.make_workload(args.workload)
+    if w.__class__.__name__ != "PagedInputs":
+        raise SystemExit("bench.py times the paged decode workloads")
+    t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, qpe = t16(w.q), t16(w.qpe)
+    cache = torch.from_numpy(w.cache).to(dev)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    num_cus = mla.device_num_cus(0)
+    G = args.num_splits or mla.plan_paged(num_cus, w.B, w.q_len, w.H)
+    call = mla.PagedCall(q, qpe, cache, w.fmt, bt, sl, w.page_size, w.page_stride, w.kv_scale, w.sm_scale,
+                         num_splits=G)
+    flops, nbytes, kvbytes = algorithmic_counts(w)
+    log(f"[bench] B={w.B} H={w.H} q_len={w.q_len} tokens={int(w.seq_lens.sum())} num_splits={G} "
+        f"flops={flops:.3e} bytes={nbytes:.3e}")
+
+    for _ in range(args.warmup):
+        call.partials()
+        call.combine()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record()
+        call.partials()
+        ev[k][1].record()
+        call.combine()
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    comb_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    ms_step = wall / args.steps * 1e3
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    log(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step wall, decode {dec_avg:.4f} ms "
+        f"(min {min(dec_ms):.4f}, max {max(dec_ms):.4f}), combine {sum(comb_ms) / len(comb_ms):.4f} ms")
+
+    value = flops / (ms_step * 1e-3) / 1e12
+    kv_gbps = nbytes / (ms_step * 1e-3) / 1e9
+    dec_tflops = flops / (dec_avg * 1e-3) / 1e12
+    intensity = flops / nbytes
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profiles(args.workload, src_hash)
+    if intensity >= ridge:
+        roof = {"bound": "mfma", "achieved": round(dec_tflops, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dec_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic}
+    else:
+        dec_gbps = nbytes / (dec_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "B": w.B, "H": w.H, "q_len": w.q_len, "page_size": w.page_size,
+                   "kv_format": gen.FMT_NAMES[w.fmt], "tokens": int(w.seq_lens.sum()), "num_splits": G,
+                   "decode_ms": round(dec_avg, 5), "combine_ms": round(sum(comb_ms) / len(comb_ms), 5),
+                   "kv_GBps": round(kv_gbps, 1), "kv_GBps_frac_of_hbm": round(kv_gbps / HBM_PEAK_GBPS, 4),
+                   "step_TFLOPs_frac_of_bf16_mfma": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
+                   "kernel_source_sha": src_hash},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

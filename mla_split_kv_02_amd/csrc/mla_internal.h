@@ -12,10 +12,11 @@ constexpr int kRope = 64;     // rope key width
 constexpr int kRow = 576;     // one cache token
 
 constexpr int kTileTokens = 32;    // tokens per KV tile streamed through LDS
-constexpr int kRowsPerWave = 32;   // query rows (query x head) one wavefront owns
-constexpr int kWaves = 4;          // wavefronts per workgroup
+constexpr int kWaves = 8;          // wavefronts per workgroup (two per SIMD)
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerGroup = kRowsPerWave * kWaves;  // rows per workgroup
+constexpr int kQkRows = 16;        // query rows whose scores one wavefront computes
+constexpr int kPvDims = 64;        // output dims one wavefront accumulates, for every row
+constexpr int kRowsPerGroup = kQkRows * kWaves;  // query rows (query x head) per workgroup: 128
 constexpr int kMaxBatch = 4096;
 
 constexpr int kFmtBf16 = 0;

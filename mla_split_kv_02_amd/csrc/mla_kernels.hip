@@ -1,19 +1,19 @@
 // gfx950 kernels for absorbed-MLA split-KV decode.
 //
-// Decode kernel.  One workgroup = 4 wavefronts = up to 128 query rows (query x head)
-// of one request and one token range.  The workgroup streams the range's KV tiles
-// (32 tokens x 576 values) from HBM straight into LDS with global->LDS loads (no
-// register staging), dequantises FP8 / NVFP4 tiles in LDS to bf16, and each wavefront
-// then runs, for its 32 rows:
-//   S^T[32 tok x 32 rows] = KV_tile[32 x 576] . Q^T[576 x 32]       36 MFMA 32x32x16
-//   masked online softmax over the tokens; a row lives in lanes l and l ^ 32
-//   O^T[512 x 32] += V^T[512 x 32 tok] . P^T[32 tok x 32 rows]       32 MFMA 32x32x16
-// Q^T stays in registers for the whole range and O^T accumulates in registers.  V^T
-// operands come from the token-major tile through the LDS transpose read.  All heads
-// of a request share one latent (absorbed MLA), so they all run against the same LDS
-// tile (the TileGym page's kernel re-reads the tile once per group of 16 heads).
-// Pipeline: raw tiles are loaded two tiles ahead of the MFMA work and dequantised one
-// tile ahead, with one workgroup barrier per tile.
+// Decode kernel.  One workgroup = 8 wavefronts (two per SIMD) = up to 128 query rows
+// (query x head) of one request and one token range.  The workgroup streams the
+// range's KV tiles (32 tokens x 576 values) from HBM straight into LDS with global->LDS
+// loads (no register staging) and dequantises FP8 / NVFP4 tiles in LDS to bf16.  Each
+// tile then takes two phases separated by a workgroup barrier:
+//   scores:  wavefront w computes S^T[32 tok x 16 rows] for rows 16w..16w+15 with MFMA
+//            16x16x32 (its Q^T rows stay in registers), applies the mask and the online
+//            softmax, and publishes P (bf16) and the rows' rescale factors in LDS;
+//   output:  wavefront w accumulates O^T[64 dims x 128 rows] for dims 64w..64w+63 with
+//            MFMA 32x32x16, V^T read from the token-major tile with the LDS transpose
+//            load and P^T from LDS.
+// All heads of a request share one latent (absorbed MLA), so every row of the group
+// runs against the same LDS tile (the TileGym page's kernel instead re-reads the tile
+// once per group of 16 heads).
 //
 // Combine kernels.  One wavefront per output row merges the partials with the split-K
 // log-sum-exp reduce (TileGym page, forward: splitk_reduce).
@@ -158,9 +158,7 @@ template <bool PAGED>
 __device__ __forceinline__ void load_bf16_tile(const Range& R, int tbase, uint8_t* tile, int wave, int lane) {
   const DecodeParams& p = *R.p;
   const uint8_t* pg = PAGED ? tile_page(R, tbase) : nullptr;
-#pragma unroll
-  for (int jj = 0; jj < kTileTokens * kRowChunks / 64 / kWaves; ++jj) {
-    const int j = wave + kWaves * jj;
+  for (int j = wave; j < kTileTokens * kRowChunks / 64; j += kWaves) {
     const int k = 64 * j + lane;
     const int r = k / kRowChunks, pos = k % kRowChunks;
     const int c = pos ^ swz(r);
@@ -249,71 +247,141 @@ __device__ __forceinline__ void dequant_nvfp4(const uint8_t* st, uint8_t* tile, 
 }
 
 // ------------------------------------------------------------------------------------
-// Per-wavefront attention state and the work on one tile
+// Work split inside a workgroup (8 wavefronts, 128 query rows).
+//   Score phase: wavefront w owns rows 16w .. 16w+15.  S^T[32 tok x 16 rows] from
+//     18 K-steps x 2 token blocks of MFMA 16x16x32 (Q^T of its rows in registers), then
+//     the masked online softmax; P (bf16) and each row's rescale factor go to LDS.
+//   Output phase: wavefront w owns dims 64w .. 64w+63 of all 128 rows:
+//     O^T[64 x 128] += V^T[64 x 32 tok] . P^T[32 tok x 128] with MFMA 32x32x16, V^T
+//     through the LDS transpose read of the token-major tile, P^T from LDS.
+// Two wavefronts share a SIMD, so one's MFMA work overlaps the other's softmax and
+// loads, and every wavefront stays within 256 registers.
 // ------------------------------------------------------------------------------------
 
-struct WaveState {
-  bf16x8 q[kKSteps];        // Q^T operand: row lr, dims 16k + 8lh .. +8
-  f32x16 o[kDimBlocks];     // O^T accumulators: row lr, dims 32d + 8(v/4) + 4lh + v%4
-  float m_used;             // reference max (log2 domain), equal in lanes l and l^32
-  float l_sum;              // this lane's share of sum p (unrounded): for the LSE
-  float l_rnd;              // this lane's share of sum bf16(p): normalises O
-  int qk_off[4];            // LDS byte offsets of the QK operand, K-step k -> [k & 3] + 128 (k >> 2)
-  int pv_off[8];            // LDS byte offsets of the V^T transpose reads
-  int vis;                  // tokens this lane's row may see
+constexpr int kQkSteps = kRow / 32;          // 18 K-steps of 32 dims (MFMA 16x16x32)
+constexpr int kPRowPitch = 80;               // bytes per row of the P buffer (64 + 16 pad)
+constexpr int kPBufBytes = kRowsPerGroup * kPRowPitch;
+
+struct Shared {  // LDS exchanged between the two phases of a tile
+  uint8_t* pbuf;  // P as bf16 [128 rows][32 tokens], row pitch kPRowPitch
+  float* alpha;   // [128] factor for each row's accumulators before this tile's product
+  float* inv_l;   // [128] at the end of a range: v_scale / sum of bf16(p) (0 if no token)
 };
 
-__device__ __forceinline__ void mm_tile(WaveState& W, const uint8_t* tile, int tbase, float score_scale, int lh) {
-  // ---- S^T = KV . Q^T: lane holds row lr, tokens 8(v/4) + 4lh + v%4 ----
-  f32x16 s = f32x16{};
-#pragma unroll
-  for (int k = 0; k < kKSteps; ++k) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(tile + W.qk_off[k & 3] + 128 * (k >> 2));
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, W.q[k], s, 0, 0, 0);
-  }
+struct ScoreState {
+  bf16x8 q[kQkSteps];  // Q^T operand: row 16w + l%16, dims 32k + 8(l/16) .. +8
+  float m_used;        // reference max (log2 domain), equal in the 4 lanes of a row
+  float l_sum;         // this lane's share of sum p (unrounded): for the LSE
+  float l_rnd;         // this lane's share of sum bf16(p): normalises O
+  int vis;             // tokens the row may see
+  int a_off[4];        // KV operand offsets, [2 tb + (k & 1)] + 128 (k >> 1)
+  int p_off;           // P write offset: row * pitch + 8 (l / 16), + 32 tb
+};
 
-  // ---- mask + online softmax (base 2) ----
+struct OutState {
+  f32x16 o[2][4];      // o[db][rb]: row 32rb + l%32, dims 64w + 32db + 8(v/4) + 4(l/32) + v%4
+  int v_off[8];        // transpose-read offsets [4 db + 2 ks + e]
+  int p_off;           // P^T operand: row l%32, tokens 16ks + 8(l/32): + 32*pitch*rb + 32 ks
+};
+
+// Values of the four lanes l, l^16, l^32, l^48 (one row), combined with lane swaps.
+__device__ __forceinline__ float quad_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return pair_max(x);
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  return pair_sum(x);
+}
+
+// Score phase of one tile for this wavefront's 16 rows.
+__device__ __forceinline__ void score_tile(ScoreState& S, const uint8_t* tile, const Shared& X, int tbase,
+                                           float score_scale, int lane, bool active, int row_in_group) {
+  const int g = lane >> 4;
+  f32x4 s0 = f32x4{}, s1 = f32x4{};
+  if (active) {
+#pragma unroll
+    for (int k = 0; k < kQkSteps; ++k) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(tile + S.a_off[0 + (k & 1)] + 128 * (k >> 1));
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(tile + S.a_off[2 + (k & 1)] + 128 * (k >> 1));
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, S.q[k], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, S.q[k], s1, 0, 0, 0);
+    }
+  }
+  // lane holds row l%16, tokens tbase + 16 tb + 4(l/16) + v
+  float x[8];
   float mt = -INFINITY;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int tok = tbase + 8 * (v >> 2) + 4 * lh + (v & 3);
-    const float x = (tok < W.vis) ? s[v] * score_scale : -INFINITY;
-    s[v] = x;
-    mt = fmaxf(mt, x);
+  for (int v = 0; v < 8; ++v) {
+    const int tok = tbase + 16 * (v >> 2) + 4 * g + (v & 3);
+    const float sv = (v < 4) ? s0[v & 3] : s1[v & 3];
+    x[v] = (active && tok < S.vis) ? sv * score_scale : -INFINITY;
+    mt = fmaxf(mt, x[v]);
   }
-  mt = pair_max(mt);
-  const bool need = mt > W.m_used + kTau;
+  mt = quad_max(mt);
+  const bool need = mt > S.m_used + kTau;
+  float alpha = 1.0f;
   if (__any(need)) {
-    const float m_new = need ? mt : W.m_used;
-    const float alpha = need ? __builtin_amdgcn_exp2f(W.m_used - m_new) : 1.0f;
-    W.l_sum *= alpha;
-    W.l_rnd *= alpha;
-#pragma unroll
-    for (int d = 0; d < kDimBlocks; ++d) W.o[d] *= alpha;
-    W.m_used = m_new;
+    const float m_new = need ? mt : S.m_used;
+    alpha = need ? __builtin_amdgcn_exp2f(S.m_used - m_new) : 1.0f;
+    S.l_sum *= alpha;
+    S.l_rnd *= alpha;
+    S.m_used = m_new;
   }
-  const float msafe = (W.m_used == -INFINITY) ? 0.f : W.m_used;
-  bf16x8 pb[2];
+  const float msafe = (S.m_used == -INFINITY) ? 0.f : S.m_used;
+  unsigned pk[4];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const float e = __builtin_amdgcn_exp2f(s[v] - msafe);
-    W.l_sum += e;
-    const __bf16 eb = (__bf16)e;
-    W.l_rnd += (float)eb;
-    pb[v >> 3][v & 7] = eb;
+  for (int v = 0; v < 8; v += 2) {
+    const float e0 = __builtin_amdgcn_exp2f(x[v] - msafe);
+    const float e1 = __builtin_amdgcn_exp2f(x[v + 1] - msafe);
+    const __bf16 b0 = (__bf16)e0, b1 = (__bf16)e1;
+    S.l_sum += e0 + e1;
+    S.l_rnd += (float)b0 + (float)b1;
+    pk[v >> 1] = (unsigned)__builtin_bit_cast(unsigned short, b0) |
+                 ((unsigned)__builtin_bit_cast(unsigned short, b1) << 16);
   }
+  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+  *reinterpret_cast<u32x2*>(X.pbuf + S.p_off) = u32x2{pk[0], pk[1]};
+  *reinterpret_cast<u32x2*>(X.pbuf + S.p_off + 32) = u32x2{pk[2], pk[3]};
+  if (g == 0) X.alpha[row_in_group] = alpha;
+}
 
-  // ---- O^T += V^T . P^T; K index e of K-step ks <-> token 16ks + 8(e/4) + 4lh + e%4 ----
+// Output phase of one tile for this wavefront's 64 dims of the first nrb row blocks.
+__device__ __forceinline__ void out_tile(OutState& O, const uint8_t* tile, const Shared& X, int nrb, int lane) {
+  const int lr = lane & 31;
+  float al[4];
+  bool resc = false;
 #pragma unroll
-  for (int d = 0; d < kDimBlocks; ++d) {
+  for (int rb = 0; rb < 4; ++rb) {
+    al[rb] = (rb < nrb) ? X.alpha[32 * rb + lr] : 1.0f;
+    resc |= al[rb] != 1.0f;
+  }
+  if (__any(resc)) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int o0 = W.pv_off[4 * (d & 1) + 2 * ks + 0] + 128 * (d >> 1);
-      const int o1 = W.pv_off[4 * (d & 1) + 2 * ks + 1] + 128 * (d >> 1);
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(tile + o0));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(tile + o1));
-      const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      W.o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], W.o[d], 0, 0, 0);
+    for (int rb = 0; rb < 4; ++rb) {
+      O.o[0][rb] *= al[rb];
+      O.o[1][rb] *= al[rb];
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    bf16x8 va[2];
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(tile + O.v_off[4 * db + 2 * ks]));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(tile + O.v_off[4 * db + 2 * ks + 1]));
+      va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      if (rb < nrb) {
+        const bf16x8 pb =
+            *reinterpret_cast<const bf16x8*>(X.pbuf + O.p_off + 32 * kPRowPitch * rb + 32 * ks);
+        O.o[0][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0], pb, O.o[0][rb], 0, 0, 0);
+        O.o[1][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1], pb, O.o[1][rb], 0, 0, 0);
+      }
     }
   }
 }
@@ -324,53 +392,74 @@ __device__ __forceinline__ void mm_tile(WaveState& W, const uint8_t* tile, int t
 
 template <int FMT, bool PAGED>
 __device__ __forceinline__ void run_range(const DecodeParams& p, uint8_t* bf0, uint8_t* bf1, uint8_t* st0,
-                                          uint8_t* st1, int b, int n, int rg, int lt0, int lt1, int64_t slot) {
+                                          uint8_t* st1, const Shared& X, int b, int n, int rg, int lt0, int lt1,
+                                          int64_t slot) {
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
-  const int row_w0 = rg * kRowsPerGroup + wave * kRowsPerWave;  // first row of this wave
-  const bool active = row_w0 < p.rows;
-  const int row = row_w0 + lr;
-  const int rc = min(row, p.rows - 1);
+  const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, lr = lane & 31, lh = lane >> 5;
+  const int row0 = rg * kRowsPerGroup;                   // first row of this workgroup
+  const int rows_here = min(kRowsPerGroup, p.rows - row0);
+  const int nrb = (rows_here + 31) / 32;                 // row blocks with rows
+  const int my_row = wave * kQkRows + (lane & 15);       // score-phase row (in the group)
+  const bool active = wave * kQkRows < rows_here;        // this wavefront has score rows
+  const int rc = min(row0 + my_row, p.rows - 1);
 
-  WaveState W;
-  W.vis = max(n - p.q_len + rc / p.H + 1, 0);
-  W.m_used = -INFINITY;
-  W.l_sum = 0.f;
-  W.l_rnd = 0.f;
+  ScoreState S;
+  S.vis = (row0 + my_row < p.rows) ? max(n - p.q_len + rc / p.H + 1, 0) : 0;
+  S.m_used = -INFINITY;
+  S.l_sum = 0.f;
+  S.l_rnd = 0.f;
   {
     const uint16_t* qrow = p.q + ((int64_t)b * p.rows + rc) * kLatent;
     const uint16_t* prow = p.qpe + ((int64_t)b * p.rows + rc) * kRope;
 #pragma unroll
-    for (int k = 0; k < kKSteps; ++k) {
-      const uint16_t* src = (k < kLatent / 16) ? qrow + 16 * k + 8 * lh : prow + 16 * (k - kLatent / 16) + 8 * lh;
-      W.q[k] = *reinterpret_cast<const bf16x8*>(src);
+    for (int k = 0; k < kQkSteps; ++k) {
+      const int d = 32 * k + 8 * g;
+      const uint16_t* src = (d < kLatent) ? qrow + d : prow + (d - kLatent);
+      S.q[k] = *reinterpret_cast<const bf16x8*>(src);
     }
   }
 #pragma unroll
-  for (int d = 0; d < kDimBlocks; ++d) W.o[d] = f32x16{};
-  // QK operand: token lr, logical chunk 2k + lh.  (2k + lh) ^ s = 8(k >> 2) + ((2(k & 3) + lh) ^ s).
+  for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) W.qk_off[kk] = lr * kTileRowBytes + (((2 * kk + lh) ^ swz(lr)) << 4);
-  // V^T transpose reads: in a group of 16 lanes (g = lane / 16, j = lane % 16), lane j
-  // addresses token 16ks + 8e + 4(g >> 1) + j / 4 and dims 32d + 16(g & 1) + 4(j % 4)..+4;
-  // lane i of the group then receives dim 32d + 16(g & 1) + i of those four tokens.
+    for (int kk = 0; kk < 2; ++kk) {
+      const int t = 16 * tb + (lane & 15);
+      S.a_off[2 * tb + kk] = t * kTileRowBytes + (((4 * kk + g) ^ swz(t)) << 4);
+    }
+  S.p_off = my_row * kPRowPitch + 8 * g;
+
+  OutState O;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) O.o[db][rb] = f32x16{};
+  // transpose reads: in a group of 16 lanes (g, j = lane % 16), lane j addresses token
+  // 16ks + 8(g >> 1) + 4e + j / 4 and dims d0 + 16(g & 1) + 4(j % 4) .. +4; lane i of
+  // the group then receives dim d0 + 16(g & 1) + i of those four tokens.
   {
-    const int g = lane >> 4, j = lane & 15;
-    const int dlo = 16 * (g & 1) + 4 * (j & 3);  // dim inside the 32-dim block
+    const int j = lane & 15;
 #pragma unroll
-    for (int dp = 0; dp < 2; ++dp)
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int tok = 16 * ks + 8 * e + 4 * (g >> 1) + (j >> 2);
-          const int dim = 32 * dp + dlo;
-          W.pv_off[4 * dp + 2 * ks + e] = tile_off(tok, dim >> 3) + 2 * (dim & 7);
+          const int tok = 16 * ks + 8 * (g >> 1) + 4 * e + (j >> 2);
+          const int dim = kPvDims * wave + 32 * db + 16 * (g & 1) + 4 * (j & 3);
+          O.v_off[4 * db + 2 * ks + e] = tile_off(tok, dim >> 3) + 2 * (dim & 7);
         }
   }
+  O.p_off = lr * kPRowPitch + 16 * lh;
+
   const float score_scale = p.score_scale;
   const int nt = lt1 - lt0;
   Range R{&p, b, n};
+
+  // one tile: score phase, barrier, output phase
+  auto tile_step = [&](const uint8_t* tile, int i) {
+    score_tile(S, tile, X, (lt0 + i) * kTileTokens, score_scale, lane, active, my_row);
+    __syncthreads();
+    out_tile(O, tile, X, nrb, lane);
+  };
 
   if (nt > 0) {
     if (FMT == kFmtBf16) {
@@ -380,12 +469,12 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint8_t* bf0, u
         wait_dma();
         __syncthreads();
         if (i + 1 < nt) load_bf16_tile<PAGED>(R, (lt0 + i + 1) * kTileTokens, bf1, wave, lane);
-        if (active) mm_tile(W, bf0, (lt0 + i) * kTileTokens, score_scale, lh);
+        tile_step(bf0, i);
         if (++i >= nt) break;
         wait_dma();
         __syncthreads();
         if (i + 1 < nt) load_bf16_tile<PAGED>(R, (lt0 + i + 1) * kTileTokens, bf0, wave, lane);
-        if (active) mm_tile(W, bf1, (lt0 + i) * kTileTokens, score_scale, lh);
+        tile_step(bf1, i);
         if (++i >= nt) break;
       }
     } else {
@@ -408,40 +497,48 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint8_t* bf0, u
         __syncthreads();
         if (i + 2 < nt) load_raw(i + 2, st0);
         if (i + 1 < nt) dequant(st1, bf1);
-        if (active) mm_tile(W, bf0, (lt0 + i) * kTileTokens, score_scale, lh);
+        tile_step(bf0, i);
         if (++i >= nt) break;
         wait_dma();
         __syncthreads();
         if (i + 2 < nt) load_raw(i + 2, st1);
         if (i + 1 < nt) dequant(st0, bf0);
-        if (active) mm_tile(W, bf1, (lt0 + i) * kTileTokens, score_scale, lh);
+        tile_step(bf1, i);
         if (++i >= nt) break;
       }
     }
   }
-  __syncthreads();  // the next range reuses the buffers
 
-  // ---- epilogue: normalised partial and its log-sum-exp ----
-  if (active) {
-    const float l_tot = pair_sum(W.l_sum);
-    const float l_rnd = pair_sum(W.l_rnd);
+  // ---- epilogue: the score-phase owner of each row publishes 1/l and writes lse ----
+  {
+    const float l_tot = quad_sum(S.l_sum);
+    const float l_rnd = quad_sum(S.l_rnd);
     const bool ok = l_tot > 0.f;
-    const float inv = ok ? p.v_scale / l_rnd : 0.f;
-    const float lse = ok ? (W.m_used + __log2f(l_tot)) * kLn2 : -INFINITY;
-    if (row < p.rows) {
-      float* orow = p.o_part + slot * p.o_slot + (int64_t)row * p.o_row;
-#pragma unroll
-      for (int d = 0; d < kDimBlocks; ++d) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 val = {W.o[d][4 * g] * inv, W.o[d][4 * g + 1] * inv, W.o[d][4 * g + 2] * inv,
-                             W.o[d][4 * g + 3] * inv};
-          *reinterpret_cast<f32x4*>(orow + 32 * d + 8 * g + 4 * lh) = val;
-        }
-      }
-      if (lh == 0) p.lse_part[slot * p.l_slot + (int64_t)row * p.l_row] = lse;
+    if (g == 0) {
+      X.inv_l[my_row] = ok ? p.v_scale / l_rnd : 0.f;
+      if (row0 + my_row < p.rows)
+        p.lse_part[slot * p.l_slot + (int64_t)(row0 + my_row) * p.l_row] =
+            ok ? (S.m_used + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
   }
+  __syncthreads();
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int row = row0 + 32 * rb + lr;
+    if (rb < nrb && row < p.rows) {
+      const float inv = X.inv_l[32 * rb + lr];
+      float* orow = p.o_part + slot * p.o_slot + (int64_t)row * p.o_row + kPvDims * wave;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x16& o = O.o[db][rb];
+          const f32x4 val = {o[4 * q4] * inv, o[4 * q4 + 1] * inv, o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * q4 + 4 * lh) = val;
+        }
+    }
+  }
+  __syncthreads();  // the next range reuses the LDS buffers
 }
 
 // ------------------------------------------------------------------------------------
@@ -452,13 +549,17 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint8_t* bf0, u
 __global__ __launch_bounds__(kThreads) void decode_contig_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t bf0[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t bf1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[kPBufBytes];
+  __shared__ float alpha[kRowsPerGroup];
+  __shared__ float inv_l[kRowsPerGroup];
+  const Shared X{pbuf, alpha, inv_l};
   const int rg = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int t0 = j * p.kv_len_per_split;
   const int t1 = min(t0 + p.kv_len_per_split, p.S);
   const int lt0 = t0 / kTileTokens;
   const int lt1 = (t1 + kTileTokens - 1) / kTileTokens;
   // slot b*H*NS + j with row = head addresses o_part [B, H, NS, 512]
-  run_range<kFmtBf16, false>(p, bf0, bf1, nullptr, nullptr, b, p.S, rg, lt0, lt1,
+  run_range<kFmtBf16, false>(p, bf0, bf1, nullptr, nullptr, X, b, p.S, rg, lt0, lt1,
                              (int64_t)b * p.rows * p.num_splits + j);
 }
 
@@ -473,8 +574,12 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(const DecodePara
   __shared__ __attribute__((aligned(16))) uint8_t bf1[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t st0[StageBytes<FMT>::value];
   __shared__ __attribute__((aligned(16))) uint8_t st1[StageBytes<FMT>::value];
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[kPBufBytes];
+  __shared__ float alpha[kRowsPerGroup];
+  __shared__ float inv_l[kRowsPerGroup];
   __shared__ int pre[kMaxBatch + 1];
   __shared__ int wsum[kWaves];
+  const Shared X{pbuf, alpha, inv_l};
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int max_len = p.max_blocks * p.page_size;
 
@@ -532,7 +637,7 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(const DecodePara
     while (pre[b + 1] <= t) ++b;  // skip empty requests
     const int seg_end = min(t1, pre[b + 1]);
     const int n = min(max(p.seq_lens[b], 0), max_len);
-    run_range<FMT, true>(p, bf0, bf1, st0, st1, b, n, rg, t - pre[b], seg_end - pre[b], (int64_t)w + b);
+    run_range<FMT, true>(p, bf0, bf1, st0, st1, X, b, n, rg, t - pre[b], seg_end - pre[b], (int64_t)w + b);
     if (tid == 0 && rg == 0) {
       if (t == pre[b]) p.seg_first[b] = w;
       if (seg_end == pre[b + 1]) p.seg_last[b] = w;
