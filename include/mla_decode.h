@@ -112,7 +112,7 @@ size_t mla_paged_workspace_bytes(int B, int q_len, int H, int num_splits);
  *   lse_part [B, H, NS] fp32 (out)       lse_j (natural log; -inf for no token)
  * with NS = ceil(S_kv / kv_len_per_split); split j covers tokens
  * [j*L, min((j+1)*L, S_kv)).  kv_len_per_split must be a power of two >= 128 (the
- * page's assertions).  H: multiple of 16, <= 128.  1 <= B <= 65535; NS <= 65535. */
+ * page's assertions); sm_scale finite and >= 0.  H: multiple of 16, <= 128.  1 <= B <= 65535; NS <= 65535. */
 int mla_decode_splitkv(const uint16_t* q, const uint16_t* qpe, const uint16_t* kv,
                        const uint16_t* kpe, int B, int H, int S_kv, float sm_scale,
                        int kv_len_per_split, float* o_part, float* lse_part, void* stream);
@@ -166,7 +166,7 @@ int mla_paged_combine(const void* workspace, size_t workspace_bytes, const int32
  * are clamped on the device, so a violation gives wrong numbers, never an access outside
  * the cache or the table.  Constraints checked on the host: fmt valid; page_size 32 or
  * 64; page_stride_bytes a multiple of 16 and at least page_size * (1152, 576 or 324)
- * bytes; 1 <= q_len <= 8; H a multiple of 16, <= 128; 1 <= B <= 4096;
+ * bytes; sm_scale finite and >= 0; 1 <= q_len <= 8; H a multiple of 16, <= 128; 1 <= B <= 4096;
  * 1 <= num_splits <= 65536; B * max_blocks_per_seq * page_size < 2^31;
  * workspace_bytes >= mla_paged_workspace_bytes(B, q_len, H, num_splits). */
 int mla_paged_decode(const uint16_t* q, const uint16_t* qpe, const void* kv_cache, int fmt,

@@ -115,7 +115,7 @@ int mla_decode_splitkv(const uint16_t* q, const uint16_t* qpe, const uint16_t* k
   if (!aligned(q, 16) || !aligned(qpe, 16) || !aligned(kv, 16) || !aligned(kpe, 16) || !aligned(o_part, 16) ||
       !aligned(lse_part, 4))
     return MLA_ERR_INVALID_ARG;
-  if (B < 1 || S_kv < 1 || !isfinite(sm_scale)) return MLA_ERR_INVALID_ARG;
+  if (B < 1 || S_kv < 1 || !isfinite(sm_scale) || sm_scale < 0.f) return MLA_ERR_INVALID_ARG;
   if (H < 16 || H > MLA_MAX_HEADS || H % 16 != 0) return MLA_ERR_UNSUPPORTED;
   // the page's assertions: power of two and at least TILE_N = 128
   if (kv_len_per_split < 128 || (kv_len_per_split & (kv_len_per_split - 1)) != 0) return MLA_ERR_INVALID_ARG;
@@ -197,7 +197,7 @@ int paged_partials(const uint16_t* q, const uint16_t* qpe, const void* kv_cache,
   if (num_pages < 1 || max_blocks_per_seq < 1) return MLA_ERR_INVALID_ARG;
   if (page_stride_bytes < page_size * rb || page_stride_bytes % 16 != 0) return MLA_ERR_INVALID_ARG;
   if ((int64_t)B * max_blocks_per_seq * page_size >= ((int64_t)1 << 31)) return MLA_ERR_INVALID_ARG;
-  if (!isfinite(sm_scale)) return MLA_ERR_INVALID_ARG;
+  if (!isfinite(sm_scale) || sm_scale < 0.f) return MLA_ERR_INVALID_ARG;
   if (fmt == MLA_KV_FP8_E4M3 && !(isfinite(kv_scale) && kv_scale > 0.f)) return MLA_ERR_INVALID_ARG;
   PagedLayout L;
   const int st = check_paged_shape(B, q_len, H, num_splits, workspace, workspace_bytes, &L);

@@ -30,6 +30,7 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 #define LDS_AS __attribute__((address_space(3)))
 #define GLB_AS __attribute__((address_space(1)))
@@ -66,13 +67,6 @@ __device__ __forceinline__ unsigned pack_hi16(float lo, float hi) {
   return (__float_as_uint(hi) & 0xFFFF0000u) | (__float_as_uint(lo) >> 16);
 }
 
-// Four E4M3 codes (one dword) -> four bf16 (two dwords), exactly.
-__device__ __forceinline__ void fp8x4_to_bf16(unsigned w, unsigned& o0, unsigned& o1) {
-  f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  o0 = pack_hi16(a[0], a[1]);
-  o1 = pack_hi16(b[0], b[1]);
-}
 
 // E2M1 code (low 4 bits) -> float: 0, 0.5, 1, 1.5, 2, 3, 4, 6 with sign.
 __device__ __forceinline__ float e2m1_to_f32(unsigned c) {
@@ -134,9 +128,11 @@ __device__ __forceinline__ void dma4(const void* g, void* lds_base) {
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ------------------------------------------------------------------------------------
-// Tile sources.  Tokens past the end of the request are clamped to its last token
-// (their scores are masked, and a real row keeps every value finite); a 32-token tile
-// never crosses a page (page sizes 32 and 64), so one block-table entry serves a tile.
+// Tile sources.  Every global->LDS load instruction runs on all 64 lanes and moves 64
+// consecutive 16-byte chunks of the tile.  Tokens past the end of the request are clamped
+// to its last token (their scores are masked, and a real row keeps every value finite);
+// a 32-token tile never crosses a page (page sizes 32 and 64), so one block-table entry
+// serves a tile.
 // ------------------------------------------------------------------------------------
 
 struct Range {
@@ -209,6 +205,13 @@ __device__ __forceinline__ void load_nvfp4_raw(const Range& R, int tbase, uint8_
   }
 }
 
+// Four E4M3 codes (one dword) -> four bf16 (two dwords), exactly (hardware convert with
+// unit scale).
+__device__ __forceinline__ void fp8x4_to_bf16(unsigned w, unsigned& o0, unsigned& o1) {
+  o0 = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false));
+  o1 = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true));
+}
+
 // Raw staging -> bf16 tile.
 __device__ __forceinline__ void dequant_fp8(const uint8_t* st, uint8_t* tile, int tid) {
 #pragma unroll
@@ -274,13 +277,15 @@ struct ScoreState {
   float l_sum;         // this lane's share of sum p (unrounded): for the LSE
   float l_rnd;         // this lane's share of sum bf16(p): normalises O
   int vis;             // tokens the row may see
-  int a_off[4];        // KV operand offsets, [2 tb + (k & 1)] + 128 (k >> 1)
+  int a_off;           // KV operand offset of token l%16, chunk l/16 (K-step 0, token block 0);
+                       // K-step k: ^ 64 (k & 1), + 128 (k >> 1); token block 1: + 16 rows
   int p_off;           // P write offset: row * pitch + 8 (l / 16), + 32 tb
 };
 
 struct OutState {
   f32x16 o[2][4];      // o[db][rb]: row 32rb + l%32, dims 64w + 32db + 8(v/4) + 4(l/32) + v%4
-  int v_off[8];        // transpose-read offsets [4 db + 2 ks + e]
+  int v_off[2];        // transpose-read offsets for e = 0, 1 (db = 0, ks = 0); db = 1: ^ 64,
+                       // ks = 1: + 16 rows
   int p_off;           // P^T operand: row l%32, tokens 16ks + 8(l/32): + 32*pitch*rb + 32 ks
 };
 
@@ -296,31 +301,33 @@ __device__ __forceinline__ float quad_sum(float x) {
   return pair_sum(x);
 }
 
-// Score phase of one tile for this wavefront's 16 rows.
-__device__ __forceinline__ void score_tile(ScoreState& S, const uint8_t* tile, const Shared& X, int tbase,
-                                           float score_scale, int lane, bool active, int row_in_group) {
+// Score phase of one tile for this wavefront's 16 rows.  `full`: every token of the tile
+// is visible to every row of this wavefront, so no mask is needed.  c = score scale
+// (log2 units, >= 0).
+__device__ __forceinline__ void score_tile(ScoreState& S, const uint8_t* tile, const Shared& X, int tbase, float c,
+                                           int lane, bool active, bool full, int row_in_group) {
   const int g = lane >> 4;
   f32x4 s0 = f32x4{}, s1 = f32x4{};
   if (active) {
 #pragma unroll
     for (int k = 0; k < kQkSteps; ++k) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(tile + S.a_off[0 + (k & 1)] + 128 * (k >> 1));
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(tile + S.a_off[2 + (k & 1)] + 128 * (k >> 1));
+      const int off = (S.a_off ^ (64 * (k & 1))) + 128 * (k >> 1);
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(tile + off);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(tile + off + 16 * kTileRowBytes);
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, S.q[k], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, S.q[k], s1, 0, 0, 0);
     }
   }
-  // lane holds row l%16, tokens tbase + 16 tb + 4(l/16) + v
-  float x[8];
-  float mt = -INFINITY;
+  // lane holds row l%16, raw scores of tokens tbase + 16 tb + 4(l/16) + v
+  float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  const int lim = S.vis - tbase - 4 * g;  // token j of this lane (16 tb + v) is visible iff j < lim
+  if (!full) {
 #pragma unroll
-  for (int v = 0; v < 8; ++v) {
-    const int tok = tbase + 16 * (v >> 2) + 4 * g + (v & 3);
-    const float sv = (v < 4) ? s0[v & 3] : s1[v & 3];
-    x[v] = (active && tok < S.vis) ? sv * score_scale : -INFINITY;
-    mt = fmaxf(mt, x[v]);
+    for (int v = 0; v < 8; ++v) x[v] = (16 * (v >> 2) + (v & 3) < lim) ? x[v] : -INFINITY;
   }
+  float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
   mt = quad_max(mt);
+  mt = (mt == -INFINITY) ? -INFINITY : mt * c;
   const bool need = mt > S.m_used + kTau;
   float alpha = 1.0f;
   if (__any(need)) {
@@ -330,17 +337,22 @@ __device__ __forceinline__ void score_tile(ScoreState& S, const uint8_t* tile, c
     S.l_rnd *= alpha;
     S.m_used = m_new;
   }
-  const float msafe = (S.m_used == -INFINITY) ? 0.f : S.m_used;
-  unsigned pk[4];
+  const float nm = (S.m_used == -INFINITY) ? 0.f : -S.m_used;
+  float e[8];
 #pragma unroll
-  for (int v = 0; v < 8; v += 2) {
-    const float e0 = __builtin_amdgcn_exp2f(x[v] - msafe);
-    const float e1 = __builtin_amdgcn_exp2f(x[v + 1] - msafe);
-    const __bf16 b0 = (__bf16)e0, b1 = (__bf16)e1;
-    S.l_sum += e0 + e1;
-    S.l_rnd += (float)b0 + (float)b1;
-    pk[v >> 1] = (unsigned)__builtin_bit_cast(unsigned short, b0) |
-                 ((unsigned)__builtin_bit_cast(unsigned short, b1) << 16);
+  for (int v = 0; v < 8; ++v) e[v] = __builtin_amdgcn_exp2f(fmaf(x[v], c, nm));
+  if (!full) {
+#pragma unroll
+    for (int v = 0; v < 8; ++v) e[v] = (16 * (v >> 2) + (v & 3) < lim) ? e[v] : 0.f;
+  }
+  S.l_sum += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+  unsigned pk[4];
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const bf16x2 pr = {(__bf16)e[2 * v], (__bf16)e[2 * v + 1]};
+    S.l_rnd = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, S.l_rnd, false);
+    pk[v] = __builtin_bit_cast(unsigned, pr);
   }
   typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
   *reinterpret_cast<u32x2*>(X.pbuf + S.p_off) = u32x2{pk[0], pk[1]};
@@ -348,8 +360,11 @@ __device__ __forceinline__ void score_tile(ScoreState& S, const uint8_t* tile, c
   if (g == 0) X.alpha[row_in_group] = alpha;
 }
 
-// Output phase of one tile for this wavefront's 64 dims of the first nrb row blocks.
-__device__ __forceinline__ void out_tile(OutState& O, const uint8_t* tile, const Shared& X, int nrb, int lane) {
+// Output phase of one tile for this wavefront's 64 dims of the first nrb row blocks;
+// `side` is independent work (the next tile's dequantisation) issued between the MFMAs.
+template <class Side>
+__device__ __forceinline__ void out_tile(OutState& O, const uint8_t* tile, const Shared& X, int nrb, int lane,
+                                         Side side) {
   const int lr = lane & 31;
   float al[4];
   bool resc = false;
@@ -365,20 +380,22 @@ __device__ __forceinline__ void out_tile(OutState& O, const uint8_t* tile, const
       O.o[1][rb] *= al[rb];
     }
   }
+  side();
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     bf16x8 va[2];
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(tile + O.v_off[4 * db + 2 * ks]));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(tile + O.v_off[4 * db + 2 * ks + 1]));
+      const int o0 = (O.v_off[0] ^ (64 * db)) + 16 * kTileRowBytes * ks;
+      const int o1 = (O.v_off[1] ^ (64 * db)) + 16 * kTileRowBytes * ks;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(tile + o0));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(tile + o1));
       va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       if (rb < nrb) {
-        const bf16x8 pb =
-            *reinterpret_cast<const bf16x8*>(X.pbuf + O.p_off + 32 * kPRowPitch * rb + 32 * ks);
+        const bf16x8 pb = *reinterpret_cast<const bf16x8*>(X.pbuf + O.p_off + 32 * kPRowPitch * rb + 32 * ks);
         O.o[0][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0], pb, O.o[0][rb], 0, 0, 0);
         O.o[1][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1], pb, O.o[1][rb], 0, 0, 0);
       }
@@ -404,7 +421,12 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint8_t* bf0, u
   const int rc = min(row0 + my_row, p.rows - 1);
 
   ScoreState S;
-  S.vis = (row0 + my_row < p.rows) ? max(n - p.q_len + rc / p.H + 1, 0) : 0;
+  // rows past the end of the problem repeat the last row: finite values, never stored
+  S.vis = max(n - p.q_len + rc / p.H + 1, 0);
+  // fewest tokens any row of this wavefront sees: tiles below it need no mask
+  int min_vis = S.vis;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) min_vis = min(min_vis, __shfl_xor(min_vis, o));
   S.m_used = -INFINITY;
   S.l_sum = 0.f;
   S.l_rnd = 0.f;
@@ -418,13 +440,9 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint8_t* bf0, u
       S.q[k] = *reinterpret_cast<const bf16x8*>(src);
     }
   }
-#pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int t = 16 * tb + (lane & 15);
-      S.a_off[2 * tb + kk] = t * kTileRowBytes + (((4 * kk + g) ^ swz(t)) << 4);
-    }
+  // chunk 4k + g of token t: (4k + g) ^ swz(t) = 8(k >> 1) + ((4(k & 1) + g) ^ swz(t)), and
+  // swz(t + 16) = swz(t); byte offsets of whole 128-byte groups never have bit 6 set
+  S.a_off = (lane & 15) * kTileRowBytes + ((g ^ swz(lane & 15)) << 4);
   S.p_off = my_row * kPRowPitch + 8 * g;
 
   OutState O;
@@ -435,18 +453,16 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint8_t* bf0, u
   // transpose reads: in a group of 16 lanes (g, j = lane % 16), lane j addresses token
   // 16ks + 8(g >> 1) + 4e + j / 4 and dims d0 + 16(g & 1) + 4(j % 4) .. +4; lane i of
   // the group then receives dim d0 + 16(g & 1) + i of those four tokens.
+  // (dims 32 apart are 4 chunks apart: chunk ^ 4 flips byte-offset bit 6; tokens 16
+  // apart share the swizzle)
   {
     const int j = lane & 15;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int tok = 16 * ks + 8 * (g >> 1) + 4 * e + (j >> 2);
-          const int dim = kPvDims * wave + 32 * db + 16 * (g & 1) + 4 * (j & 3);
-          O.v_off[4 * db + 2 * ks + e] = tile_off(tok, dim >> 3) + 2 * (dim & 7);
-        }
+    for (int e = 0; e < 2; ++e) {
+      const int tok = 8 * (g >> 1) + 4 * e + (j >> 2);
+      const int dim = kPvDims * wave + 16 * (g & 1) + 4 * (j & 3);
+      O.v_off[e] = tile_off(tok, dim >> 3) + 2 * (dim & 7);
+    }
   }
   O.p_off = lr * kPRowPitch + 16 * lh;
 
@@ -454,12 +470,14 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint8_t* bf0, u
   const int nt = lt1 - lt0;
   Range R{&p, b, n};
 
-  // one tile: score phase, barrier, output phase
-  auto tile_step = [&](const uint8_t* tile, int i) {
-    score_tile(S, tile, X, (lt0 + i) * kTileTokens, score_scale, lane, active, my_row);
+  // one tile: score phase, barrier, output phase (with `side` work issued inside it)
+  auto tile_step = [&](const uint8_t* tile, int i, auto side) {
+    const int tbase = (lt0 + i) * kTileTokens;
+    score_tile(S, tile, X, tbase, score_scale, lane, active, active && tbase + kTileTokens <= min_vis, my_row);
     __syncthreads();
-    out_tile(O, tile, X, nrb, lane);
+    out_tile(O, tile, X, nrb, lane, side);
   };
+  auto nothing = [] {};
 
   if (nt > 0) {
     if (FMT == kFmtBf16) {
@@ -469,16 +487,18 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint8_t* bf0, u
         wait_dma();
         __syncthreads();
         if (i + 1 < nt) load_bf16_tile<PAGED>(R, (lt0 + i + 1) * kTileTokens, bf1, wave, lane);
-        tile_step(bf0, i);
+        tile_step(bf0, i, nothing);
         if (++i >= nt) break;
         wait_dma();
         __syncthreads();
         if (i + 1 < nt) load_bf16_tile<PAGED>(R, (lt0 + i + 1) * kTileTokens, bf0, wave, lane);
-        tile_step(bf1, i);
+        tile_step(bf1, i, nothing);
         if (++i >= nt) break;
       }
     } else {
-      // raw tiles two ahead of the MFMA work, dequantised one ahead
+      // raw tiles are loaded two ahead of the MFMA work and dequantised one ahead, during
+      // the output phase of the current tile (a dequantisation past the last tile only
+      // rewrites an unused buffer)
       auto load_raw = [&](int i, uint8_t* st) {
         if (FMT == kFmtFp8) load_fp8_raw(R, (lt0 + i) * kTileTokens, st, wave, lane);
         else load_nvfp4_raw(R, (lt0 + i) * kTileTokens, st, wave, lane);
@@ -496,14 +516,12 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint8_t* bf0, u
         wait_dma();
         __syncthreads();
         if (i + 2 < nt) load_raw(i + 2, st0);
-        if (i + 1 < nt) dequant(st1, bf1);
-        tile_step(bf0, i);
+        tile_step(bf0, i, [&] { dequant(st1, bf1); });
         if (++i >= nt) break;
         wait_dma();
         __syncthreads();
         if (i + 2 < nt) load_raw(i + 2, st1);
-        if (i + 1 < nt) dequant(st0, bf0);
-        tile_step(bf1, i);
+        tile_step(bf1, i, [&] { dequant(st0, bf0); });
         if (++i >= nt) break;
       }
     }

@@ -102,6 +102,7 @@ def _paged(**kw):
     (dict(kv_scale=0.0), mla.MLA_ERR_INVALID_ARG),
     (dict(kv_scale=float("nan")), mla.MLA_ERR_INVALID_ARG),
     (dict(sm=float("inf")), mla.MLA_ERR_INVALID_ARG),
+    (dict(sm=-0.125), mla.MLA_ERR_INVALID_ARG),
     (dict(ws_bytes=1000), mla.MLA_ERR_WORKSPACE_TOO_SMALL),
 ])
 def test_paged_decode_rejects(kw, status):
@@ -135,6 +136,7 @@ def _contig(**kw):
     (dict(H=8), mla.MLA_ERR_UNSUPPORTED),
     (dict(H=136), mla.MLA_ERR_UNSUPPORTED),
     (dict(sm=float("nan")), mla.MLA_ERR_INVALID_ARG),
+    (dict(sm=-1.0), mla.MLA_ERR_INVALID_ARG),
 ])
 def test_decode_splitkv_rejects(kw, status):
     assert _contig(**kw) == status
