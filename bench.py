@@ -57,9 +57,10 @@ def algorithmic_counts(w):
 
 
 def traffic_from_profiles(workload: str, src_hash: str):
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"decode_paged_{workload}_counters.json")
+    """HBM bytes per decode launch (FETCH_SIZE and WRITE_SIZE, each scaled by what the
+    counter reads for a copy kernel of known size) from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_paged.{workload}.counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -94,6 +95,18 @@ def cpu_baseline(w, budget_s: float):
             "sample": f"requests 0..{used - 1} of the same batch ({used} of {w.B}), float64 numpy, {dt:.1f} s"}
 
 
+def copy_calibration(torch, dev, nbytes: int, steps: int):
+    """Known-traffic kernels for the HBM counters: fill writes nbytes, copy reads nbytes
+    and writes nbytes.  Buffers are far larger than the last-level caches."""
+    x = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(steps):
+        x.fill_(7)
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "steps": steps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +116,9 @@ def main():
     ap.add_argument("--num-splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="instead of the decode, run torch's fill and copy kernels on buffers of this many MiB "
+                         "(known HBM bytes, used to scale the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this decode path is built and measured on a single MI355X "
@@ -116,6 +132,9 @@ def main():
     from workloads import gen
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration_mib:
+        copy_calibration(torch, dev, args.copy_calibration_mib << 20, args.steps)
+        return
     log(f"[bench] generating {args.workload}")
     w = gen.make_workload(args.workload)
     if w.__class__.__name__ != "PagedInputs":
