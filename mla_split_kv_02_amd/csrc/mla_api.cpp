@@ -214,6 +214,7 @@ int paged_partials(const uint16_t* q, const uint16_t* qpe, const void* kv_cache,
   p.max_blocks = max_blocks_per_seq;
   p.seq_lens = seq_lens;
   p.page_size = page_size;
+  p.page_shift = page_size == 64 ? 6 : 5;
   p.num_pages = num_pages;
   p.B = B;
   p.q_len = q_len;

@@ -12,12 +12,10 @@ constexpr int kRope = 64;     // rope key width
 constexpr int kRow = 576;     // one cache token
 
 constexpr int kTileTokens = 32;    // tokens per KV tile streamed through LDS
-constexpr int kWaves = 8;          // wavefronts per workgroup (two per SIMD)
+constexpr int kWaves = 4;          // wavefronts per workgroup (one per SIMD)
 constexpr int kThreads = 64 * kWaves;
-constexpr int kQkRows = 16;        // query rows whose scores one wavefront computes
-constexpr int kPvDims = 64;        // output dims one wavefront accumulates, for every row
-constexpr int kRowsPerGroup = kQkRows * kWaves;  // query rows (query x head) per workgroup: 128
-constexpr int kMaxBatch = 4096;
+constexpr int kWaveRows = 32;      // query rows one wavefront owns
+constexpr int kRowsPerGroup = kWaveRows * kWaves;  // query rows (query x head) per workgroup: 128
 
 constexpr int kFmtBf16 = 0;
 constexpr int kFmtFp8 = 1;
@@ -39,6 +37,7 @@ struct DecodeParams {
   int max_blocks;
   const int32_t* seq_lens;
   int page_size;
+  int page_shift;       // log2(page_size)
   int num_pages;
   // problem
   int B, q_len, H;

@@ -1,19 +1,26 @@
 // gfx950 kernels for absorbed-MLA split-KV decode.
 //
-// Decode kernel.  One workgroup = 8 wavefronts (two per SIMD) = up to 128 query rows
-// (query x head) of one request and one token range.  The workgroup streams the
-// range's KV tiles (32 tokens x 576 values) from HBM straight into LDS with global->LDS
-// loads (no register staging) and dequantises FP8 / NVFP4 tiles in LDS to bf16.  Each
-// tile then takes two phases separated by a workgroup barrier:
-//   scores:  wavefront w computes S^T[32 tok x 16 rows] for rows 16w..16w+15 with MFMA
-//            16x16x32 (its Q^T rows stay in registers), applies the mask and the online
-//            softmax, and publishes P (bf16) and the rows' rescale factors in LDS;
-//   output:  wavefront w accumulates O^T[64 dims x 128 rows] for dims 64w..64w+63 with
-//            MFMA 32x32x16, V^T read from the token-major tile with the LDS transpose
-//            load and P^T from LDS.
-// All heads of a request share one latent (absorbed MLA), so every row of the group
-// runs against the same LDS tile (the TileGym page's kernel instead re-reads the tile
-// once per group of 16 heads).
+// Decode kernel.  One workgroup = 4 wavefronts, one per SIMD, so every wavefront has its
+// SIMD's whole register file: its output accumulators (O^T, 512 dims x 32 rows, fp32 =
+// 256 registers) live in the accumulation registers and its Q^T operand (32 rows x 576
+// dims, bf16 = 144 registers) in the vector registers.  A workgroup owns up to 128 query
+// rows (query x head) of one request and one token range; wavefront w owns rows
+// 32w .. 32w+31 and does all of their arithmetic:
+//   scores   S^T[32 tok x 32 rows] = K . Q^T         36 MFMA 32x32x16, K from LDS
+//   softmax  online, base 2, lazy rescale; P^T is moved into the operand layout of the
+//            output product with cross-half lane swaps, without touching LDS
+//   output   O^T[512 x 32 rows] += V^T . P^T          32 MFMA 32x32x16, V^T read from the
+//                                                      token-major tile with the LDS
+//                                                      transpose read
+// All heads of a request share one latent (absorbed MLA), so the four wavefronts work on
+// the same LDS tile, which crosses HBM once per workgroup (the TileGym page's kernel
+// re-reads it once per group of 16 heads).  The tile buffers are the only shared state:
+// one workgroup barrier per tile hands them over.
+//
+// Per tile i: the global->LDS loads of a later tile are issued first; then the scores of
+// tile i, with the dequantisation (FP8 / NVFP4) of tile i+1 in the same instruction
+// stream; then the softmax of tile i, with the output product of tile i-1 in the same
+// stream, so the matrix cores have work while the softmax runs; then one barrier.
 //
 // Combine kernels.  One wavefront per output row merges the partials with the split-K
 // log-sum-exp reduce (TileGym page, forward: splitk_reduce).
@@ -25,67 +32,85 @@
 namespace mla {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 #define LDS_AS __attribute__((address_space(3)))
-#define GLB_AS __attribute__((address_space(1)))
+typedef LDS_AS uint8_t* lds_ptr;
 
-constexpr int kKSteps = kRow / 16;                        // 36 K-steps of 16 for QK
+constexpr int kKSteps = kRow / 16;                        // 36 K-steps of 16 dims (scores)
+constexpr int kDimBlocks = kLatent / 32;                  // 16 output blocks of 32 dims
 constexpr int kRowChunks = kRow * 2 / 16;                 // 72 bf16 chunks of 16 B per token
 constexpr int kTileRowBytes = kRowChunks * 16;            // 1152
 constexpr int kTileBytes = kTileTokens * kTileRowBytes;   // 36864
-constexpr int kDimBlocks = kLatent / 32;                  // 16 output blocks of 32 dims
-constexpr int kFp8Chunks = kTileTokens * (kRow / 16);     // 1152 chunks of 16 codes
+constexpr int kBf16Loads = kTileBytes / 1024;             // 36 wavefront loads of 1 KiB
+constexpr int kFp8RawBytes = kTileTokens * kRow;          // 18432
+constexpr int kFp8Loads = kFp8RawBytes / 1024;            // 18
 constexpr int kNvDataBytes = kRow / 2;                    // 288 packed E2M1 bytes per token
 constexpr int kNvScaleBytes = kRow / 16;                  // 36 E4M3 scales per token
-constexpr int kNvChunks = kTileTokens * kNvDataBytes / 16;        // 576
-constexpr int kNvScaleWords = kTileTokens * kNvScaleBytes / 4;    // 288
-constexpr int kNvStageData = kTileTokens * kNvDataBytes;          // 9216
+constexpr int kNvRawData = kTileTokens * kNvDataBytes;    // 9216
+constexpr int kNvDataLoads = kNvRawData / 1024;           // 9
+constexpr int kNvScaleWords = kTileTokens * kNvScaleBytes / 4;   // 288
+constexpr int kNvScaleLoads = (kNvScaleWords + 63) / 64;          // 5 (the last one 32 words)
+constexpr int kNvRawBytes = kNvRawData + 256 * kNvScaleLoads;     // 10496
 constexpr float kTau = 8.0f;   // lazy rescale threshold (log2 units)
 constexpr float kLn2 = 0.69314718055994531f;
 
-template <int FMT>
-struct StageBytes {
-  static constexpr int value = FMT == kFmtFp8 ? kFp8Chunks * 16
-                               : FMT == kFmtNvfp4 ? kNvStageData + kTileTokens * kNvScaleBytes
-                                                  : 16;
+// Buffers and load distance per cache format.  Tile i sits in bf16 buffer i % kTiles; raw
+// tile i (FP8 / NVFP4) in staging buffer i % kRaw.  In iteration i the loads of tile
+// i + kAhead are issued.
+template <int FMT> struct Pipe;
+template <> struct Pipe<kFmtBf16> {
+  static constexpr int kTiles = 4, kRaw = 0, kRawBytes = 0, kAhead = 2, kLoads = kBf16Loads;
 };
+template <> struct Pipe<kFmtFp8> {
+  static constexpr int kTiles = 3, kRaw = 2, kRawBytes = kFp8RawBytes, kAhead = 2, kLoads = kFp8Loads;
+};
+template <> struct Pipe<kFmtNvfp4> {
+  static constexpr int kTiles = 3, kRaw = 3, kRawBytes = kNvRawBytes, kAhead = 3,
+                       kLoads = kNvDataLoads + kNvScaleLoads;
+};
+template <int FMT> constexpr int smem_bytes() {
+  return Pipe<FMT>::kTiles * kTileBytes + Pipe<FMT>::kRaw * Pipe<FMT>::kRawBytes;
+}
 
-// Byte offset of 16-byte chunk c (0..71) of token row r in a bf16 tile.  The chunk
-// index is XOR-swizzled inside its aligned group of 8 (72 = 9 x 8) so that MFMA operand
-// reads of consecutive token rows, 1152 B apart, spread over the LDS banks.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int tile_off(int r, int c) { return r * kTileRowBytes + ((c ^ swz(r)) << 4); }
+// Byte offset of 16-byte chunk c (0..71) of token row r in a bf16 tile.  The tile is
+// nine 4 KiB groups, one per 8 chunks (128 bytes) of every row: group c / 8 holds
+// [32 rows][8 chunks], and inside a row the chunk position is XOR-swizzled with swz(r).
+// Every global->LDS load instruction then fills one kilobyte of one group (8 rows), so
+// each lane's source address is one per-tile base plus a multiple of 128 bytes.
+// The swizzle keeps the three LDS access patterns free of bank conflicts (whether the
+// LDS serves 16 or 32 lanes of a 16-byte access per cycle):
+//   scores: rows 0..31 at one logical chunk  -> for any 8 rows of one parity within 16,
+//           and for rows r, r + 4, .., r + 28, the positions differ;
+//   output: transpose reads of rows t..t+3 and t+8..t+11 at chunks 0..3 -> rows two or
+//           eight apart land in opposite halves of the 8-chunk group (position bit 2);
+//   dequantisation writes: rows r, r+1 at all 8 chunks of a group.
+// With u = (r / 2) % 8: position bit 2 = u0 ^ u2 ^ (r / 16) % 2, bits 1..0 = (u2, u1).
+constexpr int kGroupBytes = kTileTokens * 128;            // 4096
+__device__ __forceinline__ int swz(int r) { return ((((r >> 1) ^ (r >> 3) ^ (r >> 4)) & 1) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return kGroupBytes * (c >> 3) + 128 * r + (((c & 7) ^ swz(r)) << 4);
+}
+
+// ------------------------------------------------------------------------------------
+// Conversions
+// ------------------------------------------------------------------------------------
+
+// Four E4M3 codes (one dword) -> four bf16 (two dwords), exactly (hardware convert with
+// unit scale).
+__device__ __forceinline__ void fp8x4_to_bf16(unsigned w, unsigned& o0, unsigned& o1) {
+  o0 = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false));
+  o1 = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true));
+}
 
 __device__ __forceinline__ unsigned pack_hi16(float lo, float hi) {
   // bf16 pair from two floats whose low 16 bits are zero (exact conversion)
   return (__float_as_uint(hi) & 0xFFFF0000u) | (__float_as_uint(lo) >> 16);
-}
-
-
-// E2M1 code (low 4 bits) -> float: 0, 0.5, 1, 1.5, 2, 3, 4, 6 with sign.
-__device__ __forceinline__ float e2m1_to_f32(unsigned c) {
-  unsigned m = c & 7u;
-  float mag = (m >= 2u) ? __uint_as_float((m << 22) + 0x3F000000u) : (m ? 0.5f : 0.0f);
-  return (c & 8u) ? -mag : mag;
-}
-
-// Eight E2M1 codes (one dword, even value in the low nibble) times one scale -> eight
-// bf16 (four dwords).  The products have at most 6 significant bits: exact in bf16.
-__device__ __forceinline__ u32x4 fp4x8_to_bf16(unsigned w, float s) {
-  u32x4 out;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float lo = e2m1_to_f32(w >> (8 * i)) * s;
-    float hi = e2m1_to_f32(w >> (8 * i + 4)) * s;
-    out[i] = pack_hi16(lo, hi);
-  }
-  return out;
 }
 
 __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
@@ -95,8 +120,12 @@ __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
   return (unsigned short)(u >> 16);
 }
 
-// Combine the values of lanes l and l ^ 32 with one cross-half lane swap: r[0] holds the
-// low half's value in both halves, r[1] the high half's.
+// ------------------------------------------------------------------------------------
+// Lane reductions
+// ------------------------------------------------------------------------------------
+
+// Values of lanes l and l ^ 32 combined with one cross-half lane swap (r[0] holds the low
+// half's value in both halves, r[1] the high half's).
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -105,7 +134,6 @@ __device__ __forceinline__ float pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
@@ -117,444 +145,678 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// 16 bytes (or 4) per lane from global memory into LDS at lds_base + lane * size; the
-// LDS base is the same for the whole wavefront.
-__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const GLB_AS void*)g, (LDS_AS void*)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const GLB_AS void*)g, (LDS_AS void*)lds_base, 4, 0, 0);
-}
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // ------------------------------------------------------------------------------------
-// Tile sources.  Every global->LDS load instruction runs on all 64 lanes and moves 64
-// consecutive 16-byte chunks of the tile.  Tokens past the end of the request are clamped
-// to its last token (their scores are masked, and a real row keeps every value finite);
-// a 32-token tile never crosses a page (page sizes 32 and 64), so one block-table entry
-// serves a tile.
+// Global -> LDS loads.  Each instruction runs on all 64 lanes and writes 16 (or 4) bytes
+// per lane at LDS address lds + 16 * lane (4 * lane).  They are issued as inline assembly
+// so that the compiler adds no waits of its own for them; every consumer waits with
+// wait_vmcnt and a workgroup barrier.  The "s" forms take a wavefront-uniform 64-bit
+// base and a per-lane 32-bit byte offset.
 // ------------------------------------------------------------------------------------
 
-struct Range {
+__device__ __forceinline__ uint32_t lds_addr(lds_ptr p) { return (uint32_t)(uintptr_t)p; }
+template <class T>
+__device__ __forceinline__ LDS_AS T* at(uint32_t a) { return (LDS_AS T*)(uintptr_t)a; }
+
+__device__ __forceinline__ void dma16_s(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4_s(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma16_v(const void* src, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+// Wait until at most n of this wavefront's vector-memory operations are outstanding
+// (they complete in issue order).  n is wavefront-uniform.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+#define MLA_VMCNT_CASE(k) \
+  case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+  switch (n) {
+    MLA_VMCNT_CASE(1) MLA_VMCNT_CASE(2) MLA_VMCNT_CASE(3) MLA_VMCNT_CASE(4) MLA_VMCNT_CASE(5)
+    MLA_VMCNT_CASE(6) MLA_VMCNT_CASE(7) MLA_VMCNT_CASE(8) MLA_VMCNT_CASE(9) MLA_VMCNT_CASE(10)
+    MLA_VMCNT_CASE(11) MLA_VMCNT_CASE(12) MLA_VMCNT_CASE(13) MLA_VMCNT_CASE(14) MLA_VMCNT_CASE(15)
+    MLA_VMCNT_CASE(16) MLA_VMCNT_CASE(17) MLA_VMCNT_CASE(18)
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+#undef MLA_VMCNT_CASE
+}
+
+// ------------------------------------------------------------------------------------
+// Tile sources.  Tokens past the end of the request are clamped to its last token
+// (their scores are masked, and a real row keeps every value finite); a 32-token tile
+// never crosses a page (page sizes 32 and 64), so one block-table entry serves a tile.
+// Load instruction j of a tile is issued by wavefront j % 4, as its (j / 4)-th; every
+// lane keeps one source row for the whole tile, and its source address moves by a
+// fixed stride from one of its instructions to the next (added to the uniform base).
+// ------------------------------------------------------------------------------------
+
+struct Src {
   const DecodeParams* p;
-  int b;   // request
-  int n;   // its tokens
+  int b;  // request
+  int n;  // its tokens (>= 1 whenever a tile is loaded)
 };
 
-__device__ __forceinline__ const uint8_t* tile_page(const Range& R, int tbase) {
-  const DecodeParams& p = *R.p;
-  int page = p.block_tables[(int64_t)R.b * p.max_blocks + tbase / p.page_size];
+// Page holding tile tb (clamped into the cache) and the tile's first row in it.
+__device__ __forceinline__ const uint8_t* tile_page(const Src& S, int tb, int& row_in_page) {
+  const DecodeParams& p = *S.p;
+  int page = p.block_tables[(int64_t)S.b * p.max_blocks + (tb >> p.page_shift)];
   page = min(max(page, 0), p.num_pages - 1);
+  row_in_page = tb & (p.page_size - 1);
   return p.cache + (int64_t)page * p.page_stride;
 }
 
-// bf16 rows straight into the swizzled tile: LDS chunk position q of row r holds
-// logical chunk q ^ swz(r).  2304 chunks = 36 wave loads, 9 per wavefront.
+// bf16 rows straight into the tile.  Instruction j = 4m + w fills group m, rows 8w ..
+// 8w+7: lane l takes row 8w + l/8 and the chunk whose swizzled position is l % 8.
 template <bool PAGED>
-__device__ __forceinline__ void load_bf16_tile(const Range& R, int tbase, uint8_t* tile, int wave, int lane) {
-  const DecodeParams& p = *R.p;
-  const uint8_t* pg = PAGED ? tile_page(R, tbase) : nullptr;
-  for (int j = wave; j < kTileTokens * kRowChunks / 64; j += kWaves) {
-    const int k = 64 * j + lane;
-    const int r = k / kRowChunks, pos = k % kRowChunks;
-    const int c = pos ^ swz(r);
-    const int tok = min(tbase + r, R.n - 1);
-    const void* src;
-    if (PAGED) {
-      src = pg + (int64_t)(tok % p.page_size) * (2 * kRow) + 16 * c;
+__device__ __forceinline__ void load_bf16_tile(const Src& S, int tb, uint32_t tile, int wave, int lane) {
+  const DecodeParams& p = *S.p;
+  const int r = 8 * wave + (lane >> 3);
+  const int tok = min(tb + r, S.n - 1);
+  const int cpos = ((lane & 7) ^ swz(r)) << 4;  // byte offset of the chunk inside its group of 8
+  const uint32_t lds = tile + 1024 * wave;
+  if (PAGED) {
+    int rip;
+    const uint8_t* pg = tile_page(S, tb, rip);
+    const uint32_t voff = (uint32_t)((rip + tok - tb) * (2 * kRow) + cpos);
+#pragma unroll
+    for (int m = 0; m < 9; ++m) dma16_s(pg + 128 * m, voff, lds + kGroupBytes * m);
+  } else {
+    const int64_t t0 = (int64_t)S.b * p.S + tb;
+    const uint8_t* kv = reinterpret_cast<const uint8_t*>(p.kv + t0 * kLatent);
+    const uint8_t* kpe = reinterpret_cast<const uint8_t*>(p.kpe + t0 * kRope);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) dma16_s(kv + 128 * m, (uint32_t)((tok - tb) * (2 * kLatent) + cpos), lds + kGroupBytes * m);
+    dma16_s(kpe, (uint32_t)((tok - tb) * (2 * kRope) + cpos), lds + kGroupBytes * 8);
+  }
+}
+
+// FP8 rows, raw.  Staging layout: chunk c (16 codes) of row r at 2048 (c / 4) + 64 r +
+// 16 (c % 4).  Instruction j = 4m + w covers chunk group j / 2 of rows 16 (j % 2) ..:
+// lane l takes row 16 (w % 2) + l / 4 and chunk 4 (w / 2 + 2m) + l % 4.
+__device__ __forceinline__ void load_fp8_raw(const Src& S, int tb, uint32_t st, int wave, int lane) {
+  int rip;
+  const uint8_t* pg = tile_page(S, tb, rip);
+  const int r = 16 * (wave & 1) + (lane >> 2);
+  const int tok = min(tb + r, S.n - 1);
+  const uint32_t voff = (uint32_t)((rip + tok - tb) * kRow + 16 * (4 * (wave >> 1) + (lane & 3)));
+#pragma unroll
+  for (int m = 0; m < 5; ++m) {
+    if (4 * m + wave >= kFp8Loads) break;
+    dma16_s(pg + 128 * m, voff, st + 1024 * (4 * m + wave));
+  }
+}
+
+// NVFP4 rows, raw.  Data: chunk c (32 codes) of row r at 1024 (c / 2) + 32 r + 16 (c % 2);
+// instruction j < 9 covers chunks 2j, 2j+1 of all rows (lane l: row l / 2, chunk
+// 2j + l % 2).  Scales: instruction 9 + s writes 256 bytes at 9216 + 256 s, lane l the
+// dword min(2s + l % 2, 8) of row l / 2 (the repeated dword 8 lands in a spare slot).
+__device__ __forceinline__ void load_nvfp4_raw(const Src& S, int tb, uint32_t st, int wave, int lane) {
+  const DecodeParams& p = *S.p;
+  int rip;
+  const uint8_t* pg = tile_page(S, tb, rip);
+  const int r = lane >> 1;
+  const int tok = min(tb + r, S.n - 1);
+  const int prow = rip + tok - tb;
+  const uint32_t dvoff = (uint32_t)(prow * kNvDataBytes + 16 * (lane & 1));
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int j = 4 * m + wave;
+    if (j >= kNvDataLoads + kNvScaleLoads) break;
+    if (j < kNvDataLoads) {
+      dma16_s(pg + 32 * j, dvoff, st + 1024 * j);
     } else {
-      const int64_t t = (int64_t)R.b * p.S + tok;
-      src = (c < kLatent / 8) ? (const void*)(p.kv + t * kLatent + 8 * c)
-                              : (const void*)(p.kpe + t * kRope + 8 * (c - kLatent / 8));
-    }
-    dma16(src, tile + 1024 * j);
-  }
-}
-
-// FP8 rows, raw, into staging [32][576]: 18 wave loads.
-__device__ __forceinline__ void load_fp8_raw(const Range& R, int tbase, uint8_t* st, int wave, int lane) {
-  const DecodeParams& p = *R.p;
-  const uint8_t* pg = tile_page(R, tbase);
-  for (int j = wave; j < kFp8Chunks / 64; j += kWaves) {
-    const int k = 64 * j + lane;
-    const int r = k / (kRow / 16), c = k % (kRow / 16);
-    const int tok = min(tbase + r, R.n - 1);
-    dma16(pg + (int64_t)(tok % p.page_size) * kRow + 16 * c, st + 1024 * j);
-  }
-}
-
-// NVFP4 rows, raw: data [32][288] (9 wave loads of 16 B), then scales [32][36]
-// (5 wave loads of 4 B, the last one half masked).
-__device__ __forceinline__ void load_nvfp4_raw(const Range& R, int tbase, uint8_t* st, int wave, int lane) {
-  const DecodeParams& p = *R.p;
-  const uint8_t* pg = tile_page(R, tbase);
-  for (int j = wave; j < kNvChunks / 64; j += kWaves) {
-    const int k = 64 * j + lane;
-    const int r = k / (kNvDataBytes / 16), c = k % (kNvDataBytes / 16);
-    const int tok = min(tbase + r, R.n - 1);
-    dma16(pg + (int64_t)(tok % p.page_size) * kNvDataBytes + 16 * c, st + 1024 * j);
-  }
-  const uint8_t* sc = pg + (int64_t)p.page_size * kNvDataBytes;
-  for (int j = wave; j < (kNvScaleWords + 63) / 64; j += kWaves) {
-    const int d = 64 * j + lane;
-    if (d < kNvScaleWords) {
-      const int r = d / (kNvScaleBytes / 4), c = d % (kNvScaleBytes / 4);
-      const int tok = min(tbase + r, R.n - 1);
-      dma4(sc + (int64_t)(tok % p.page_size) * kNvScaleBytes + 4 * c, st + kNvStageData + 256 * j);
+      const int sidx = j - kNvDataLoads;
+      const int q = min(2 * sidx + (lane & 1), kNvScaleBytes / 4 - 1);
+      dma4_s(pg, (uint32_t)(p.page_size * kNvDataBytes + prow * kNvScaleBytes + 4 * q),
+             st + kNvRawData + 256 * sidx);
     }
   }
 }
 
-// Four E4M3 codes (one dword) -> four bf16 (two dwords), exactly (hardware convert with
-// unit scale).
-__device__ __forceinline__ void fp8x4_to_bf16(unsigned w, unsigned& o0, unsigned& o1) {
-  o0 = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false));
-  o1 = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true));
-}
-
-// Raw staging -> bf16 tile.
-__device__ __forceinline__ void dequant_fp8(const uint8_t* st, uint8_t* tile, int tid) {
+// Raw FP8 staging -> bf16 tile.  Thread t writes chunk t % 8 of group m (m = 0..8) of
+// row t / 8: eight codes read as 8 bytes (raw chunk c / 2 of the row, half c % 2), four
+// converts, one 16-byte write.  Sixteen lanes cover two rows x one whole group.
+__device__ __forceinline__ void dequant_fp8(uint32_t st, uint32_t tile, int tid) {
+  const int r = tid >> 3, t7 = tid & 7;
+  const uint32_t rd = st + 64 * r + 8 * t7;                  // + 2048 m
+  const uint32_t wr = tile + 128 * r + ((t7 ^ swz(r)) << 4);  // + 4096 m
 #pragma unroll
-  for (int j = 0; j < (kFp8Chunks + kThreads - 1) / kThreads; ++j) {
-    const int k = tid + kThreads * j;
-    if (k < kFp8Chunks) {
-      const int r = k / (kRow / 16), c = k % (kRow / 16);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(st + 16 * k);
-      unsigned t[8];
-      fp8x4_to_bf16(v[0], t[0], t[1]);
-      fp8x4_to_bf16(v[1], t[2], t[3]);
-      fp8x4_to_bf16(v[2], t[4], t[5]);
-      fp8x4_to_bf16(v[3], t[6], t[7]);
-      *reinterpret_cast<u32x4*>(tile + tile_off(r, 2 * c)) = u32x4{t[0], t[1], t[2], t[3]};
-      *reinterpret_cast<u32x4*>(tile + tile_off(r, 2 * c + 1)) = u32x4{t[4], t[5], t[6], t[7]};
-    }
+  for (int m = 0; m < 9; ++m) {
+    typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+    const u32x2 v = *at<u32x2>(rd + 2048 * m);
+    unsigned t[4];
+    fp8x4_to_bf16(v[0], t[0], t[1]);
+    fp8x4_to_bf16(v[1], t[2], t[3]);
+    *at<u32x4>(wr + kGroupBytes * m) = u32x4{t[0], t[1], t[2], t[3]};
   }
 }
 
-__device__ __forceinline__ void dequant_nvfp4(const uint8_t* st, uint8_t* tile, int tid) {
+// Raw NVFP4 staging -> bf16 tile.  Thread t writes chunk t % 8 of group m of row t / 8:
+// eight codes (4 data bytes at 1024 m + 32 r + 4 (t % 8)) times their scale (group
+// (t % 8) / 2 + 4m of the row: byte (t % 8) / 2 of scale dword m).  The hardware
+// converts the codes exactly to f32 (unit scale); the products have at most 6
+// significant bits, so their high halves are the exact bf16 values.
+__device__ __forceinline__ void dequant_nvfp4(uint32_t st, uint32_t tile, int tid) {
+  const int r = tid >> 3, t7 = tid & 7;
+  const uint32_t rd = st + 32 * r + 4 * t7;                                   // + 1024 m
+  const uint32_t sd = st + kNvRawData + 8 * r + (t7 >> 1);                    // + 256 (m/2) + 4 (m%2)
+  const uint32_t wr = tile + 128 * r + ((t7 ^ swz(r)) << 4);                  // + 4096 m
 #pragma unroll
-  for (int j = 0; j < (kNvChunks + kThreads - 1) / kThreads; ++j) {
-    const int k = tid + kThreads * j;
-    if (k < kNvChunks) {
-      const int r = k / (kNvDataBytes / 16), c = k % (kNvDataBytes / 16);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(st + 16 * k);
-      const unsigned short sc =
-          *reinterpret_cast<const unsigned short*>(st + kNvStageData + r * kNvScaleBytes + 2 * c);
-      const f32x2 s = __builtin_amdgcn_cvt_pk_f32_fp8((int)sc, false);
-      *reinterpret_cast<u32x4*>(tile + tile_off(r, 4 * c + 0)) = fp4x8_to_bf16(v[0], s[0]);
-      *reinterpret_cast<u32x4*>(tile + tile_off(r, 4 * c + 1)) = fp4x8_to_bf16(v[1], s[0]);
-      *reinterpret_cast<u32x4*>(tile + tile_off(r, 4 * c + 2)) = fp4x8_to_bf16(v[2], s[1]);
-      *reinterpret_cast<u32x4*>(tile + tile_off(r, 4 * c + 3)) = fp4x8_to_bf16(v[3], s[1]);
-    }
+  for (int m = 0; m < 9; ++m) {
+    const unsigned w = *at<unsigned>(rd + 1024 * m);
+    const unsigned char sc = *at<unsigned char>(sd + 256 * (m >> 1) + 4 * (m & 1));
+    const float scale = __builtin_amdgcn_cvt_pk_f32_fp8((int)sc, false)[0];
+    const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    *at<u32x4>(wr + kGroupBytes * m) =
+        u32x4{pack_hi16(f0[0] * scale, f0[1] * scale), pack_hi16(f1[0] * scale, f1[1] * scale),
+              pack_hi16(f2[0] * scale, f2[1] * scale), pack_hi16(f3[0] * scale, f3[1] * scale)};
   }
 }
 
 // ------------------------------------------------------------------------------------
-// Work split inside a workgroup (8 wavefronts, 128 query rows).
-//   Score phase: wavefront w owns rows 16w .. 16w+15.  S^T[32 tok x 16 rows] from
-//     18 K-steps x 2 token blocks of MFMA 16x16x32 (Q^T of its rows in registers), then
-//     the masked online softmax; P (bf16) and each row's rescale factor go to LDS.
-//   Output phase: wavefront w owns dims 64w .. 64w+63 of all 128 rows:
-//     O^T[64 x 128] += V^T[64 x 32 tok] . P^T[32 tok x 128] with MFMA 32x32x16, V^T
-//     through the LDS transpose read of the token-major tile, P^T from LDS.
-// Two wavefronts share a SIMD, so one's MFMA work overlaps the other's softmax and
-// loads, and every wavefront stays within 256 registers.
+// Per-wavefront arithmetic.  MFMA 32x32x16 bf16 operand layouts (lane l, element e):
+// A[i = l % 32][k = 8 (l / 32) + e], B[k = 8 (l / 32) + e][j = l % 32]; result register v
+// of lane l holds D[i = 8 (v / 4) + 4 (l / 32) + v % 4][j = l % 32].
 // ------------------------------------------------------------------------------------
 
-constexpr int kQkSteps = kRow / 32;          // 18 K-steps of 32 dims (MFMA 16x16x32)
-constexpr int kPRowPitch = 80;               // bytes per row of the P buffer (64 + 16 pad)
-constexpr int kPBufBytes = kRowsPerGroup * kPRowPitch;
-
-struct Shared {  // LDS exchanged between the two phases of a tile
-  uint8_t* pbuf;  // P as bf16 [128 rows][32 tokens], row pitch kPRowPitch
-  float* alpha;   // [128] factor for each row's accumulators before this tile's product
-  float* inv_l;   // [128] at the end of a range: v_scale / sum of bf16(p) (0 if no token)
-};
-
-struct ScoreState {
-  bf16x8 q[kQkSteps];  // Q^T operand: row 16w + l%16, dims 32k + 8(l/16) .. +8
-  float m_used;        // reference max (log2 domain), equal in the 4 lanes of a row
-  float l_sum;         // this lane's share of sum p (unrounded): for the LSE
-  float l_rnd;         // this lane's share of sum bf16(p): normalises O
-  int vis;             // tokens the row may see
-  int a_off;           // KV operand offset of token l%16, chunk l/16 (K-step 0, token block 0);
-                       // K-step k: ^ 64 (k & 1), + 128 (k >> 1); token block 1: + 16 rows
-  int p_off;           // P write offset: row * pitch + 8 (l / 16), + 32 tb
-};
-
-struct OutState {
-  f32x16 o[2][4];      // o[db][rb]: row 32rb + l%32, dims 64w + 32db + 8(v/4) + 4(l/32) + v%4
-  int v_off[2];        // transpose-read offsets for e = 0, 1 (db = 0, ks = 0); db = 1: ^ 64,
-                       // ks = 1: + 16 rows
-  int p_off;           // P^T operand: row l%32, tokens 16ks + 8(l/32): + 32*pitch*rb + 32 ks
-};
-
-// Values of the four lanes l, l^16, l^32, l^48 (one row), combined with lane swaps.
-__device__ __forceinline__ float quad_max(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  return pair_max(x);
+// Scores of one tile: S^T[token][row], A = K (token l % 32, dims 16k + 8 (l / 32) ..),
+// B = Q^T (in registers).  K-step k reads chunk 2k + l/32 of the lane's token row: group
+// k / 4, swizzled position 2 (k % 4) + l/32, i.e. address ab[k % 4] + 4096 (k / 4) past
+// the tile.  The accumulation registers all hold the output, so this chain accumulates
+// in vector registers, which the compiler does not give MFMA results; it is written out
+// as one instruction block: operand reads run five K-steps ahead (about the LDS read
+// latency over the MFMA issue interval) through seven operand buffers, each MFMA waits
+// only for its own operand (LDS reads complete in order), and
+// back-to-back MFMAs accumulating into the same registers need no wait states.  The
+// closing s_nop run gives the wait states (more than the 18 required) before vector ALU
+// instructions may read the result.
+__device__ __forceinline__ f32x16 qk_tile(const bf16x8* q, uint32_t tile, const int* ab) {
+  const uint32_t b0 = tile + ab[0], b1 = tile + ab[1], b2 = tile + ab[2], b3 = tile + ab[3];
+  f32x16 s;
+  bf16x8 a0, a1, a2, a3, a4, a5, a6;
+  asm volatile(
+      "ds_read_b128 %[a0], %[b0] offset:0\n\t"
+      "ds_read_b128 %[a1], %[b1] offset:0\n\t"
+      "ds_read_b128 %[a2], %[b2] offset:0\n\t"
+      "ds_read_b128 %[a3], %[b3] offset:0\n\t"
+      "ds_read_b128 %[a4], %[b0] offset:4096\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q0], 0\n\t"
+      "ds_read_b128 %[a5], %[b1] offset:4096\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q1], %[s]\n\t"
+      "ds_read_b128 %[a6], %[b2] offset:4096\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q2], %[s]\n\t"
+      "ds_read_b128 %[a0], %[b3] offset:4096\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q3], %[s]\n\t"
+      "ds_read_b128 %[a1], %[b0] offset:8192\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q4], %[s]\n\t"
+      "ds_read_b128 %[a2], %[b1] offset:8192\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q5], %[s]\n\t"
+      "ds_read_b128 %[a3], %[b2] offset:8192\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q6], %[s]\n\t"
+      "ds_read_b128 %[a4], %[b3] offset:8192\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q7], %[s]\n\t"
+      "ds_read_b128 %[a5], %[b0] offset:12288\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q8], %[s]\n\t"
+      "ds_read_b128 %[a6], %[b1] offset:12288\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q9], %[s]\n\t"
+      "ds_read_b128 %[a0], %[b2] offset:12288\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q10], %[s]\n\t"
+      "ds_read_b128 %[a1], %[b3] offset:12288\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q11], %[s]\n\t"
+      "ds_read_b128 %[a2], %[b0] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q12], %[s]\n\t"
+      "ds_read_b128 %[a3], %[b1] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q13], %[s]\n\t"
+      "ds_read_b128 %[a4], %[b2] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q14], %[s]\n\t"
+      "ds_read_b128 %[a5], %[b3] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q15], %[s]\n\t"
+      "ds_read_b128 %[a6], %[b0] offset:20480\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q16], %[s]\n\t"
+      "ds_read_b128 %[a0], %[b1] offset:20480\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q17], %[s]\n\t"
+      "ds_read_b128 %[a1], %[b2] offset:20480\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q18], %[s]\n\t"
+      "ds_read_b128 %[a2], %[b3] offset:20480\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q19], %[s]\n\t"
+      "ds_read_b128 %[a3], %[b0] offset:24576\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q20], %[s]\n\t"
+      "ds_read_b128 %[a4], %[b1] offset:24576\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q21], %[s]\n\t"
+      "ds_read_b128 %[a5], %[b2] offset:24576\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q22], %[s]\n\t"
+      "ds_read_b128 %[a6], %[b3] offset:24576\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q23], %[s]\n\t"
+      "ds_read_b128 %[a0], %[b0] offset:28672\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q24], %[s]\n\t"
+      "ds_read_b128 %[a1], %[b1] offset:28672\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q25], %[s]\n\t"
+      "ds_read_b128 %[a2], %[b2] offset:28672\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q26], %[s]\n\t"
+      "ds_read_b128 %[a3], %[b3] offset:28672\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q27], %[s]\n\t"
+      "ds_read_b128 %[a4], %[b0] offset:32768\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q28], %[s]\n\t"
+      "ds_read_b128 %[a5], %[b1] offset:32768\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q29], %[s]\n\t"
+      "ds_read_b128 %[a6], %[b2] offset:32768\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q30], %[s]\n\t"
+      "ds_read_b128 %[a0], %[b3] offset:32768\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q31], %[s]\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q32], %[s]\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q33], %[s]\n\t"
+      "s_waitcnt lgkmcnt(1)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q34], %[s]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q35], %[s]\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : [s] "=&v"(s), [a0] "=&v"(a0), [a1] "=&v"(a1), [a2] "=&v"(a2), [a3] "=&v"(a3), [a4] "=&v"(a4), [a5] "=&v"(a5), [a6] "=&v"(a6)
+      : [b0] "v"(b0), [b1] "v"(b1), [b2] "v"(b2), [b3] "v"(b3),
+        [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]), [q5] "v"(q[5]),
+        [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8]), [q9] "v"(q[9]), [q10] "v"(q[10]), [q11] "v"(q[11]),
+        [q12] "v"(q[12]), [q13] "v"(q[13]), [q14] "v"(q[14]), [q15] "v"(q[15]), [q16] "v"(q[16]), [q17] "v"(q[17]),
+        [q18] "v"(q[18]), [q19] "v"(q[19]), [q20] "v"(q[20]), [q21] "v"(q[21]), [q22] "v"(q[22]), [q23] "v"(q[23]),
+        [q24] "v"(q[24]), [q25] "v"(q[25]), [q26] "v"(q[26]), [q27] "v"(q[27]), [q28] "v"(q[28]), [q29] "v"(q[29]),
+        [q30] "v"(q[30]), [q31] "v"(q[31]), [q32] "v"(q[32]), [q33] "v"(q[33]), [q34] "v"(q[34]), [q35] "v"(q[35])
+      : "memory");
+  return s;
 }
-__device__ __forceinline__ float quad_sum(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  return pair_sum(x);
-}
 
-// Score phase of one tile for this wavefront's 16 rows.  `full`: every token of the tile
-// is visible to every row of this wavefront, so no mask is needed.  c = score scale
-// (log2 units, >= 0).
-__device__ __forceinline__ void score_tile(ScoreState& S, const uint8_t* tile, const Shared& X, int tbase, float c,
-                                           int lane, bool active, bool full, int row_in_group) {
-  const int g = lane >> 4;
-  f32x4 s0 = f32x4{}, s1 = f32x4{};
-  if (active) {
+// Output product of one tile: O^T[dim][row] += V^T[dim][token] . P^T[token][row] for the
+// 16 blocks of 32 dims and the two K-steps of 16 tokens.  V^T comes from two transpose
+// reads per operand (vb[2e]: tokens 4e .. of the lane's half.  Dims 32 apart are 4
+// chunks apart, i.e. position bit 2 (byte-offset bit 6) flipped inside the same group;
+// 64 dims apart are one group further; tokens 16 apart have position bit 2 of the
+// swizzle flipped, so the second K-step flips byte-offset bit 6 as well; vb[2e + 1] is
+// vb[2e] with that bit flipped).  pp holds P^T.
+__device__ __forceinline__ void pv_tile(f32x16* o, uint32_t tile, const unsigned* pp, const int* vb) {
+  uint32_t base[4];  // [e][db & 1]
 #pragma unroll
-    for (int k = 0; k < kQkSteps; ++k) {
-      const int off = (S.a_off ^ (64 * (k & 1))) + 128 * (k >> 1);
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(tile + off);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(tile + off + 16 * kTileRowBytes);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, S.q[k], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, S.q[k], s1, 0, 0, 0);
-    }
-  }
-  // lane holds row l%16, raw scores of tokens tbase + 16 tb + 4(l/16) + v
-  float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-  const int lim = S.vis - tbase - 4 * g;  // token j of this lane (16 tb + v) is visible iff j < lim
-  if (!full) {
-#pragma unroll
-    for (int v = 0; v < 8; ++v) x[v] = (16 * (v >> 2) + (v & 3) < lim) ? x[v] : -INFINITY;
-  }
-  float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-  mt = quad_max(mt);
-  mt = (mt == -INFINITY) ? -INFINITY : mt * c;
-  const bool need = mt > S.m_used + kTau;
-  float alpha = 1.0f;
-  if (__any(need)) {
-    const float m_new = need ? mt : S.m_used;
-    alpha = need ? __builtin_amdgcn_exp2f(S.m_used - m_new) : 1.0f;
-    S.l_sum *= alpha;
-    S.l_rnd *= alpha;
-    S.m_used = m_new;
-  }
-  const float nm = (S.m_used == -INFINITY) ? 0.f : -S.m_used;
-  float e[8];
-#pragma unroll
-  for (int v = 0; v < 8; ++v) e[v] = __builtin_amdgcn_exp2f(fmaf(x[v], c, nm));
-  if (!full) {
-#pragma unroll
-    for (int v = 0; v < 8; ++v) e[v] = (16 * (v >> 2) + (v & 3) < lim) ? e[v] : 0.f;
-  }
-  S.l_sum += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-  unsigned pk[4];
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const bf16x2 pr = {(__bf16)e[2 * v], (__bf16)e[2 * v + 1]};
-    S.l_rnd = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, S.l_rnd, false);
-    pk[v] = __builtin_bit_cast(unsigned, pr);
-  }
-  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
-  *reinterpret_cast<u32x2*>(X.pbuf + S.p_off) = u32x2{pk[0], pk[1]};
-  *reinterpret_cast<u32x2*>(X.pbuf + S.p_off + 32) = u32x2{pk[2], pk[3]};
-  if (g == 0) X.alpha[row_in_group] = alpha;
-}
-
-// Output phase of one tile for this wavefront's 64 dims of the first nrb row blocks;
-// `side` is independent work (the next tile's dequantisation) issued between the MFMAs.
-template <class Side>
-__device__ __forceinline__ void out_tile(OutState& O, const uint8_t* tile, const Shared& X, int nrb, int lane,
-                                         Side side) {
-  const int lr = lane & 31;
-  float al[4];
-  bool resc = false;
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    al[rb] = (rb < nrb) ? X.alpha[32 * rb + lr] : 1.0f;
-    resc |= al[rb] != 1.0f;
-  }
-  if (__any(resc)) {
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      O.o[0][rb] *= al[rb];
-      O.o[1][rb] *= al[rb];
-    }
-  }
-  side();
+  for (int x = 0; x < 4; ++x) base[x] = tile + vb[x];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    bf16x8 va[2];
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pp[4 * ks], pp[4 * ks + 1], pp[4 * ks + 2], pp[4 * ks + 3]});
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      const int o0 = (O.v_off[0] ^ (64 * db)) + 16 * kTileRowBytes * ks;
-      const int o1 = (O.v_off[1] ^ (64 * db)) + 16 * kTileRowBytes * ks;
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(tile + o0));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(tile + o1));
-      va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      if (rb < nrb) {
-        const bf16x8 pb = *reinterpret_cast<const bf16x8*>(X.pbuf + O.p_off + 32 * kPRowPitch * rb + 32 * ks);
-        O.o[0][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0], pb, O.o[0][rb], 0, 0, 0);
-        O.o[1][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1], pb, O.o[1][rb], 0, 0, 0);
-      }
+    for (int db = 0; db < kDimBlocks; ++db) {
+      const uint32_t off = kGroupBytes * (db >> 1) + 16 * 128 * ks;
+      const int flip = (db & 1) ^ ks;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at<s16x4>(base[flip] + off));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at<s16x4>(base[2 + flip] + off));
+      const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[db], 0, 0, 0);
     }
   }
 }
 
+// o *= alpha in place in the accumulation registers, one value at a time through one
+// vector register.
+__device__ __forceinline__ void rescale(f32x16* o, float alpha) {
+#pragma unroll
+  for (int db = 0; db < kDimBlocks; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float e = o[db][v], t;
+      asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                   : "+a"(e), "=&v"(t)
+                   : "v"(alpha));
+      o[db][v] = e;
+    }
+}
+
+struct Softmax {
+  float m_used;  // reference max of the row (log2 domain), equal in lanes l and l ^ 32
+  float l_sum;   // this lane's share of sum p (unrounded): for the LSE
+  float l_rnd;   // this lane's share of sum bf16(p): normalises O
+};
+
+// Online softmax of one tile.  x: raw scores of this lane (row l % 32, tokens
+// 8 (v / 4) + 4 (l / 32) + v % 4), masked ones already -inf; c > 0 is the score scale in
+// log2 units.  Returns the factor for the row's accumulators before this tile's
+// product and P^T in the output product's B layout: pp[4 ks + ..] holds tokens
+// 16 ks + 8 (l / 32) .. + 8 of the row.
+__device__ __forceinline__ float softmax_tile(Softmax& S, float* x, float c, unsigned* pp) {
+  float mt = x[0];
+#pragma unroll
+  for (int v = 1; v < 16; ++v) mt = fmaxf(mt, x[v]);
+  mt = pair_max(mt) * c;  // -inf stays -inf (c > 0)
+  const bool need = mt > S.m_used + kTau;
+  const float m_new = need ? mt : S.m_used;
+  // (while no token has been seen the accumulators are zero and need no factor)
+  const float alpha = (need && S.m_used != -INFINITY) ? __builtin_amdgcn_exp2f(S.m_used - m_new) : 1.0f;
+  S.l_sum *= alpha;
+  S.l_rnd *= alpha;
+  S.m_used = m_new;
+  const float nm = (m_new == -INFINITY) ? 0.f : -m_new;
+  float e[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) e[v] = __builtin_amdgcn_exp2f(fmaf(x[v], c, nm));
+  float acc = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc += e[v];
+  S.l_sum += acc;
+  unsigned d[8];
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const bf16x2 pr = {(__bf16)e[2 * v], (__bf16)e[2 * v + 1]};
+    S.l_rnd = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, S.l_rnd, false);
+    d[v] = __builtin_bit_cast(unsigned, pr);
+  }
+  // d[4ks + 0..1]: tokens 16ks + 4 (l/32) + 0..3; d[4ks + 2..3]: tokens 16ks + 8 + 4 (l/32) + 0..3.
+  // The low half needs tokens 16ks + 0..7 (its own d0 d1, then the high half's d0 d1), the
+  // high half tokens 16ks + 8..15 (the low half's d2 d3, then its own d2 d3).
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const auto r02 = __builtin_amdgcn_permlane32_swap(d[4 * ks + 0], d[4 * ks + 2], false, false);
+    const auto r13 = __builtin_amdgcn_permlane32_swap(d[4 * ks + 1], d[4 * ks + 3], false, false);
+    pp[4 * ks + 0] = r02[0];
+    pp[4 * ks + 1] = r13[0];
+    pp[4 * ks + 2] = r02[1];
+    pp[4 * ks + 3] = r13[1];
+  }
+  return alpha;
+}
+
+// The output phase of a tile as 32 steps, one output MFMA each, fenced by scheduling
+// barriers so that the work between the MFMAs stays spread out: the transpose reads
+// run four MFMAs ahead (the LDS read latency is about four MFMA issue intervals), and
+// the online softmax of the current tile and the dequantisation of the next one are
+// cut into pieces of a few vector instructions per step.  The softmax pieces compute
+// exactly what softmax_tile does.
+struct SoftmaxPieces {
+  float mt, m_new, ex, nm, acc;
+  bool need;
+  unsigned d[8];
+};
+
+__device__ __forceinline__ void softmax_piece(int k, Softmax& S, float* x, float c, SoftmaxPieces& w, unsigned* pp,
+                                              float& alpha) {
+  if (k == 0) {
+    w.mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+  } else if (k == 1) {
+    w.mt = fmaxf(w.mt, fmaxf(fmaxf(fmaxf(x[8], x[9]), fmaxf(x[10], x[11])), fmaxf(fmaxf(x[12], x[13]), fmaxf(x[14], x[15]))));
+  } else if (k == 2) {
+    w.mt = pair_max(w.mt) * c;  // -inf stays -inf (c > 0)
+  } else if (k == 3) {
+    w.need = w.mt > S.m_used + kTau;
+    w.m_new = w.need ? w.mt : S.m_used;
+    w.ex = __builtin_amdgcn_exp2f(S.m_used - w.m_new);
+  } else if (k == 4) {
+    // (while no token has been seen the accumulators are zero and need no factor)
+    alpha = (w.need && S.m_used != -INFINITY) ? w.ex : 1.0f;
+    S.l_sum *= alpha;
+    S.l_rnd *= alpha;
+    S.m_used = w.m_new;
+    w.nm = (w.m_new == -INFINITY) ? 0.f : -w.m_new;
+    w.acc = 0.f;
+  } else if (k >= 5 && k < 21) {
+    const int v = k - 5;
+    x[v] = __builtin_amdgcn_exp2f(fmaf(x[v], c, w.nm));
+    w.acc += x[v];
+  } else if (k >= 21 && k < 25) {
+    const int j = k - 21;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    const bf16x2 p0 = {(__bf16)x[4 * j], (__bf16)x[4 * j + 1]};
+    const bf16x2 p1 = {(__bf16)x[4 * j + 2], (__bf16)x[4 * j + 3]};
+    S.l_rnd = __builtin_amdgcn_fdot2_f32_bf16(p0, ones, S.l_rnd, false);
+    S.l_rnd = __builtin_amdgcn_fdot2_f32_bf16(p1, ones, S.l_rnd, false);
+    w.d[2 * j] = __builtin_bit_cast(unsigned, p0);
+    w.d[2 * j + 1] = __builtin_bit_cast(unsigned, p1);
+  } else if (k == 25 || k == 26) {
+    if (k == 25) S.l_sum += w.acc;
+    const int ks = k - 25;
+    const auto r02 = __builtin_amdgcn_permlane32_swap(w.d[4 * ks + 0], w.d[4 * ks + 2], false, false);
+    const auto r13 = __builtin_amdgcn_permlane32_swap(w.d[4 * ks + 1], w.d[4 * ks + 3], false, false);
+    pp[4 * ks + 0] = r02[0];
+    pp[4 * ks + 1] = r13[0];
+    pp[4 * ks + 2] = r02[1];
+    pp[4 * ks + 3] = r13[1];
+  }
+}
+
+// Output product of tile i-1 (vtile, P^T in pp) with, between its MFMAs, the softmax of
+// tile i (raw scores x -> P^T in pn, factor alpha) and, for FP8, the dequantisation of
+// raw tile i+1 (staging st -> bf16 tile dtile; the same work as dequant_fp8).
+template <int FMT>
+__device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const unsigned* pp, const int* vb, float* x,
+                                             Softmax& S, float c, unsigned* pn, float& alpha, uint32_t st,
+                                             uint32_t dtile, int tid) {
+  constexpr int kAhead = 4;
+  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+  uint32_t base[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) base[v] = vtile + vb[v];
+  const bf16x8 pb0 = __builtin_bit_cast(bf16x8, u32x4{pp[0], pp[1], pp[2], pp[3]});
+  const bf16x8 pb1 = __builtin_bit_cast(bf16x8, u32x4{pp[4], pp[5], pp[6], pp[7]});
+  auto tr = [&](int k) {  // V^T operand of output MFMA k (dims block k % 16, K-step k / 16)
+    const int db = k & 15, ks = k >> 4, flip = (db & 1) ^ ks;
+    const uint32_t off = kGroupBytes * (db >> 1) + 16 * 128 * ks;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at<s16x4>(base[flip] + off));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at<s16x4>(base[2 + flip] + off));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  const int r = tid >> 3, t7 = tid & 7;
+  const uint32_t rd = st + 64 * r + 8 * t7;                   // FP8 dequantisation (see dequant_fp8)
+  const uint32_t wr = dtile + 128 * r + ((t7 ^ swz(r)) << 4);
+  u32x2 raw[9];
+  SoftmaxPieces w;
+  bf16x8 va[2 * kDimBlocks];
+#pragma unroll
+  for (int k = 0; k < kAhead; ++k) va[k] = tr(k);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < 2 * kDimBlocks; ++k) {
+    o[k & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k], (k < kDimBlocks) ? pb0 : pb1, o[k & 15], 0, 0, 0);
+    if (k + kAhead < 2 * kDimBlocks) va[k + kAhead] = tr(k + kAhead);
+    softmax_piece(k, S, x, c, w, pn, alpha);
+    if (FMT == kFmtFp8) {
+      if ((k & 1) == 0 && k / 2 < 9) raw[k / 2] = *at<u32x2>(rd + 2048 * (k / 2));
+      if ((k & 1) == 0 && k >= 2 && k / 2 - 1 < 9) {
+        const int m = k / 2 - 1;
+        unsigned t[4];
+        fp8x4_to_bf16(raw[m][0], t[0], t[1]);
+        fp8x4_to_bf16(raw[m][1], t[2], t[3]);
+        *at<u32x4>(wr + kGroupBytes * m) = u32x4{t[0], t[1], t[2], t[3]};
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // ------------------------------------------------------------------------------------
-// One token range of one request: Q load, pipelined tile loop, partial epilogue
+// One token range of one request: Q load, pipelined tile loop, partial epilogue.
 // ------------------------------------------------------------------------------------
 
 template <int FMT, bool PAGED>
-__device__ __forceinline__ void run_range(const DecodeParams& p, uint8_t* bf0, uint8_t* bf1, uint8_t* st0,
-                                          uint8_t* st1, const Shared& X, int b, int n, int rg, int lt0, int lt1,
-                                          int64_t slot) {
+__device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, int b, int n, int rg, int lt0,
+                                          int lt1, int64_t slot) {
+  using PP = Pipe<FMT>;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, lr = lane & 31, lh = lane >> 5;
-  const int row0 = rg * kRowsPerGroup;                   // first row of this workgroup
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform, and known so
+  const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
+  const int row0 = rg * kRowsPerGroup;                    // first row of this workgroup
   const int rows_here = min(kRowsPerGroup, p.rows - row0);
-  const int nrb = (rows_here + 31) / 32;                 // row blocks with rows
-  const int my_row = wave * kQkRows + (lane & 15);       // score-phase row (in the group)
-  const bool active = wave * kQkRows < rows_here;        // this wavefront has score rows
-  const int rc = min(row0 + my_row, p.rows - 1);
+  const int my_row = kWaveRows * wave + lr;               // this lane's row (in the group)
+  const int rc = min(row0 + my_row, p.rows - 1);          // rows past the end repeat the last row
+  const float c = fmaxf(p.score_scale, 1e-30f);           // sm_scale = 0 gives the plain mean
+  const int nt = lt1 - lt0;
 
-  ScoreState S;
-  // rows past the end of the problem repeat the last row: finite values, never stored
-  S.vis = max(n - p.q_len + rc / p.H + 1, 0);
-  // fewest tokens any row of this wavefront sees: tiles below it need no mask
-  int min_vis = S.vis;
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) min_vis = min(min_vis, __shfl_xor(min_vis, o));
-  S.m_used = -INFINITY;
-  S.l_sum = 0.f;
-  S.l_rnd = 0.f;
+  // Q^T operand: row rc, dims 16k + 8 (l / 32) .. + 8
+  bf16x8 q[kKSteps];
   {
     const uint16_t* qrow = p.q + ((int64_t)b * p.rows + rc) * kLatent;
     const uint16_t* prow = p.qpe + ((int64_t)b * p.rows + rc) * kRope;
 #pragma unroll
-    for (int k = 0; k < kQkSteps; ++k) {
-      const int d = 32 * k + 8 * g;
+    for (int k = 0; k < kKSteps; ++k) {
+      const int d = 16 * k + 8 * lh;
       const uint16_t* src = (d < kLatent) ? qrow + d : prow + (d - kLatent);
-      S.q[k] = *reinterpret_cast<const bf16x8*>(src);
+      q[k] = *reinterpret_cast<const bf16x8*>(src);
     }
   }
-  // chunk 4k + g of token t: (4k + g) ^ swz(t) = 8(k >> 1) + ((4(k & 1) + g) ^ swz(t)), and
-  // swz(t + 16) = swz(t); byte offsets of whole 128-byte groups never have bit 6 set
-  S.a_off = (lane & 15) * kTileRowBytes + ((g ^ swz(lane & 15)) << 4);
-  S.p_off = my_row * kPRowPitch + 8 * g;
+  // query i of a request sees tokens 0 .. n - q_len + i
+  const int vis = max(n - p.q_len + rc / p.H + 1, 0);
+  int min_vis = vis;  // fewest tokens any row of this wavefront sees: tiles below it need no mask
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) min_vis = min(min_vis, __shfl_xor(min_vis, o));
 
-  OutState O;
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) O.o[db][rb] = f32x16{};
-  // transpose reads: in a group of 16 lanes (g, j = lane % 16), lane j addresses token
-  // 16ks + 8(g >> 1) + 4e + j / 4 and dims d0 + 16(g & 1) + 4(j % 4) .. +4; lane i of
-  // the group then receives dim d0 + 16(g & 1) + i of those four tokens.
-  // (dims 32 apart are 4 chunks apart: chunk ^ 4 flips byte-offset bit 6; tokens 16
-  // apart share the swizzle)
+  int ab[4];  // score operand offsets, a_base ^ 32x (see qk_tile)
   {
-    const int j = lane & 15;
+    const int a_base = 128 * lr + ((lh ^ swz(lr)) << 4);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) ab[x] = a_base ^ (32 * x);
+  }
+  // transpose reads: in a group of 16 lanes (g = l / 16, j = l % 16), lane j addresses
+  // token 8 (g >> 1) + 4e + j / 4 and dims 16 (g & 1) + 4 (j % 4) .. + 4; lane i of the
+  // group then receives dim 16 (g & 1) + i of those four tokens
+  int vb[4];  // transpose-read offsets [e][db & 1] (see pv_tile)
+  {
+    const int g = lane >> 4, j = lane & 15;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int tok = 8 * (g >> 1) + 4 * e + (j >> 2);
-      const int dim = kPvDims * wave + 16 * (g & 1) + 4 * (j & 3);
-      O.v_off[e] = tile_off(tok, dim >> 3) + 2 * (dim & 7);
+      const int dim = 16 * (g & 1) + 4 * (j & 3);
+      const int v_off = tile_off(tok, dim >> 3) + 2 * (dim & 7);
+      vb[2 * e] = v_off;
+      vb[2 * e + 1] = v_off ^ 64;
     }
   }
-  O.p_off = lr * kPRowPitch + 16 * lh;
 
-  const float score_scale = p.score_scale;
-  const int nt = lt1 - lt0;
-  Range R{&p, b, n};
+  f32x16 o[kDimBlocks];
+#pragma unroll
+  for (int db = 0; db < kDimBlocks; ++db) o[db] = f32x16{};
+  Softmax S{-INFINITY, 0.f, 0.f};
+  unsigned pp[8];
+  float alpha_prev = 1.f;
 
-  // one tile: score phase, barrier, output phase (with `side` work issued inside it)
-  auto tile_step = [&](const uint8_t* tile, int i, auto side) {
-    const int tbase = (lt0 + i) * kTileTokens;
-    score_tile(S, tile, X, tbase, score_scale, lane, active, active && tbase + kTileTokens <= min_vis, my_row);
-    __syncthreads();
-    out_tile(O, tile, X, nrb, lane, side);
+  const Src src{&p, b, n};
+  const int nloads = (PP::kLoads - wave + kWaves - 1) / kWaves;  // load instructions per tile here
+  // buffer addresses go through readfirstlane, which keeps the loop optimiser from
+  // turning every per-lane LDS address into an induction variable of its own
+  auto tile_buf = [&](int i) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(smem + (uint32_t)((i % PP::kTiles) * kTileBytes)));
   };
-  auto nothing = [] {};
+  auto raw_buf = [&](int i) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(smem + (uint32_t)(PP::kTiles * kTileBytes + (i % (PP::kRaw ? PP::kRaw : 1)) * PP::kRawBytes)));
+  };
+  auto issue = [&](int i) {  // loads of tile i
+    const int tb = (lt0 + i) * kTileTokens;
+    if (FMT == kFmtBf16) load_bf16_tile<PAGED>(src, tb, tile_buf(i), wave, lane);
+    else if (FMT == kFmtFp8) load_fp8_raw(src, tb, raw_buf(i), wave, lane);
+    else load_nvfp4_raw(src, tb, raw_buf(i), wave, lane);
+  };
+  auto dequant = [&](int i) {  // raw tile i -> its bf16 buffer
+    if (FMT == kFmtFp8) dequant_fp8(raw_buf(i), tile_buf(i), tid);
+    else if (FMT == kFmtNvfp4) dequant_nvfp4(raw_buf(i), tile_buf(i), tid);
+  };
+
+  // one tile; FIRST: there is no previous tile to multiply
+  auto body = [&](int i, auto FIRST) {
+    constexpr bool first = decltype(FIRST)::value;
+    const bool more = i + PP::kAhead < nt;
+    if (more) issue(i + PP::kAhead);
+    if (!first && __any(alpha_prev != 1.f)) rescale(o, alpha_prev);
+    const f32x16 s = qk_tile(q, tile_buf(i), ab);
+    float x[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) x[v] = s[v];
+    const int tbase = (lt0 + i) * kTileTokens;
+    if (tbase + kTileTokens > min_vis) {
+      const int lim = vis - tbase - 4 * lh;  // value v (token 8 (v/4) + v%4 of the lane) visible iff < lim
+#pragma unroll
+      for (int v = 0; v < 16; ++v) x[v] = (8 * (v >> 2) + (v & 3) < lim) ? x[v] : -INFINITY;
+    }
+    unsigned pn[8];
+    float alpha;
+    // past the last tile the dequantisation only rewrites an unused buffer
+    if (first || FMT == kFmtNvfp4) {
+      if (FMT != kFmtBf16) dequant(i + 1);
+    }
+    if (first) {
+      alpha = softmax_tile(S, x, c, pn);
+    } else {
+      output_phase<FMT>(o, tile_buf(i - 1), pp, vb, x, S, c, pn, alpha, raw_buf(i + 1), tile_buf(i + 1), tid);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) pp[k] = pn[k];
+    alpha_prev = alpha;
+    // the loads the next tile depends on: bf16 tile i+1 (issued one tile ago), raw tile
+    // i+2 (issued now for FP8, one tile ago for NVFP4)
+    if (FMT == kFmtFp8) wait_vmcnt(0);
+    else wait_vmcnt(more ? nloads : 0);
+    __syncthreads();
+  };
 
   if (nt > 0) {
-    if (FMT == kFmtBf16) {
-      // raw bf16 rows go straight into the two tiles; loads run one tile ahead
-      load_bf16_tile<PAGED>(R, lt0 * kTileTokens, bf0, wave, lane);
-      for (int i = 0;;) {
-        wait_dma();
-        __syncthreads();
-        if (i + 1 < nt) load_bf16_tile<PAGED>(R, (lt0 + i + 1) * kTileTokens, bf1, wave, lane);
-        tile_step(bf0, i, nothing);
-        if (++i >= nt) break;
-        wait_dma();
-        __syncthreads();
-        if (i + 1 < nt) load_bf16_tile<PAGED>(R, (lt0 + i + 1) * kTileTokens, bf0, wave, lane);
-        tile_step(bf1, i, nothing);
-        if (++i >= nt) break;
-      }
-    } else {
-      // raw tiles are loaded two ahead of the MFMA work and dequantised one ahead, during
-      // the output phase of the current tile (a dequantisation past the last tile only
-      // rewrites an unused buffer)
-      auto load_raw = [&](int i, uint8_t* st) {
-        if (FMT == kFmtFp8) load_fp8_raw(R, (lt0 + i) * kTileTokens, st, wave, lane);
-        else load_nvfp4_raw(R, (lt0 + i) * kTileTokens, st, wave, lane);
-      };
-      auto dequant = [&](const uint8_t* st, uint8_t* tile) {
-        if (FMT == kFmtFp8) dequant_fp8(st, tile, tid);
-        else dequant_nvfp4(st, tile, tid);
-      };
-      load_raw(0, st0);
-      if (nt > 1) load_raw(1, st1);
-      wait_dma();
+    const int pro = min(nt, PP::kAhead);
+    for (int k = 0; k < pro; ++k) issue(k);
+    wait_vmcnt((pro - 1) * nloads);  // tile 0
+    __syncthreads();
+    if (FMT != kFmtBf16) {
+      dequant(0);
+      wait_vmcnt(max(pro - 2, 0) * nloads);  // raw tile 1
       __syncthreads();
-      dequant(st0, bf0);
-      for (int i = 0;;) {
-        wait_dma();
-        __syncthreads();
-        if (i + 2 < nt) load_raw(i + 2, st0);
-        tile_step(bf0, i, [&] { dequant(st1, bf1); });
-        if (++i >= nt) break;
-        wait_dma();
-        __syncthreads();
-        if (i + 2 < nt) load_raw(i + 2, st1);
-        tile_step(bf1, i, [&] { dequant(st0, bf0); });
-        if (++i >= nt) break;
-      }
     }
+    body(0, std::true_type{});
+    for (int i = 1; i < nt; ++i) body(i, std::false_type{});
+    if (__any(alpha_prev != 1.f)) rescale(o, alpha_prev);
+    pv_tile(o, tile_buf(nt - 1), pp, vb);
   }
 
-  // ---- epilogue: the score-phase owner of each row publishes 1/l and writes lse ----
-  {
-    const float l_tot = quad_sum(S.l_sum);
-    const float l_rnd = quad_sum(S.l_rnd);
-    const bool ok = l_tot > 0.f;
-    if (g == 0) {
-      X.inv_l[my_row] = ok ? p.v_scale / l_rnd : 0.f;
-      if (row0 + my_row < p.rows)
-        p.lse_part[slot * p.l_slot + (int64_t)(row0 + my_row) * p.l_row] =
-            ok ? (S.m_used + __log2f(l_tot)) * kLn2 : -INFINITY;
-    }
-  }
-  __syncthreads();
+  // ---- epilogue: normalised partial O and its lse ----
+  const float l_tot = pair_sum(S.l_sum);
+  const float l_rnd = pair_sum(S.l_rnd);
+  const bool ok = l_tot > 0.f;
+  if (my_row < rows_here) {
+    const int row = row0 + my_row;
+    if (lh == 0)
+      p.lse_part[slot * p.l_slot + (int64_t)row * p.l_row] = ok ? (S.m_used + __log2f(l_tot)) * kLn2 : -INFINITY;
+    rescale(o, ok ? p.v_scale / l_rnd : 0.f);  // normalise in place
+    float* orow = p.o_part + slot * p.o_slot + (int64_t)row * p.o_row + 4 * lh;
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int row = row0 + 32 * rb + lr;
-    if (rb < nrb && row < p.rows) {
-      const float inv = X.inv_l[32 * rb + lr];
-      float* orow = p.o_part + slot * p.o_slot + (int64_t)row * p.o_row + kPvDims * wave;
+    for (int db = 0; db < kDimBlocks; ++db)
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x16& o = O.o[db][rb];
-          const f32x4 val = {o[4 * q4] * inv, o[4 * q4 + 1] * inv, o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv};
-          *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * q4 + 4 * lh) = val;
-        }
-    }
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * q4) =
+            f32x4{o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]};
   }
   __syncthreads();  // the next range reuses the LDS buffers
 }
@@ -564,21 +826,15 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint8_t* bf0, u
 // ------------------------------------------------------------------------------------
 
 // Contiguous: grid (row_groups, num_splits, B); split j covers [j*L, min((j+1)*L, S)).
-__global__ __launch_bounds__(kThreads) void decode_contig_kernel(const DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t bf0[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t bf1[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t pbuf[kPBufBytes];
-  __shared__ float alpha[kRowsPerGroup];
-  __shared__ float inv_l[kRowsPerGroup];
-  const Shared X{pbuf, alpha, inv_l};
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_contig_kernel(const DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<kFmtBf16>()];
   const int rg = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int t0 = j * p.kv_len_per_split;
   const int t1 = min(t0 + p.kv_len_per_split, p.S);
-  const int lt0 = t0 / kTileTokens;
-  const int lt1 = (t1 + kTileTokens - 1) / kTileTokens;
   // slot b*H*NS + j with row = head addresses o_part [B, H, NS, 512]
-  run_range<kFmtBf16, false>(p, bf0, bf1, nullptr, nullptr, X, b, p.S, rg, lt0, lt1,
-                             (int64_t)b * p.rows * p.num_splits + j);
+  run_range<kFmtBf16, false>(p, lds_addr((lds_ptr)smem), b, p.S, rg, t0 / kTileTokens,
+                             (t1 + kTileTokens - 1) / kTileTokens, (int64_t)b * p.rows * p.num_splits + j);
 }
 
 // Paged: the batch's tiles (request b has ceil(n_b / 32)) are cut into num_splits equal
@@ -587,19 +843,14 @@ __global__ __launch_bounds__(kThreads) void decode_contig_kernel(const DecodePar
 // unique because the ranges are ordered.  seg_first[b] / seg_last[b] record the first
 // and last range touching request b; info[0] records the total tile count.
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void decode_paged_kernel(const DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t bf0[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t bf1[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t st0[StageBytes<FMT>::value];
-  __shared__ __attribute__((aligned(16))) uint8_t st1[StageBytes<FMT>::value];
-  __shared__ __attribute__((aligned(16))) uint8_t pbuf[kPBufBytes];
-  __shared__ float alpha[kRowsPerGroup];
-  __shared__ float inv_l[kRowsPerGroup];
-  __shared__ int pre[kMaxBatch + 1];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_paged_kernel(const DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<FMT>()];
   __shared__ int wsum[kWaves];
-  const Shared X{pbuf, alpha, inv_l};
+  __shared__ int found[2];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int max_len = p.max_blocks * p.page_size;
+  auto tiles_of = [&](int b) { return (min(max(p.seq_lens[b], 0), max_len) + kTileTokens - 1) / kTileTokens; };
 
   // workgroup id -> (range w, row group rg); the row groups of one range sit 8 ids
   // apart so that they land on the same XCD (ids are dealt round-robin over 8 XCDs)
@@ -609,58 +860,55 @@ __global__ __launch_bounds__(kThreads) void decode_paged_kernel(const DecodePara
   const int w = (id / per_blk) * 8 + (id % 8);
   if (w >= p.num_splits) return;
 
-  // exclusive prefix of tile counts over requests -> pre[0..B]
-  {
-    const int per = (p.B + kThreads - 1) / kThreads;
-    const int s0 = min(tid * per, p.B), s1 = min(s0 + per, p.B);
-    int acc = 0;
-    for (int b = s0; b < s1; ++b) {
-      const int n = min(max(p.seq_lens[b], 0), max_len);
-      acc += (n + kTileTokens - 1) / kTileTokens;
-    }
-    int x = acc;
+  // tile counts: thread t sums requests [s0, s1); an exclusive scan gives each chunk's
+  // first tile, the total T, and the request holding tile t0 of this range
+  const int per = (p.B + kThreads - 1) / kThreads;
+  const int s0 = min(tid * per, p.B), s1 = min(s0 + per, p.B);
+  int acc = 0;
+  for (int b = s0; b < s1; ++b) acc += tiles_of(b);
+  int x = acc;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o);
-      if (lane >= o) x += y;
-    }
-    if (lane == 63) wsum[wave] = x;
-    __syncthreads();
-    int run = x - acc;
-    for (int i = 0; i < wave; ++i) run += wsum[i];
-    if (tid == 0) pre[0] = 0;
-    for (int b = s0; b < s1; ++b) {
-      const int n = min(max(p.seq_lens[b], 0), max_len);
-      run += (n + kTileTokens - 1) / kTileTokens;
-      pre[b + 1] = run;
-    }
-    __syncthreads();
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
   }
-
-  const int T = pre[p.B];
-  if (w == 0 && rg == 0 && tid == 0) p.info[0] = T;
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int start = x - acc, T = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    start += (i < wave) ? wsum[i] : 0;
+    T += wsum[i];
+  }
   const int t0 = (int)(((int64_t)w * T) / p.num_splits);
   const int t1 = (int)(((int64_t)(w + 1) * T) / p.num_splits);
-  if (t0 >= t1) return;
-
-  // request holding tile t0: the last b with pre[b] <= t0
-  int lo = 0, hi = p.B;  // pre[lo] <= t0 < pre[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (pre[mid] <= t0) lo = mid; else hi = mid;
+  if (w == 0 && rg == 0 && tid == 0) p.info[0] = T;
+  if (t0 >= t1) return;  // uniform over the workgroup
+  if (start <= t0 && t0 < start + acc) {  // exactly one thread
+    int base = start, b = s0;
+    while (base + tiles_of(b) <= t0) base += tiles_of(b), ++b;
+    found[0] = b;
+    found[1] = base;
   }
-  int b = lo;
+  __syncthreads();
+  int b = found[0], base = found[1];
   int t = t0;
   while (t < t1) {
-    while (pre[b + 1] <= t) ++b;  // skip empty requests
-    const int seg_end = min(t1, pre[b + 1]);
+    const int nb = tiles_of(b);
+    if (base + nb <= t) {  // empty request
+      base += nb;
+      ++b;
+      continue;
+    }
+    const int seg_end = min(t1, base + nb);
     const int n = min(max(p.seq_lens[b], 0), max_len);
-    run_range<FMT, true>(p, bf0, bf1, st0, st1, X, b, n, rg, t - pre[b], seg_end - pre[b], (int64_t)w + b);
+    run_range<FMT, true>(p, lds_addr((lds_ptr)smem), b, n, rg, t - base, seg_end - base, (int64_t)w + b);
     if (tid == 0 && rg == 0) {
-      if (t == pre[b]) p.seg_first[b] = w;
-      if (seg_end == pre[b + 1]) p.seg_last[b] = w;
+      if (t == base) p.seg_first[b] = w;
+      if (seg_end == base + nb) p.seg_last[b] = w;
     }
     t = seg_end;
+    base += nb;
     ++b;
   }
 }
@@ -692,9 +940,9 @@ __device__ __forceinline__ void combine_row(int ns, Part part, uint16_t* orow, f
       if (pj.lse == -INFINITY) continue;
       const float wgt = expf(pj.lse - LSE);
       const f32x4* src = reinterpret_cast<const f32x4*>(pj.o + 8 * lane);
-      const f32x4 a = src[0], c = src[1];
+      const f32x4 a = src[0], b = src[1];
       acc[0] += wgt * a[0]; acc[1] += wgt * a[1]; acc[2] += wgt * a[2]; acc[3] += wgt * a[3];
-      acc[4] += wgt * c[0]; acc[5] += wgt * c[1]; acc[6] += wgt * c[2]; acc[7] += wgt * c[3];
+      acc[4] += wgt * b[0]; acc[5] += wgt * b[1]; acc[6] += wgt * b[2]; acc[7] += wgt * b[3];
     }
   }
   u32x4 packed;
@@ -759,11 +1007,9 @@ hipError_t launch_decode_paged(int fmt, const DecodeParams& p, hipStream_t strea
     case kFmtFp8:
       hipLaunchKernelGGL(decode_paged_kernel<kFmtFp8>, dim3(blocks), dim3(kThreads), 0, stream, p);
       break;
-    case kFmtNvfp4:
+    default:
       hipLaunchKernelGGL(decode_paged_kernel<kFmtNvfp4>, dim3(blocks), dim3(kThreads), 0, stream, p);
       break;
-    default:
-      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
