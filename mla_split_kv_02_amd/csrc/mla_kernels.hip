@@ -197,27 +197,34 @@ struct Src {
   int n;  // its tokens (>= 1 whenever a tile is loaded)
 };
 
-// Page holding tile tb (clamped into the cache) and the tile's first row in it.
-__device__ __forceinline__ const uint8_t* tile_page(const Src& S, int tb, int& row_in_page) {
+// Block-table entry of tile tb.  The table is only read by the kernel, so it is read
+// through the constant address space: a scalar load, whose wait the compiler places
+// at the first use.  The kernel reads the entry one tile before the loads that use it,
+// which keeps the load latency off the critical path (a vector load here would be
+// waited for together with the tile loads in flight).
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+__device__ __forceinline__ int table_entry(const Src& S, int tb) {
   const DecodeParams& p = *S.p;
-  int page = p.block_tables[(int64_t)S.b * p.max_blocks + (tb >> p.page_shift)];
-  page = min(max(page, 0), p.num_pages - 1);
-  row_in_page = tb & (p.page_size - 1);
-  return p.cache + (int64_t)page * p.page_stride;
+  return ((const_i32_ptr)p.block_tables)[(int64_t)S.b * p.max_blocks + (tb >> p.page_shift)];
+}
+// Start of the page an entry names, clamped into the cache.
+__device__ __forceinline__ const uint8_t* page_start(const Src& S, int entry) {
+  const DecodeParams& p = *S.p;
+  return p.cache + (int64_t)min(max(entry, 0), p.num_pages - 1) * p.page_stride;
 }
 
 // bf16 rows straight into the tile.  Instruction j = 4m + w fills group m, rows 8w ..
 // 8w+7: lane l takes row 8w + l/8 and the chunk whose swizzled position is l % 8.
 template <bool PAGED>
-__device__ __forceinline__ void load_bf16_tile(const Src& S, int tb, uint32_t tile, int wave, int lane) {
+__device__ __forceinline__ void load_bf16_tile(const Src& S, int tb, const uint8_t* pg, uint32_t tile, int wave,
+                                               int lane) {
   const DecodeParams& p = *S.p;
   const int r = 8 * wave + (lane >> 3);
   const int tok = min(tb + r, S.n - 1);
   const int cpos = ((lane & 7) ^ swz(r)) << 4;  // byte offset of the chunk inside its group of 8
   const uint32_t lds = tile + 1024 * wave;
   if (PAGED) {
-    int rip;
-    const uint8_t* pg = tile_page(S, tb, rip);
+    const int rip = tb & (p.page_size - 1);
     const uint32_t voff = (uint32_t)((rip + tok - tb) * (2 * kRow) + cpos);
 #pragma unroll
     for (int m = 0; m < 9; ++m) dma16_s(pg + 128 * m, voff, lds + kGroupBytes * m);
@@ -234,9 +241,8 @@ __device__ __forceinline__ void load_bf16_tile(const Src& S, int tb, uint32_t ti
 // FP8 rows, raw.  Staging layout: chunk c (16 codes) of row r at 2048 (c / 4) + 64 r +
 // 16 (c % 4).  Instruction j = 4m + w covers chunk group j / 2 of rows 16 (j % 2) ..:
 // lane l takes row 16 (w % 2) + l / 4 and chunk 4 (w / 2 + 2m) + l % 4.
-__device__ __forceinline__ void load_fp8_raw(const Src& S, int tb, uint32_t st, int wave, int lane) {
-  int rip;
-  const uint8_t* pg = tile_page(S, tb, rip);
+__device__ __forceinline__ void load_fp8_raw(const Src& S, int tb, const uint8_t* pg, uint32_t st, int wave, int lane) {
+  const int rip = tb & (S.p->page_size - 1);
   const int r = 16 * (wave & 1) + (lane >> 2);
   const int tok = min(tb + r, S.n - 1);
   const uint32_t voff = (uint32_t)((rip + tok - tb) * kRow + 16 * (4 * (wave >> 1) + (lane & 3)));
@@ -251,10 +257,10 @@ __device__ __forceinline__ void load_fp8_raw(const Src& S, int tb, uint32_t st, 
 // instruction j < 9 covers chunks 2j, 2j+1 of all rows (lane l: row l / 2, chunk
 // 2j + l % 2).  Scales: instruction 9 + s writes 256 bytes at 9216 + 256 s, lane l the
 // dword min(2s + l % 2, 8) of row l / 2 (the repeated dword 8 lands in a spare slot).
-__device__ __forceinline__ void load_nvfp4_raw(const Src& S, int tb, uint32_t st, int wave, int lane) {
+__device__ __forceinline__ void load_nvfp4_raw(const Src& S, int tb, const uint8_t* pg, uint32_t st, int wave,
+                                               int lane) {
   const DecodeParams& p = *S.p;
-  int rip;
-  const uint8_t* pg = tile_page(S, tb, rip);
+  const int rip = tb & (p.page_size - 1);
   const int r = lane >> 1;
   const int tok = min(tb + r, S.n - 1);
   const int prow = rip + tok - tb;
@@ -737,12 +743,17 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
     return (uint32_t)__builtin_amdgcn_readfirstlane(
         (int)(smem + (uint32_t)(PP::kTiles * kTileBytes + (i % (PP::kRaw ? PP::kRaw : 1)) * PP::kRawBytes)));
   };
-  auto issue = [&](int i) {  // loads of tile i
-    const int tb = (lt0 + i) * kTileTokens;
-    if (FMT == kFmtBf16) load_bf16_tile<PAGED>(src, tb, tile_buf(i), wave, lane);
-    else if (FMT == kFmtFp8) load_fp8_raw(src, tb, raw_buf(i), wave, lane);
-    else load_nvfp4_raw(src, tb, raw_buf(i), wave, lane);
+  auto entry = [&](int i) {  // block-table entry of tile i (paged caches)
+    return PAGED ? table_entry(src, (lt0 + min(i, nt - 1)) * kTileTokens) : 0;
   };
+  auto issue = [&](int i, int e) {  // loads of tile i, whose block-table entry is e
+    const int tb = (lt0 + i) * kTileTokens;
+    const uint8_t* pg = PAGED ? page_start(src, e) : nullptr;
+    if (FMT == kFmtBf16) load_bf16_tile<PAGED>(src, tb, pg, tile_buf(i), wave, lane);
+    else if (FMT == kFmtFp8) load_fp8_raw(src, tb, pg, raw_buf(i), wave, lane);
+    else load_nvfp4_raw(src, tb, pg, raw_buf(i), wave, lane);
+  };
+  int e_next = 0;  // block-table entry of tile i + kAhead, read one tile early
   auto dequant = [&](int i) {  // raw tile i -> its bf16 buffer
     if (FMT == kFmtFp8) dequant_fp8(raw_buf(i), tile_buf(i), tid);
     else if (FMT == kFmtNvfp4) dequant_nvfp4(raw_buf(i), tile_buf(i), tid);
@@ -752,7 +763,10 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
   auto body = [&](int i, auto FIRST) {
     constexpr bool first = decltype(FIRST)::value;
     const bool more = i + PP::kAhead < nt;
-    if (more) issue(i + PP::kAhead);
+    if (more) {
+      issue(i + PP::kAhead, e_next);
+      e_next = entry(i + PP::kAhead + 1);
+    }
     if (!first && __any(alpha_prev != 1.f)) rescale(o, alpha_prev);
     const f32x16 s = qk_tile(q, tile_buf(i), ab);
     float x[16];
@@ -787,7 +801,8 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
 
   if (nt > 0) {
     const int pro = min(nt, PP::kAhead);
-    for (int k = 0; k < pro; ++k) issue(k);
+    for (int k = 0; k < pro; ++k) issue(k, entry(k));
+    e_next = entry(PP::kAhead);
     wait_vmcnt((pro - 1) * nloads);  // tile 0
     __syncthreads();
     if (FMT != kFmtBf16) {
