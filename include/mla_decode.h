@@ -176,6 +176,30 @@ int mla_paged_decode(const uint16_t* q, const uint16_t* qpe, const void* kv_cach
                      int num_splits, void* workspace, size_t workspace_bytes, uint16_t* o,
                      float* lse, void* stream);
 
+/* KV-cache append: store T new tokens into the paged pool before decoding them
+ * (TokenSpeed page, forward_decode: each new token's latent and rope key are written into
+ * the paged pool at its cache location before attention; metrale page,
+ * mla_cache_assemble: a cache row is the latent followed by the rope key).
+ *   latent   [T, 512] bf16   rope [T, 64] bf16
+ *   slots    [T] int32, device: token j goes to row slots[j] % page_size of page
+ *            slots[j] / page_size; slots outside [0, num_pages * page_size) are skipped
+ *            (padding).  Slots must be distinct.
+ *   kv_cache the page pool (num_pages pages of page_stride_bytes), same layout as
+ *            mla_paged_decode reads; only the addressed rows (and, for NVFP4, their scale
+ *            bytes) are written.
+ * Encoding: bf16 stores the bit patterns; FP8 stores the E4M3 code of x / kv_scale
+ * (binary32 division), saturated at +-448, nearest value, ties to the even code; NVFP4
+ * stores per 16 values the E4M3 code of amax / 6 as the scale and the E2M1 codes of
+ * x / scale (saturated at +-6, nearest, ties to even; all zero when the scale decodes to
+ * 0).  Every code keeps the sign of its scaled value.  Inputs must be finite.
+ * Constraints checked on the host: T >= 0 (0 enqueues nothing); fmt valid; page_size 32
+ * or 64; num_pages >= 1 and num_pages * page_size < 2^31; page_stride_bytes a multiple of
+ * 16 and at least page_size * (1152, 576 or 324); kv_scale finite and > 0 for FP8;
+ * latent, rope and kv_cache 16-byte aligned, slots 4-byte aligned. */
+int mla_kv_append(const uint16_t* latent, const uint16_t* rope, const int32_t* slots, int T, void* kv_cache,
+                  int fmt, float kv_scale, int num_pages, int page_size, int64_t page_stride_bytes,
+                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     PagedCall,
     decode_splitkv,
     device_num_cus,
+    kv_append,
     lib,
     paged_decode,
     paged_workspace,

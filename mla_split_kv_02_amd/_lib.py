@@ -40,6 +40,7 @@ EXPORTED_SYMBOLS = (
     "mla_paged_decode_partials",
     "mla_paged_combine",
     "mla_paged_decode",
+    "mla_kv_append",
 )
 
 
@@ -84,6 +85,8 @@ def lib() -> ctypes.CDLL:
     L.mla_paged_decode.restype = c_int
     L.mla_paged_decode.argtypes = [vp, vp, vp, c_int, c_float, c_int, c_int, c_i64, vp, c_int, vp, c_int, c_int,
                                    c_int, c_float, c_int, vp, c_size, vp, vp, vp]
+    L.mla_kv_append.restype = c_int
+    L.mla_kv_append.argtypes = [vp, vp, vp, c_int, vp, c_int, c_float, c_int, c_int, c_i64, vp]
     _lib = L
     return L
 
@@ -273,3 +276,24 @@ def paged_decode(q, qpe, kv_cache, fmt, block_tables, seq_lens, page_size, page_
     (device).  Returns (o [B,q_len,H,512] bf16, lse [B,q_len,H] f32 or None)."""
     return PagedCall(q, qpe, kv_cache, fmt, block_tables, seq_lens, page_size, page_stride, kv_scale, sm_scale,
                      num_splits, workspace, o, lse, want_lse, num_cus).run()
+
+
+def kv_append(latent, rope, slots, kv_cache, fmt, page_size, page_stride=None, kv_scale=1.0):
+    """Store T new tokens into the page pool in place.  latent [T,512], rope [T,64] bf16;
+    slots [T] int32 (page * page_size + row; slots outside the pool are skipped);
+    kv_cache uint8 page pool of num_pages * page_stride bytes.  Returns kv_cache."""
+    T = latent.shape[0] if latent.dim() == 2 else -1
+    dev = kv_cache.device
+    _need(latent, "latent", torch.bfloat16, (T, LATENT), dev)
+    _need(rope, "rope", torch.bfloat16, (T, ROPE), dev)
+    _need(slots, "slots", torch.int32, (T,), dev)
+    _need(kv_cache, "kv_cache", torch.uint8, None, dev)
+    rb = {MLA_KV_BF16: 2 * ROW, MLA_KV_FP8_E4M3: ROW, MLA_KV_NVFP4: ROW // 2 + ROW // 16}.get(fmt)
+    if rb is None:
+        raise MlaError(MLA_ERR_UNSUPPORTED, "cache format")
+    if page_stride is None:
+        page_stride = page_size * rb
+    _check(lib().mla_kv_append(_ptr(latent), _ptr(rope), _ptr(slots), T, _ptr(kv_cache), int(fmt), float(kv_scale),
+                               int(kv_cache.numel() // page_stride), int(page_size), int(page_stride),
+                               _stream(dev)), "mla_kv_append")
+    return kv_cache

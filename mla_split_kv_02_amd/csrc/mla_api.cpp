@@ -301,3 +301,35 @@ int mla_paged_decode(const uint16_t* q, const uint16_t* qpe, const void* kv_cach
 }
 
 }  // extern "C"
+
+extern "C" {
+
+int mla_kv_append(const uint16_t* latent, const uint16_t* rope, const int32_t* slots, int T, void* kv_cache,
+                  int fmt, float kv_scale, int num_pages, int page_size, int64_t page_stride_bytes, void* stream) {
+  if (T < 0) return MLA_ERR_INVALID_ARG;
+  const int64_t rb = row_bytes(fmt);
+  if (rb < 0) return MLA_ERR_UNSUPPORTED;
+  if (page_size != 32 && page_size != 64) return MLA_ERR_UNSUPPORTED;
+  if (num_pages < 1 || (int64_t)num_pages * page_size >= ((int64_t)1 << 31)) return MLA_ERR_INVALID_ARG;
+  if (page_stride_bytes < page_size * rb || page_stride_bytes % 16 != 0) return MLA_ERR_INVALID_ARG;
+  if (fmt == MLA_KV_FP8_E4M3 && !(isfinite(kv_scale) && kv_scale > 0.f)) return MLA_ERR_INVALID_ARG;
+  if (T == 0) return MLA_OK;
+  if (!latent || !rope || !slots || !kv_cache) return MLA_ERR_INVALID_ARG;
+  if (!aligned(latent, 16) || !aligned(rope, 16) || !aligned(slots, 4) || !aligned(kv_cache, 16))
+    return MLA_ERR_INVALID_ARG;
+  AppendParams p{};
+  p.latent = latent;
+  p.rope = rope;
+  p.slots = slots;
+  p.cache = static_cast<uint8_t*>(kv_cache);
+  p.page_stride = page_stride_bytes;
+  p.T = T;
+  p.page_size = page_size;
+  p.num_pages = num_pages;
+  p.fmt = fmt;
+  p.kv_scale = (fmt == MLA_KV_FP8_E4M3) ? kv_scale : 1.f;
+  if (launch_kv_append(p, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -1,5 +1,5 @@
 // Internal interface between the C-ABI host code (mla_api.cpp) and the gfx950 kernels
-// (mla_kernels.hip).  Not installed; the public interface is include/mla_decode.h.
+// (mla_kernels.hip: decode and combine; mla_append.hip: cache append).  Not installed; the public interface is include/mla_decode.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -70,9 +70,21 @@ struct CombineParams {
   int max_len;     // paged: max_blocks * page_size (clamp for seq_lens)
 };
 
+// One cache append launch: token j's row [latent_j | rope_j] goes to flat slot slots[j].
+struct AppendParams {
+  const uint16_t* latent;  // [T, 512] bf16 bits
+  const uint16_t* rope;    // [T, 64] bf16 bits
+  const int32_t* slots;    // [T]: page * page_size + row; outside [0, num_pages * page_size): skipped
+  uint8_t* cache;
+  int64_t page_stride;
+  int T, page_size, num_pages, fmt;
+  float kv_scale;          // FP8: the stored code is that of x / kv_scale
+};
+
 hipError_t launch_decode_contig(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_paged(int fmt, const DecodeParams& p, hipStream_t stream);
 hipError_t launch_combine_generic(const CombineParams& p, hipStream_t stream);
 hipError_t launch_combine_paged(const CombineParams& p, hipStream_t stream);
+hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);
 
 }  // namespace mla

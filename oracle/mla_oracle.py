@@ -350,3 +350,113 @@ def paged_decode(q, qpe, cache, fmt: int, kv_scale: float, page_size: int, page_
         outs.append(o)
         lses.append(l)
     return np.stack(outs), np.stack(lses)
+
+
+# ----------------------------------------------------------------------------------
+# KV-cache append: the write that precedes the decode
+# ----------------------------------------------------------------------------------
+#
+# TokenSpeed page, ``forward_decode``: before attending, the new tokens' latent
+# (k[..., :kv_lora_rank]) and rope key (k[..., kv_lora_rank:]) are stored into the
+# paged pool at their cache locations (``set_mla_kv_buffer`` with ``out_cache_loc``);
+# the pool holds the cache dtype (FP8 E4M3 for that backend).  metrale page,
+# ``mla_cache_assemble``: one token's cache row is [kv_latent | k_rope].  The pages do
+# not spell out the quantisation; the readings used here are the same as the input
+# recipe's: FP8 code = nearest E4M3 value of x / kv_scale after saturation at +-448,
+# ties to the even code; NVFP4 scale = nearest E4M3 value of amax/6 (saturated at 448),
+# data = nearest E2M1 value of x / scale (saturated at +-6), ties to the even code, all
+# zeros when the scale is zero.  The sign of the scaled value is kept (so a negative
+# value that rounds to zero gives the negative-zero code).  Divisions are binary32.
+
+def _e4m3_positive_values() -> np.ndarray:
+    """Values of the non-negative finite E4M3 codes 0x00 .. 0x7E, in code order (which
+    is increasing value order)."""
+    return decode_e4m3fn(np.arange(0x7F))
+
+
+def _e2m1_positive_values() -> np.ndarray:
+    """Values of the non-negative E2M1 codes 0 .. 7, in code order."""
+    return decode_e2m1(np.arange(8))
+
+
+def _nearest_even_code(a: np.ndarray, values: np.ndarray) -> np.ndarray:
+    """For magnitudes a (float64, 0 <= a <= values[-1]), the index of the nearest entry
+    of the increasing table `values`; on a tie the even index (even mantissa) wins."""
+    a = np.asarray(a, dtype=np.float64)
+    hi = np.clip(np.searchsorted(values, a, side="left"), 0, len(values) - 1)
+    lo = np.clip(hi - 1, 0, len(values) - 1)
+    d_lo = a - values[lo]
+    d_hi = values[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    return np.where(pick_hi, hi, lo)
+
+
+def quantize_e4m3(y) -> np.ndarray:
+    """binary32 values -> E4M3 codes (uint8): saturate at +-448, nearest value, ties to
+    the even code, sign of y kept."""
+    y = np.asarray(y, dtype=np.float32)
+    a = np.minimum(np.abs(y).astype(np.float64), 448.0)
+    mag = _nearest_even_code(a, _e4m3_positive_values()).astype(np.uint8)
+    return np.where(np.signbit(y), mag | 0x80, mag).astype(np.uint8)
+
+
+def quantize_e2m1(y) -> np.ndarray:
+    """binary32 values -> E2M1 codes (low 4 bits of uint8): saturate at +-6, nearest
+    value, ties to the even code, sign of y kept."""
+    y = np.asarray(y, dtype=np.float32)
+    a = np.minimum(np.abs(y).astype(np.float64), 6.0)
+    mag = _nearest_even_code(a, _e2m1_positive_values()).astype(np.uint8)
+    return np.where(np.signbit(y), mag | 0x8, mag).astype(np.uint8)
+
+
+def encode_row(row_bits: np.ndarray, fmt: int, kv_scale: float = 1.0) -> np.ndarray:
+    """One cache row (576 bf16 bit patterns: latent then rope) -> its bytes in the page
+    format.  bf16: the bit patterns themselves.  FP8: 576 codes of x / kv_scale.
+    NVFP4: (288 data bytes, 36 scale codes) returned concatenated."""
+    row_bits = np.asarray(row_bits, dtype=np.uint16).reshape(ROW)
+    if fmt == FMT_BF16:
+        return row_bits.view(np.uint8).copy()
+    x = decode_bf16_bits(row_bits).astype(np.float32)  # exact
+    if fmt == FMT_FP8:
+        y = x / np.float32(kv_scale)
+        return quantize_e4m3(y)
+    if fmt == FMT_NVFP4:
+        g = x.reshape(ROW // NVFP4_GROUP, NVFP4_GROUP)
+        amax = np.abs(g).max(axis=1)
+        s_code = quantize_e4m3(amax / np.float32(6.0))
+        s_val = decode_e4m3fn(s_code).astype(np.float32)
+        codes = np.zeros_like(g, dtype=np.uint8)
+        for i in range(g.shape[0]):
+            if s_val[i] > 0:
+                codes[i] = quantize_e2m1(g[i] / s_val[i])
+        codes = codes.reshape(ROW)
+        data = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+        return np.concatenate([data, s_code])
+    raise ValueError(f"unknown cache format {fmt}")
+
+
+def kv_append(cache: np.ndarray, latent_bits, rope_bits, slots, fmt: int, kv_scale: float,
+              page_size: int, page_stride: int, num_pages: int) -> np.ndarray:
+    """Returns a copy of the page pool (uint8 bytes) with token j's row [latent_j |
+    rope_j] stored at flat slot slots[j] = page * page_size + row.  Slots outside
+    [0, num_pages * page_size) are skipped.  NVFP4: the 288 data bytes go to the page's
+    data section at row * 288, the 36 scales to its scale section (after page_size *
+    288 data bytes) at row * 36, as decode_page reads them."""
+    out = np.array(cache, dtype=np.uint8, copy=True)
+    latent_bits = np.asarray(latent_bits, dtype=np.uint16).reshape(-1, LATENT)
+    rope_bits = np.asarray(rope_bits, dtype=np.uint16).reshape(-1, ROPE)
+    for j, slot in enumerate(np.asarray(slots, dtype=np.int64)):
+        if slot < 0 or slot >= num_pages * page_size:
+            continue
+        page, r = divmod(int(slot), page_size)
+        base = page * page_stride
+        enc = encode_row(np.concatenate([latent_bits[j], rope_bits[j]]), fmt, kv_scale)
+        if fmt == FMT_NVFP4:
+            d, s = enc[: ROW // 2], enc[ROW // 2:]
+            out[base + r * (ROW // 2): base + (r + 1) * (ROW // 2)] = d
+            sc = base + page_size * (ROW // 2) + r * (ROW // NVFP4_GROUP)
+            out[sc: sc + ROW // NVFP4_GROUP] = s
+        else:
+            nb = page_row_bytes(fmt)
+            out[base + r * nb: base + (r + 1) * nb] = enc
+    return out

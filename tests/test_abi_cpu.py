@@ -184,3 +184,42 @@ def test_paged_partials_and_combine_reject():
         args = list(c_ok)
         args[i] = v
         assert L.mla_paged_combine(*args) == st, (i, v)
+
+
+def _append(**kw):
+    a = dict(lat=F, rope=F, slots=F, T=4, cache=F, fmt=1, kv_scale=0.5, num_pages=10, page_size=64,
+             stride=64 * 576)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return mla.lib().mla_kv_append(vp(a["lat"]), vp(a["rope"]), vp(a["slots"]), a["T"], vp(a["cache"]), a["fmt"],
+                                   a["kv_scale"], a["num_pages"], a["page_size"], a["stride"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lat=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(rope=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(slots=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(cache=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(lat=F + 8), mla.MLA_ERR_INVALID_ARG),
+    (dict(slots=F + 2), mla.MLA_ERR_INVALID_ARG),
+    (dict(cache=F + 8), mla.MLA_ERR_INVALID_ARG),
+    (dict(T=-1), mla.MLA_ERR_INVALID_ARG),
+    (dict(fmt=3), mla.MLA_ERR_UNSUPPORTED),
+    (dict(page_size=16), mla.MLA_ERR_UNSUPPORTED),
+    (dict(num_pages=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(num_pages=1 << 25), mla.MLA_ERR_INVALID_ARG),
+    (dict(stride=64 * 576 - 16), mla.MLA_ERR_INVALID_ARG),
+    (dict(stride=64 * 576 + 4), mla.MLA_ERR_INVALID_ARG),
+    (dict(fmt=0, stride=64 * 576), mla.MLA_ERR_INVALID_ARG),
+    (dict(kv_scale=0.0), mla.MLA_ERR_INVALID_ARG),
+    (dict(kv_scale=float("inf")), mla.MLA_ERR_INVALID_ARG),
+])
+def test_kv_append_rejects(kw, status):
+    assert _append(**kw) == status
+
+
+def test_kv_append_no_tokens_enqueues_nothing():
+    # T = 0 is accepted before any pointer is looked at; nothing is launched
+    assert _append(T=0, lat=0, rope=0, slots=0, cache=0) == mla.MLA_OK
+    # kv_scale only matters for FP8
+    assert _append(T=0, fmt=2, stride=64 * 324, kv_scale=0.0) == mla.MLA_OK

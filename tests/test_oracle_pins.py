@@ -399,3 +399,158 @@ def _mutant(kind):
 def test_pins_catch_planted_mistakes(kind):
     assert _attend_vs_sdpa(_mutant("none")) < 1e-10
     assert _attend_vs_sdpa(_mutant(kind)) > 1e-3
+
+
+# ----------------------------------------------------------------------------------
+# cache append: the quantisers and the row placement
+# ----------------------------------------------------------------------------------
+
+def _e4m3_midpoints():
+    """Every midpoint between adjacent non-negative finite E4M3 values (exact in fp32)."""
+    v = oracle.decode_e4m3fn(np.arange(0x7F))
+    return ((v[:-1] + v[1:]) / 2).astype(np.float32), np.arange(0x7E)
+
+
+def test_e4m3_quantiser_round_trips_every_code():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = oracle.decode_e4m3fn(codes).astype(np.float32)
+    assert np.array_equal(oracle.quantize_e4m3(vals), codes)
+
+
+def test_e4m3_quantiser_matches_torch_cast():
+    # torch's float8_e4m3fn cast rounds to nearest, ties to even (no saturation, so the
+    # inputs stay within +-448); random values, every midpoint, and its neighbours
+    rng = np.random.default_rng(11)
+    mids, _ = _e4m3_midpoints()
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * np.float32(50),
+                        rng.uniform(-2 ** -5, 2 ** -5, 5000).astype(np.float32),
+                        mids, -mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(500))])
+    x = np.clip(x, -448, 448).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.quantize_e4m3(x), ref)
+
+
+def test_e4m3_quantiser_hand_cases():
+    # ties go to the even code; saturation at 448; the sign of zero is kept
+    cases = [(1.0625, 0x38), (1.1875, 0x3A), (2 ** -10, 0x00), (3 * 2 ** -10, 0x02), (1000.0, 0x7E),
+             (-1000.0, 0xFE), (448.0, 0x7E), (464.0, 0x7E), (240.0, 0x77), (-0.0, 0x80), (-1e-6, 0x80),
+             (0.0, 0x00), (2 ** -6, 0x08)]
+    for x, c in cases:
+        assert int(oracle.quantize_e4m3(np.float32(x))) == c, (x, c)
+
+
+def test_e2m1_quantiser_cases():
+    vals = oracle.decode_e2m1(np.arange(16)).astype(np.float32)
+    assert np.array_equal(oracle.quantize_e2m1(vals), np.arange(16, dtype=np.uint8))
+    # midpoints tie to the even code (0, 1, 2, 4 have even codes); saturation at 6
+    cases = [(0.25, 0), (0.75, 2), (1.25, 2), (1.75, 4), (2.5, 4), (3.5, 6), (5.0, 6), (5.0001, 7), (7.0, 7),
+             (1e9, 7), (-0.25, 8), (-5.0, 14), (-0.1, 8), (0.2500001, 1), (0.7499999, 1), (-0.0, 8), (0.0, 0)]
+    for x, c in cases:
+        assert int(oracle.quantize_e2m1(np.float32(x))) == c, (x, c)
+
+
+def test_encode_row_matches_input_recipe_encoders():
+    # the input recipe encodes with torch's cast and its own threshold table: an
+    # implementation of the same readings that shares no code with the oracle
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((64, oracle.ROW)).astype(np.float32)
+    bits = gen.to_bf16_bits(x)
+    xb = gen.bf16_bits_to_f32(bits)
+    s = np.float32(0.0173)
+    fp8_ref = gen.to_e4m3_codes(xb / s)
+    d_ref, sc_ref = gen.encode_nvfp4_rows(xb)
+    for r in range(64):
+        assert np.array_equal(oracle.encode_row(bits[r], oracle.FMT_FP8, float(s)), fp8_ref[r])
+        enc = oracle.encode_row(bits[r], oracle.FMT_NVFP4)
+        assert np.array_equal(enc[:288], d_ref[r])
+        assert np.array_equal(enc[288:], sc_ref[r])
+        assert np.array_equal(oracle.encode_row(bits[r], oracle.FMT_BF16).view(np.uint16), bits[r])
+
+
+def test_encode_row_error_bounds():
+    # FP8: |x - kv_scale * e4m3(code)| <= half a step of the E4M3 grid at |x / kv_scale|;
+    # NVFP4: per group the scale is the E4M3 value nearest amax / 6, and each value is
+    # within half an E2M1 step (times the scale) of its code's value
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal((16, oracle.ROW)) * 3).astype(np.float32)
+    bits = gen.to_bf16_bits(x)
+    xb = gen.bf16_bits_to_f32(bits).astype(np.float64)
+    s = 0.05
+    for r in range(16):
+        y = xb[r] / s
+        got = oracle.decode_e4m3fn(oracle.encode_row(bits[r], oracle.FMT_FP8, s))
+        ulp = np.where(np.abs(y) < 2 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(y), 1e-30))) - 3))
+        assert np.all(np.abs(got - y) <= ulp / 2 + 1e-12)
+        enc = oracle.encode_row(bits[r], oracle.FMT_NVFP4)
+        page = np.zeros(324, dtype=np.uint8)
+        page[:324] = enc
+        dec = oracle.decode_page(page, oracle.FMT_NVFP4, 1)[0]
+        g = xb[r].reshape(36, 16)
+        sc = oracle.decode_e4m3fn(enc[288:])
+        for k in range(36):
+            amax = np.abs(g[k]).max()
+            cand = oracle.decode_e4m3fn(np.arange(0x7F))
+            assert abs(sc[k] - amax / 6) <= np.min(np.abs(cand - amax / 6)) + 1e-12
+            if sc[k] > 0:
+                a = np.abs(g[k] / sc[k])
+                step = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
+                err = np.abs(dec.reshape(36, 16)[k] / sc[k] - g[k] / sc[k])
+                assert np.all(err <= np.maximum(step / 2, a - 6) + 1e-9)
+
+
+def test_kv_append_places_rows_and_skips_outside_slots():
+    rng = np.random.default_rng(14)
+    page_size, num_pages = 32, 5
+    for fmt in (oracle.FMT_BF16, oracle.FMT_FP8, oracle.FMT_NVFP4):
+        stride = page_size * oracle.page_row_bytes(fmt) + 48
+        cache = rng.integers(0, 256, num_pages * stride, dtype=np.uint8)
+        lat = gen.to_bf16_bits(rng.standard_normal((4, 512)).astype(np.float32))
+        rope = gen.to_bf16_bits(rng.standard_normal((4, 64)).astype(np.float32))
+        slots = np.array([-1, 3 * page_size + 7, num_pages * page_size, 0])
+        out = oracle.kv_append(cache, lat, rope, slots, fmt, 0.25, page_size, stride, num_pages)
+        changed = np.nonzero(out != cache)[0]
+        # only the rows of slots 3*32+7 and 0 (and their NVFP4 scales) may change
+        rb = oracle.page_row_bytes(fmt) if fmt != oracle.FMT_NVFP4 else 288
+        allowed = set(range(3 * stride + 7 * rb, 3 * stride + 8 * rb)) | set(range(0, rb))
+        if fmt == oracle.FMT_NVFP4:
+            allowed |= set(range(3 * stride + 32 * 288 + 7 * 36, 3 * stride + 32 * 288 + 8 * 36))
+            allowed |= set(range(32 * 288, 32 * 288 + 36))
+        assert set(changed.tolist()) <= allowed
+        # reading back through decode_page gives the encoded row
+        for j, slot in ((1, 3 * page_size + 7), (3, 0)):
+            p, r = divmod(slot, page_size)
+            dec = oracle.decode_page(out[p * stride:(p + 1) * stride], fmt, page_size, 0.25)[r]
+            want = oracle.decode_bf16_bits(np.concatenate([lat[j], rope[j]]))
+            if fmt == oracle.FMT_BF16:
+                assert np.array_equal(dec, want)
+            elif fmt == oracle.FMT_FP8:  # half an E4M3 step: 2^-4 relative, 2^-10 * scale near zero
+                assert np.all(np.abs(dec - want) <= np.abs(want) * 2.0 ** -4 + 0.25 * 2.0 ** -10)
+            else:  # half an E2M1 step of the group's scale (<= amax / 6 * 1.07)
+                assert np.max(np.abs(dec - want)) < 1.5
+
+
+@pytest.mark.parametrize("kind", ["ties_away", "truncate", "no_saturation"])
+def test_quantiser_pins_catch_planted_mistakes(kind, monkeypatch):
+    """Plant a plausible rounding mistake in a copy of the nearest-even search and check
+    that the torch-cast and hand-case pins fail."""
+    good = oracle.mla_oracle._nearest_even_code
+
+    def bad(a, values):
+        a = np.asarray(a, dtype=np.float64)
+        if kind == "no_saturation":
+            return good(a, values) if np.all(a <= values[-1] * 0.999) else np.full(np.shape(a), len(values))
+        hi = np.clip(np.searchsorted(values, a, side="left"), 0, len(values) - 1)
+        lo = np.clip(hi - 1, 0, len(values) - 1)
+        if kind == "truncate":
+            return np.where(values[hi] == a, hi, lo)
+        d_lo, d_hi = a - values[lo], values[hi] - a
+        return np.where(d_hi <= d_lo, hi, lo)  # ties away from zero
+
+    monkeypatch.setattr(oracle.mla_oracle, "_nearest_even_code", bad)
+    failed = 0
+    for test in (test_e4m3_quantiser_matches_torch_cast, test_e4m3_quantiser_hand_cases, test_e2m1_quantiser_cases):
+        try:
+            test()
+        except (AssertionError, IndexError):
+            failed += 1
+    assert failed >= 1
