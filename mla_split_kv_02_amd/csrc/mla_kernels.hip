@@ -18,9 +18,10 @@
 // one workgroup barrier per tile hands them over.
 //
 // Per tile i: the global->LDS loads of a later tile are issued first; then the scores of
-// tile i, with the dequantisation (FP8 / NVFP4) of tile i+1 in the same instruction
-// stream; then the softmax of tile i, with the output product of tile i-1 in the same
-// stream, so the matrix cores have work while the softmax runs; then one barrier.
+// tile i; then the softmax of tile i, with the output product of tile i-1 and (FP8) the
+// dequantisation of tile i+1 in the same instruction stream, so the matrix cores have
+// work while the vector work runs (NVFP4 dequantises tile i+1 just before); then one
+// barrier.
 //
 // Combine kernels.  One wavefront per output row merges the partials with the split-K
 // log-sum-exp reduce (TileGym page, forward: splitk_reduce).
