@@ -74,7 +74,17 @@ typedef enum {
  *                    the row; value = e2m1(code) * e4m3(scale) (metrale page,
  *                    mla_paged_decode_nvfp4: packed E2M1 data followed by one E4M3 scale
  *                    per 16 values). */
-typedef enum { MLA_KV_BF16 = 0, MLA_KV_FP8_E4M3 = 1, MLA_KV_NVFP4 = 2 } mla_kv_format;
+typedef enum {
+  MLA_KV_BF16 = 0,
+  MLA_KV_FP8_E4M3 = 1,
+  MLA_KV_NVFP4 = 2,
+  /* Same page bytes and kv_scale as MLA_KV_FP8_E4M3, with the query rounded to E4M3
+   * (nearest, ties to even, saturating at 448) and the score product on FP8 matrix cores,
+   * as the TokenSpeed page's FP8 decode does (forward_decode: the query is cast to the
+   * cache's FP8 type and k_scale is folded into the softmax scale).  The output product
+   * still runs in bf16 on the exactly dequantised latent. */
+  MLA_KV_FP8_E4M3_QFP8 = 3
+} mla_kv_format;
 
 /* Static text for a status code (never NULL). */
 const char* mla_status_string(int status);
@@ -187,7 +197,8 @@ int mla_paged_decode(const uint16_t* q, const uint16_t* qpe, const void* kv_cach
  *   kv_cache the page pool (num_pages pages of page_stride_bytes), same layout as
  *            mla_paged_decode reads; only the addressed rows (and, for NVFP4, their scale
  *            bytes) are written.
- * Encoding: bf16 stores the bit patterns; FP8 stores the E4M3 code of x / kv_scale
+ * Encoding: bf16 stores the bit patterns; FP8 (and MLA_KV_FP8_E4M3_QFP8, whose pages are
+ * the same) stores the E4M3 code of x / kv_scale
  * (binary32 division), saturated at +-448, nearest value, ties to the even code; NVFP4
  * stores per 16 values the E4M3 code of amax / 6 as the scale and the E2M1 codes of
  * x / scale (saturated at +-6, nearest, ties to even; all zero when the scale decodes to

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     MLA_ERR_WORKSPACE_TOO_SMALL,
     MLA_KV_BF16,
     MLA_KV_FP8_E4M3,
+    MLA_KV_FP8_E4M3_QFP8,
     MLA_KV_NVFP4,
     MLA_OK,
     EXPORTED_SYMBOLS,

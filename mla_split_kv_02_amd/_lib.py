@@ -25,6 +25,7 @@ MLA_ERR_HIP = -4
 MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3 = 1
 MLA_KV_NVFP4 = 2
+MLA_KV_FP8_E4M3_QFP8 = 3  # FP8 pages, query rounded to E4M3, scores on FP8 matrix cores
 
 LATENT, ROPE, ROW = 512, 64, 576
 
@@ -226,7 +227,8 @@ class PagedCall:
         _need(seq_lens, "seq_lens", torch.int32, (B,), dev)
         if block_tables.dim() != 2 or block_tables.shape[0] != B:
             raise ValueError("block_tables must be [B, max_blocks]")
-        rb = {MLA_KV_BF16: 2 * ROW, MLA_KV_FP8_E4M3: ROW, MLA_KV_NVFP4: ROW // 2 + ROW // 16}.get(fmt)
+        rb = {MLA_KV_BF16: 2 * ROW, MLA_KV_FP8_E4M3: ROW, MLA_KV_NVFP4: ROW // 2 + ROW // 16,
+              MLA_KV_FP8_E4M3_QFP8: ROW}.get(fmt)
         if rb is None:
             raise MlaError(MLA_ERR_UNSUPPORTED, "cache format")
         if page_stride is None:
@@ -288,7 +290,8 @@ def kv_append(latent, rope, slots, kv_cache, fmt, page_size, page_stride=None, k
     _need(rope, "rope", torch.bfloat16, (T, ROPE), dev)
     _need(slots, "slots", torch.int32, (T,), dev)
     _need(kv_cache, "kv_cache", torch.uint8, None, dev)
-    rb = {MLA_KV_BF16: 2 * ROW, MLA_KV_FP8_E4M3: ROW, MLA_KV_NVFP4: ROW // 2 + ROW // 16}.get(fmt)
+    rb = {MLA_KV_BF16: 2 * ROW, MLA_KV_FP8_E4M3: ROW, MLA_KV_NVFP4: ROW // 2 + ROW // 16,
+              MLA_KV_FP8_E4M3_QFP8: ROW}.get(fmt)
     if rb is None:
         raise MlaError(MLA_ERR_UNSUPPORTED, "cache format")
     if page_stride is None:

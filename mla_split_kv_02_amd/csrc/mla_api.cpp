@@ -27,7 +27,8 @@ int64_t next_pow2(int64_t n) {
 int64_t row_bytes(int fmt) {
   switch (fmt) {
     case MLA_KV_BF16: return 2 * kRow;
-    case MLA_KV_FP8_E4M3: return kRow;
+    case MLA_KV_FP8_E4M3:
+    case MLA_KV_FP8_E4M3_QFP8: return kRow;
     case MLA_KV_NVFP4: return kRow / 2 + kRow / 16;
     default: return -1;
   }
@@ -198,13 +199,14 @@ int paged_partials(const uint16_t* q, const uint16_t* qpe, const void* kv_cache,
   if (page_stride_bytes < page_size * rb || page_stride_bytes % 16 != 0) return MLA_ERR_INVALID_ARG;
   if ((int64_t)B * max_blocks_per_seq * page_size >= ((int64_t)1 << 31)) return MLA_ERR_INVALID_ARG;
   if (!isfinite(sm_scale) || sm_scale < 0.f) return MLA_ERR_INVALID_ARG;
-  if (fmt == MLA_KV_FP8_E4M3 && !(isfinite(kv_scale) && kv_scale > 0.f)) return MLA_ERR_INVALID_ARG;
+  const bool fp8 = (fmt == MLA_KV_FP8_E4M3 || fmt == MLA_KV_FP8_E4M3_QFP8);
+  if (fp8 && !(isfinite(kv_scale) && kv_scale > 0.f)) return MLA_ERR_INVALID_ARG;
   PagedLayout L;
   const int st = check_paged_shape(B, q_len, H, num_splits, workspace, workspace_bytes, &L);
   if (st != MLA_OK) return st;
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const float vs = (fmt == MLA_KV_FP8_E4M3) ? kv_scale : 1.f;
+  const float vs = fp8 ? kv_scale : 1.f;
   DecodeParams p{};
   p.q = q;
   p.qpe = qpe;
@@ -312,7 +314,8 @@ int mla_kv_append(const uint16_t* latent, const uint16_t* rope, const int32_t* s
   if (page_size != 32 && page_size != 64) return MLA_ERR_UNSUPPORTED;
   if (num_pages < 1 || (int64_t)num_pages * page_size >= ((int64_t)1 << 31)) return MLA_ERR_INVALID_ARG;
   if (page_stride_bytes < page_size * rb || page_stride_bytes % 16 != 0) return MLA_ERR_INVALID_ARG;
-  if (fmt == MLA_KV_FP8_E4M3 && !(isfinite(kv_scale) && kv_scale > 0.f)) return MLA_ERR_INVALID_ARG;
+  const bool fp8 = (fmt == MLA_KV_FP8_E4M3 || fmt == MLA_KV_FP8_E4M3_QFP8);  // same page bytes
+  if (fp8 && !(isfinite(kv_scale) && kv_scale > 0.f)) return MLA_ERR_INVALID_ARG;
   if (T == 0) return MLA_OK;
   if (!latent || !rope || !slots || !kv_cache) return MLA_ERR_INVALID_ARG;
   if (!aligned(latent, 16) || !aligned(rope, 16) || !aligned(slots, 4) || !aligned(kv_cache, 16))
@@ -326,8 +329,8 @@ int mla_kv_append(const uint16_t* latent, const uint16_t* rope, const int32_t* s
   p.T = T;
   p.page_size = page_size;
   p.num_pages = num_pages;
-  p.fmt = fmt;
-  p.kv_scale = (fmt == MLA_KV_FP8_E4M3) ? kv_scale : 1.f;
+  p.fmt = fp8 ? kFmtFp8 : fmt;
+  p.kv_scale = fp8 ? kv_scale : 1.f;
   if (launch_kv_append(p, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }

@@ -17,6 +17,7 @@
 // One wavefront per token; lane g < 36 owns values 16g .. 16g+15 (latent for g < 32,
 // rope after), which is also one NVFP4 scale group, so no lane exchanges data.
 
+#include "mla_fp8.h"
 #include "mla_internal.h"
 
 namespace mla {
@@ -26,24 +27,6 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
 constexpr int kGroups = kRow / 16;  // 36 groups of 16 values per row
-
-// E4M3 code of a finite binary32 value: saturate at 448, round the magnitude to 3
-// mantissa bits (nearest, ties to even) on the binary32 bits for normal results
-// (>= 2^-6), on the 2^-9 subnormal grid below; the carry out of the mantissa moves into
-// the exponent, which is rebased from 127 to 7.
-__device__ __forceinline__ unsigned e4m3_code(float y) {
-  const unsigned sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fminf(fabsf(y), 448.0f);
-  unsigned mag;
-  if (a < 0.015625f) {
-    mag = (unsigned)__builtin_rintf(a * 512.0f);  // 0 .. 8 (8 is 2^-6, the smallest normal)
-  } else {
-    unsigned u = __float_as_uint(a);
-    u += 0x7FFFFu + ((u >> 20) & 1u);
-    mag = (u >> 20) - (120u << 3);
-  }
-  return sign | mag;
-}
 
 // E2M1 code of a finite binary32 value: the magnitude thresholds between the values
 // 0, .5, 1, 1.5, 2, 3, 4, 6 (a midpoint goes to the even code: > on the way to an odd

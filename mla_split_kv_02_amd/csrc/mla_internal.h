@@ -20,6 +20,7 @@ constexpr int kRowsPerGroup = kWaveRows * kWaves;  // query rows (query x head) 
 constexpr int kFmtBf16 = 0;
 constexpr int kFmtFp8 = 1;
 constexpr int kFmtNvfp4 = 2;
+constexpr int kFmtFp8Q = 3;  // FP8 cache, query rounded to E4M3, score product on FP8 MFMA
 
 // Everything one decode launch needs; passed by value as the kernel argument.
 struct DecodeParams {

@@ -26,6 +26,7 @@
 // Combine kernels.  One wavefront per output row merges the partials with the split-K
 // log-sum-exp reduce (TileGym page, forward: splitk_reduce).
 
+#include "mla_fp8.h"
 #include "mla_internal.h"
 
 #include <math.h>
@@ -35,6 +36,7 @@ namespace mla {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
@@ -48,6 +50,7 @@ constexpr int kDimBlocks = kLatent / 32;                  // 16 output blocks of
 constexpr int kRowChunks = kRow * 2 / 16;                 // 72 bf16 chunks of 16 B per token
 constexpr int kTileRowBytes = kRowChunks * 16;            // 1152
 constexpr int kTileBytes = kTileTokens * kTileRowBytes;   // 36864
+constexpr int kGroupBytes = kTileTokens * 128;            // 4096
 constexpr int kBf16Loads = kTileBytes / 1024;             // 36 wavefront loads of 1 KiB
 constexpr int kFp8RawBytes = kTileTokens * kRow;          // 18432
 constexpr int kFp8Loads = kFp8RawBytes / 1024;            // 18
@@ -61,23 +64,33 @@ constexpr int kNvRawBytes = kNvRawData + 256 * kNvScaleLoads;     // 10496
 constexpr float kTau = 8.0f;   // lazy rescale threshold (log2 units)
 constexpr float kLn2 = 0.69314718055994531f;
 
-// Buffers and load distance per cache format.  Tile i sits in bf16 buffer i % kTiles; raw
-// tile i (FP8 / NVFP4) in staging buffer i % kRaw.  In iteration i the loads of tile
-// i + kAhead are issued.
+// Buffers and load distance per cache format.  Tile i sits in bf16 buffer i % kTiles
+// (kStride bytes apart); raw tile i (FP8 / NVFP4) in staging buffer i % kRaw.  In
+// iteration i the loads of tile i + kAhead are issued.  With the FP8 query the scores
+// read the raw FP8 tile itself, so it stays until its own iteration (three staging
+// buffers) and the bf16 tile holds only the 512 latent dims the output product needs.
 template <int FMT> struct Pipe;
 template <> struct Pipe<kFmtBf16> {
-  static constexpr int kTiles = 4, kRaw = 0, kRawBytes = 0, kAhead = 2, kLoads = kBf16Loads;
+  static constexpr int kTiles = 4, kStride = kTileBytes, kRaw = 0, kRawBytes = 0, kAhead = 2, kLoads = kBf16Loads;
 };
 template <> struct Pipe<kFmtFp8> {
-  static constexpr int kTiles = 3, kRaw = 2, kRawBytes = kFp8RawBytes, kAhead = 2, kLoads = kFp8Loads;
+  static constexpr int kTiles = 3, kStride = kTileBytes, kRaw = 2, kRawBytes = kFp8RawBytes, kAhead = 2,
+                       kLoads = kFp8Loads;
 };
 template <> struct Pipe<kFmtNvfp4> {
-  static constexpr int kTiles = 3, kRaw = 3, kRawBytes = kNvRawBytes, kAhead = 3,
+  static constexpr int kTiles = 3, kStride = kTileBytes, kRaw = 3, kRawBytes = kNvRawBytes, kAhead = 3,
                        kLoads = kNvDataLoads + kNvScaleLoads;
 };
+template <> struct Pipe<kFmtFp8Q> {
+  static constexpr int kTiles = 3, kStride = 8 * kGroupBytes, kRaw = 3, kRawBytes = kFp8RawBytes, kAhead = 2,
+                       kLoads = kFp8Loads;
+};
 template <int FMT> constexpr int smem_bytes() {
-  return Pipe<FMT>::kTiles * kTileBytes + Pipe<FMT>::kRaw * Pipe<FMT>::kRawBytes;
+  return Pipe<FMT>::kTiles * Pipe<FMT>::kStride + Pipe<FMT>::kRaw * Pipe<FMT>::kRawBytes;
 }
+static_assert(smem_bytes<kFmtBf16>() <= 160 * 1024 && smem_bytes<kFmtFp8>() <= 160 * 1024 &&
+                  smem_bytes<kFmtNvfp4>() <= 160 * 1024 && smem_bytes<kFmtFp8Q>() <= 160 * 1024,
+              "LDS budget");
 
 // Byte offset of 16-byte chunk c (0..71) of token row r in a bf16 tile.  The tile is
 // nine 4 KiB groups, one per 8 chunks (128 bytes) of every row: group c / 8 holds
@@ -92,7 +105,6 @@ template <int FMT> constexpr int smem_bytes() {
 //           eight apart land in opposite halves of the 8-chunk group (position bit 2);
 //   dequantisation writes: rows r, r+1 at all 8 chunks of a group.
 // With u = (r / 2) % 8: position bit 2 = u0 ^ u2 ^ (r / 16) % 2, bits 1..0 = (u2, u1).
-constexpr int kGroupBytes = kTileTokens * 128;            // 4096
 __device__ __forceinline__ int swz(int r) { return ((((r >> 1) ^ (r >> 3) ^ (r >> 4)) & 1) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int tile_off(int r, int c) {
   return kGroupBytes * (c >> 3) + 128 * r + (((c & 7) ^ swz(r)) << 4);
@@ -240,13 +252,20 @@ __device__ __forceinline__ void load_bf16_tile(const Src& S, int tb, const uint8
 }
 
 // FP8 rows, raw.  Staging layout: chunk c (16 codes) of row r at 2048 (c / 4) + 64 r +
-// 16 (c % 4).  Instruction j = 4m + w covers chunk group j / 2 of rows 16 (j % 2) ..:
-// lane l takes row 16 (w % 2) + l / 4 and chunk 4 (w / 2 + 2m) + l % 4.
+// 16 p, p = (c % 4) ^ fswz(r) when SWZ, else c % 4.  Instruction j = 4m + w covers chunk
+// group j / 2 of rows 16 (j % 2) ..: lane l takes row 16 (w % 2) + l / 4 and the chunk
+// 4 (w / 2 + 2m) + c % 4 that belongs at position l % 4.  The swizzle serves the FP8
+// score reads (two 16-byte chunks of one row per lane and step): any 16 consecutive rows
+// at one logical chunk hit 16 different 16-byte bank slots, and so do 32 rows mod 32.
+__device__ __forceinline__ int fswz(int r) { return ((r >> 2) ^ (r >> 4)) & 3; }
+
+template <bool SWZ>
 __device__ __forceinline__ void load_fp8_raw(const Src& S, int tb, const uint8_t* pg, uint32_t st, int wave, int lane) {
   const int rip = tb & (S.p->page_size - 1);
   const int r = 16 * (wave & 1) + (lane >> 2);
   const int tok = min(tb + r, S.n - 1);
-  const uint32_t voff = (uint32_t)((rip + tok - tb) * kRow + 16 * (4 * (wave >> 1) + (lane & 3)));
+  const int c4 = SWZ ? ((lane & 3) ^ fswz(r)) : (lane & 3);
+  const uint32_t voff = (uint32_t)((rip + tok - tb) * kRow + 16 * (4 * (wave >> 1) + c4));
 #pragma unroll
   for (int m = 0; m < 5; ++m) {
     if (4 * m + wave >= kFp8Loads) break;
@@ -281,15 +300,21 @@ __device__ __forceinline__ void load_nvfp4_raw(const Src& S, int tb, const uint8
   }
 }
 
-// Raw FP8 staging -> bf16 tile.  Thread t writes chunk t % 8 of group m (m = 0..8) of
-// row t / 8: eight codes read as 8 bytes (raw chunk c / 2 of the row, half c % 2), four
-// converts, one 16-byte write.  Sixteen lanes cover two rows x one whole group.
+// Raw FP8 staging -> bf16 tile.  Thread t writes chunk t % 8 of group m (m < NG) of
+// row t / 8: eight codes read as 8 bytes (raw chunk (t % 8) / 2 of the row, half t % 2),
+// four converts, one 16-byte write.  Sixteen lanes cover two rows x one whole group.
+template <bool SWZ>
+__device__ __forceinline__ uint32_t fp8_dq_read_offset(int tid) {  // + 2048 m
+  const int r = tid >> 3, t7 = tid & 7;
+  return 64 * r + 16 * (SWZ ? ((t7 >> 1) ^ fswz(r)) : (t7 >> 1)) + 8 * (t7 & 1);
+}
+template <bool SWZ, int NG>
 __device__ __forceinline__ void dequant_fp8(uint32_t st, uint32_t tile, int tid) {
   const int r = tid >> 3, t7 = tid & 7;
-  const uint32_t rd = st + 64 * r + 8 * t7;                  // + 2048 m
+  const uint32_t rd = st + fp8_dq_read_offset<SWZ>(tid);     // + 2048 m
   const uint32_t wr = tile + 128 * r + ((t7 ^ swz(r)) << 4);  // + 4096 m
 #pragma unroll
-  for (int m = 0; m < 9; ++m) {
+  for (int m = 0; m < NG; ++m) {
     typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
     const u32x2 v = *at<u32x2>(rd + 2048 * m);
     unsigned t[4];
@@ -467,6 +492,67 @@ __device__ __forceinline__ f32x16 qk_tile(const bf16x8* q, uint32_t tile, const 
   return s;
 }
 
+
+// Scores of one tile with the FP8 query: S^T[token][row] on 9 MFMA 32x32x64 FP8 (E4M3 x
+// E4M3), A = the raw K codes of the lane's token row straight from the staging buffer,
+// B = the query codes (in registers).  K-step k covers dims 64k .. 64k+63 (raw chunk
+// group k); lane half h takes dims 64k + 32h .. + 31 as bytes 0..31 of its operand, in
+// both operands (the matrix core pairs equal byte positions of equal lane halves), read
+// as chunks 2h, 2h+1 at f[e] + 2048 k.  The operand buffers are five fixed 8-register
+// blocks (v216..v255) so that each 16-byte read can fill half of one: reads run three
+// K-steps ahead and a buffer is refilled two steps after its last MFMA; every wait counts
+// the reads issued after the one it needs (they complete in order).  Accumulation is in
+// vector registers, as in qk_tile; the closing s_nop run covers the wait states a vector
+// read of the result needs after this 16-pass MFMA.
+__device__ __forceinline__ f32x16 qk_tile_f8(const i32x8* q, uint32_t raw, const uint32_t* f) {
+  const uint32_t f0 = raw + f[0], f1 = raw + f[1];
+  f32x16 s;
+  asm volatile(
+      "ds_read_b128 v[216:219], %[f0] offset:0\n\t"
+      "ds_read_b128 v[220:223], %[f1] offset:0\n\t"
+      "ds_read_b128 v[224:227], %[f0] offset:2048\n\t"
+      "ds_read_b128 v[228:231], %[f1] offset:2048\n\t"
+      "ds_read_b128 v[232:235], %[f0] offset:4096\n\t"
+      "ds_read_b128 v[236:239], %[f1] offset:4096\n\t"
+      "ds_read_b128 v[240:243], %[f0] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[f1] offset:6144\n\t"
+      "s_waitcnt lgkmcnt(6)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[216:223], %[q0], 0\n\t"
+      "ds_read_b128 v[248:251], %[f0] offset:8192\n\t"
+      "ds_read_b128 v[252:255], %[f1] offset:8192\n\t"
+      "s_waitcnt lgkmcnt(6)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[224:231], %[q1], %[s]\n\t"
+      "ds_read_b128 v[216:219], %[f0] offset:10240\n\t"
+      "ds_read_b128 v[220:223], %[f1] offset:10240\n\t"
+      "s_waitcnt lgkmcnt(6)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[232:239], %[q2], %[s]\n\t"
+      "ds_read_b128 v[224:227], %[f0] offset:12288\n\t"
+      "ds_read_b128 v[228:231], %[f1] offset:12288\n\t"
+      "s_waitcnt lgkmcnt(6)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[240:247], %[q3], %[s]\n\t"
+      "ds_read_b128 v[232:235], %[f0] offset:14336\n\t"
+      "ds_read_b128 v[236:239], %[f1] offset:14336\n\t"
+      "s_waitcnt lgkmcnt(6)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[248:255], %[q4], %[s]\n\t"
+      "ds_read_b128 v[240:243], %[f0] offset:16384\n\t"
+      "ds_read_b128 v[244:247], %[f1] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(6)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[216:223], %[q5], %[s]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[224:231], %[q6], %[s]\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[232:239], %[q7], %[s]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[240:247], %[q8], %[s]\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : [s] "=&v"(s)
+      : [f0] "v"(f0), [f1] "v"(f1),
+        [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]),
+        [q5] "v"(q[5]), [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8])
+      : "memory", "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255");
+  return s;
+}
+
 // Output product of one tile: O^T[dim][row] += V^T[dim][token] . P^T[token][row] for the
 // 16 blocks of 32 dims and the two K-steps of 16 tokens.  V^T comes from two transpose
 // reads per operand (vb[2e]: tokens 4e .. of the lane's half.  Dims 32 apart are 4
@@ -621,7 +707,8 @@ __device__ __forceinline__ void softmax_piece(int k, Softmax& S, float* x, float
 
 // Output product of tile i-1 (vtile, P^T in pp) with, between its MFMAs, the softmax of
 // tile i (raw scores x -> P^T in pn, factor alpha) and, for FP8, the dequantisation of
-// raw tile i+1 (staging st -> bf16 tile dtile; the same work as dequant_fp8).
+// raw tile i+1 (staging st -> bf16 tile dtile; the same work as dequant_fp8, latent
+// groups only for the FP8 query).
 template <int FMT>
 __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const unsigned* pp, const int* vb, float* x,
                                              Softmax& S, float c, unsigned* pn, float& alpha, uint32_t st,
@@ -640,8 +727,10 @@ __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const un
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at<s16x4>(base[2 + flip] + off));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
+  constexpr bool kDq = (FMT == kFmtFp8 || FMT == kFmtFp8Q);
+  constexpr int kNg = (FMT == kFmtFp8Q) ? 8 : 9;  // groups to dequantise (latent only for the FP8 query)
   const int r = tid >> 3, t7 = tid & 7;
-  const uint32_t rd = st + 64 * r + 8 * t7;                   // FP8 dequantisation (see dequant_fp8)
+  const uint32_t rd = st + fp8_dq_read_offset<FMT == kFmtFp8Q>(tid);  // FP8 dequantisation (see dequant_fp8)
   const uint32_t wr = dtile + 128 * r + ((t7 ^ swz(r)) << 4);
   u32x2 raw[9];
   SoftmaxPieces w;
@@ -654,9 +743,9 @@ __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const un
     o[k & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k], (k < kDimBlocks) ? pb0 : pb1, o[k & 15], 0, 0, 0);
     if (k + kAhead < 2 * kDimBlocks) va[k + kAhead] = tr(k + kAhead);
     softmax_piece(k, S, x, c, w, pn, alpha);
-    if (FMT == kFmtFp8) {
-      if ((k & 1) == 0 && k / 2 < 9) raw[k / 2] = *at<u32x2>(rd + 2048 * (k / 2));
-      if ((k & 1) == 0 && k >= 2 && k / 2 - 1 < 9) {
+    if (kDq) {
+      if ((k & 1) == 0 && k / 2 < kNg) raw[k / 2] = *at<u32x2>(rd + 2048 * (k / 2));
+      if ((k & 1) == 0 && k >= 2 && k / 2 - 1 < kNg) {
         const int m = k / 2 - 1;
         unsigned t[4];
         fp8x4_to_bf16(raw[m][0], t[0], t[1]);
@@ -686,16 +775,40 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
   const float c = fmaxf(p.score_scale, 1e-30f);           // sm_scale = 0 gives the plain mean
   const int nt = lt1 - lt0;
 
-  // Q^T operand: row rc, dims 16k + 8 (l / 32) .. + 8
-  bf16x8 q[kKSteps];
+  // Q^T operand, row rc.  bf16: dims 16k + 8 (l / 32) .. + 8.  FP8 query: the E4M3 codes
+  // of dims 64k + 32 (l / 32) .. + 32, byte j of the operand holding dim 64k + 32 (l / 32)
+  // + j (TokenSpeed page, forward_decode: the query is cast to the FP8 cache type).
+  constexpr bool kQ8 = (FMT == kFmtFp8Q);
+  bf16x8 q[kQ8 ? 1 : kKSteps];
+  i32x8 q8[kQ8 ? 9 : 1];
   {
     const uint16_t* qrow = p.q + ((int64_t)b * p.rows + rc) * kLatent;
     const uint16_t* prow = p.qpe + ((int64_t)b * p.rows + rc) * kRope;
+    if constexpr (kQ8) {
 #pragma unroll
-    for (int k = 0; k < kKSteps; ++k) {
-      const int d = 16 * k + 8 * lh;
-      const uint16_t* src = (d < kLatent) ? qrow + d : prow + (d - kLatent);
-      q[k] = *reinterpret_cast<const bf16x8*>(src);
+      for (int k = 0; k < 9; ++k) {
+        const int d = 64 * k + 32 * lh;
+        const u32x4* src = reinterpret_cast<const u32x4*>((d < kLatent) ? qrow + d : prow + (d - kLatent));
+        i32x8 v = {};
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+          const u32x4 raw = src[w4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {  // dims 8 w4 + 2e, 8 w4 + 2e + 1
+            const unsigned lo = e4m3_code(__uint_as_float(raw[e] << 16));
+            const unsigned hi = e4m3_code(__uint_as_float(raw[e] & 0xFFFF0000u));
+            v[2 * w4 + (e >> 1)] |= (int)((lo | (hi << 8)) << (16 * (e & 1)));
+          }
+        }
+        q8[k] = v;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kKSteps; ++k) {
+        const int d = 16 * k + 8 * lh;
+        const uint16_t* src = (d < kLatent) ? qrow + d : prow + (d - kLatent);
+        q[k] = *reinterpret_cast<const bf16x8*>(src);
+      }
     }
   }
   // query i of a request sees tokens 0 .. n - q_len + i
@@ -710,6 +823,9 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
 #pragma unroll
     for (int x = 0; x < 4; ++x) ab[x] = a_base ^ (32 * x);
   }
+  uint32_t fq[2];  // FP8-query score reads: chunks 2h, 2h+1 of token row l % 32 (see qk_tile_f8)
+#pragma unroll
+  for (int e = 0; e < 2; ++e) fq[e] = 64 * lr + 16 * ((2 * lh + e) ^ fswz(lr));
   // transpose reads: in a group of 16 lanes (g = l / 16, j = l % 16), lane j addresses
   // token 8 (g >> 1) + 4e + j / 4 and dims 16 (g & 1) + 4 (j % 4) .. + 4; lane i of the
   // group then receives dim 16 (g & 1) + i of those four tokens
@@ -738,11 +854,11 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
   // buffer addresses go through readfirstlane, which keeps the loop optimiser from
   // turning every per-lane LDS address into an induction variable of its own
   auto tile_buf = [&](int i) {
-    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(smem + (uint32_t)((i % PP::kTiles) * kTileBytes)));
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(smem + (uint32_t)((i % PP::kTiles) * PP::kStride)));
   };
   auto raw_buf = [&](int i) {
     return (uint32_t)__builtin_amdgcn_readfirstlane(
-        (int)(smem + (uint32_t)(PP::kTiles * kTileBytes + (i % (PP::kRaw ? PP::kRaw : 1)) * PP::kRawBytes)));
+        (int)(smem + (uint32_t)(PP::kTiles * PP::kStride + (i % (PP::kRaw ? PP::kRaw : 1)) * PP::kRawBytes)));
   };
   auto entry = [&](int i) {  // block-table entry of tile i (paged caches)
     return PAGED ? table_entry(src, (lt0 + min(i, nt - 1)) * kTileTokens) : 0;
@@ -751,12 +867,13 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
     const int tb = (lt0 + i) * kTileTokens;
     const uint8_t* pg = PAGED ? page_start(src, e) : nullptr;
     if (FMT == kFmtBf16) load_bf16_tile<PAGED>(src, tb, pg, tile_buf(i), wave, lane);
-    else if (FMT == kFmtFp8) load_fp8_raw(src, tb, pg, raw_buf(i), wave, lane);
+    else if (FMT == kFmtFp8 || FMT == kFmtFp8Q) load_fp8_raw<FMT == kFmtFp8Q>(src, tb, pg, raw_buf(i), wave, lane);
     else load_nvfp4_raw(src, tb, pg, raw_buf(i), wave, lane);
   };
   int e_next = 0;  // block-table entry of tile i + kAhead, read one tile early
   auto dequant = [&](int i) {  // raw tile i -> its bf16 buffer
-    if (FMT == kFmtFp8) dequant_fp8(raw_buf(i), tile_buf(i), tid);
+    if (FMT == kFmtFp8) dequant_fp8<false, 9>(raw_buf(i), tile_buf(i), tid);
+    else if (FMT == kFmtFp8Q) dequant_fp8<true, 8>(raw_buf(i), tile_buf(i), tid);
     else if (FMT == kFmtNvfp4) dequant_nvfp4(raw_buf(i), tile_buf(i), tid);
   };
 
@@ -769,7 +886,9 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
       e_next = entry(i + PP::kAhead + 1);
     }
     if (!first && __any(alpha_prev != 1.f)) rescale(o, alpha_prev);
-    const f32x16 s = qk_tile(q, tile_buf(i), ab);
+    f32x16 s;
+    if constexpr (kQ8) s = qk_tile_f8(q8, raw_buf(i), fq);  // the raw tile itself
+    else s = qk_tile(q, tile_buf(i), ab);
     float x[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) x[v] = s[v];
@@ -795,7 +914,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
     alpha_prev = alpha;
     // the loads the next tile depends on: bf16 tile i+1 (issued one tile ago), raw tile
     // i+2 (issued now for FP8, one tile ago for NVFP4)
-    if (FMT == kFmtFp8) wait_vmcnt(0);
+    if (FMT == kFmtFp8 || FMT == kFmtFp8Q) wait_vmcnt(0);
     else wait_vmcnt(more ? nloads : 0);
     __syncthreads();
   };
@@ -1023,8 +1142,11 @@ hipError_t launch_decode_paged(int fmt, const DecodeParams& p, hipStream_t strea
     case kFmtFp8:
       hipLaunchKernelGGL(decode_paged_kernel<kFmtFp8>, dim3(blocks), dim3(kThreads), 0, stream, p);
       break;
-    default:
+    case kFmtNvfp4:
       hipLaunchKernelGGL(decode_paged_kernel<kFmtNvfp4>, dim3(blocks), dim3(kThreads), 0, stream, p);
+      break;
+    default:
+      hipLaunchKernelGGL(decode_paged_kernel<kFmtFp8Q>, dim3(blocks), dim3(kThreads), 0, stream, p);
       break;
   }
   return hipGetLastError();

@@ -45,6 +45,7 @@ ROW = LATENT + ROPE
 FMT_BF16 = 0
 FMT_FP8 = 1
 FMT_NVFP4 = 2
+FMT_FP8_QFP8 = 3  # FP8 pages; the query is rounded to E4M3 before the scores (see paged_decode_request)
 
 NVFP4_GROUP = 16  # metrale page, ``mla_paged_decode_nvfp4``: one E4M3 scale per 16 values
 
@@ -140,7 +141,7 @@ def decode_bf16_bits(bits) -> np.ndarray:
 def page_row_bytes(fmt: int) -> int:
     """Bytes of one token row inside a page: 576 bf16 values, 576 FP8 codes, or 288
     packed E2M1 bytes plus 36 E4M3 scales (NVFP4)."""
-    return {FMT_BF16: 2 * ROW, FMT_FP8: ROW, FMT_NVFP4: ROW // 2 + ROW // NVFP4_GROUP}[fmt]
+    return {FMT_BF16: 2 * ROW, FMT_FP8: ROW, FMT_NVFP4: ROW // 2 + ROW // NVFP4_GROUP, FMT_FP8_QFP8: ROW}[fmt]
 
 
 def decode_page(page: np.ndarray, fmt: int, page_size: int, kv_scale: float = 1.0) -> np.ndarray:
@@ -161,7 +162,7 @@ def decode_page(page: np.ndarray, fmt: int, page_size: int, kv_scale: float = 1.
     if fmt == FMT_BF16:
         bits = page[: page_size * 2 * ROW].view(np.uint16).reshape(page_size, ROW)
         return decode_bf16_bits(bits)
-    if fmt == FMT_FP8:
+    if fmt in (FMT_FP8, FMT_FP8_QFP8):
         codes = page[: page_size * ROW].reshape(page_size, ROW)
         return kv_scale * decode_e4m3fn(codes)
     if fmt == FMT_NVFP4:
@@ -324,9 +325,18 @@ def paged_decode_request(q_b, qpe_b, cache, fmt: int, kv_scale: float, page_size
                          page_stride: int, block_row, n: int, sm_scale: float, heads=None):
     """One request of the paged op.  q_b [q_len,H,512], qpe_b [q_len,H,64] (float64
     values).  Returns O [q_len,H',512] and LSE [q_len,H'] for the chosen heads (all by
-    default)."""
+    default).
+
+    FMT_FP8_QFP8: TokenSpeed page, ``forward_decode``: with an FP8 cache the query is
+    cast to the cache's FP8 type before the kernel (and k_scale goes into the softmax
+    scale, which is what scoring against kv_scale * e4m3(code) computes).  The query and
+    its rope part are rounded to E4M3 here (quantize_e4m3: nearest, ties to even,
+    saturating at 448); everything after is the same definition."""
     q_b = np.asarray(q_b, np.float64)
     qpe_b = np.asarray(qpe_b, np.float64)
+    if fmt == FMT_FP8_QFP8:
+        q_b = decode_e4m3fn(quantize_e4m3(q_b.astype(np.float32)))
+        qpe_b = decode_e4m3fn(quantize_e4m3(qpe_b.astype(np.float32)))
     q_len, H, _ = q_b.shape
     hs = np.arange(H) if heads is None else np.asarray(heads)
     kv = gather_request(cache, fmt, kv_scale, page_size, page_stride, block_row, n)
@@ -417,7 +427,7 @@ def encode_row(row_bits: np.ndarray, fmt: int, kv_scale: float = 1.0) -> np.ndar
     if fmt == FMT_BF16:
         return row_bits.view(np.uint8).copy()
     x = decode_bf16_bits(row_bits).astype(np.float32)  # exact
-    if fmt == FMT_FP8:
+    if fmt in (FMT_FP8, FMT_FP8_QFP8):  # the same page bytes
         y = x / np.float32(kv_scale)
         return quantize_e4m3(y)
     if fmt == FMT_NVFP4:

@@ -81,7 +81,8 @@ def _paged(**kw):
     (dict(o=0), mla.MLA_ERR_INVALID_ARG),
     (dict(q=F + 8), mla.MLA_ERR_INVALID_ARG),
     (dict(ws=F + 16), mla.MLA_ERR_INVALID_ARG),
-    (dict(fmt=3), mla.MLA_ERR_UNSUPPORTED),
+    (dict(fmt=4), mla.MLA_ERR_UNSUPPORTED),
+    (dict(fmt=-1), mla.MLA_ERR_UNSUPPORTED),
     (dict(page_size=16), mla.MLA_ERR_UNSUPPORTED),
     (dict(page_size=128), mla.MLA_ERR_UNSUPPORTED),
     (dict(q_len=0), mla.MLA_ERR_UNSUPPORTED),
@@ -101,6 +102,8 @@ def _paged(**kw):
     (dict(B=4096, mb=1 << 14), mla.MLA_ERR_INVALID_ARG),
     (dict(kv_scale=0.0), mla.MLA_ERR_INVALID_ARG),
     (dict(kv_scale=float("nan")), mla.MLA_ERR_INVALID_ARG),
+    (dict(fmt=3, kv_scale=0.0), mla.MLA_ERR_INVALID_ARG),
+    (dict(fmt=3, stride=64 * 576 - 16), mla.MLA_ERR_INVALID_ARG),
     (dict(sm=float("inf")), mla.MLA_ERR_INVALID_ARG),
     (dict(sm=-0.125), mla.MLA_ERR_INVALID_ARG),
     (dict(ws_bytes=1000), mla.MLA_ERR_WORKSPACE_TOO_SMALL),
@@ -204,7 +207,8 @@ def _append(**kw):
     (dict(slots=F + 2), mla.MLA_ERR_INVALID_ARG),
     (dict(cache=F + 8), mla.MLA_ERR_INVALID_ARG),
     (dict(T=-1), mla.MLA_ERR_INVALID_ARG),
-    (dict(fmt=3), mla.MLA_ERR_UNSUPPORTED),
+    (dict(fmt=4), mla.MLA_ERR_UNSUPPORTED),
+    (dict(fmt=-1), mla.MLA_ERR_UNSUPPORTED),
     (dict(page_size=16), mla.MLA_ERR_UNSUPPORTED),
     (dict(num_pages=0), mla.MLA_ERR_INVALID_ARG),
     (dict(num_pages=1 << 25), mla.MLA_ERR_INVALID_ARG),

@@ -244,6 +244,78 @@ def test_paged_fp8_b64_h128_full_size_sampled():
     assert max_err(lse[pick], rl) <= TOL_LSE
 
 
+# ----------------------------------------------------------------------------------
+# FP8 query (format 3): same FP8 pages, query rounded to E4M3, scores on FP8 MFMA
+# ----------------------------------------------------------------------------------
+
+def _fp8q(w):
+    w.fmt = oracle.FMT_FP8_QFP8  # the FP8 workload's pages are the format's pages
+    return w
+
+
+@pytest.mark.parametrize("q_len", [1, 2])
+@pytest.mark.parametrize("page_size", [32, 64])
+def test_paged_fp8_query_matches_oracle(q_len, page_size):
+    say(f"paged fp8-query q_len={q_len} page={page_size}")
+    w = _fp8q(gen.make_paged(B=4, H=128, q_len=q_len, lo=1, hi=400, page_size=page_size, fmt=gen.FMT_FP8,
+                             seed=140 + q_len + page_size, seq_lens=[1, 63, 290, 97], max_blocks=16,
+                             poison_tail=True))
+    ro, rl = _paged_ref(w)
+    for ns in (None, 1, 5):
+        o, lse = _paged_run(w, ns)
+        assert max_err(o, ro) <= TOL_O_QUANT, ns
+        assert max_err(lse, rl) <= TOL_LSE, ns
+    # the query really is rounded: the bf16-query path on the same pages differs
+    w.fmt = gen.FMT_FP8
+    o1, _ = _paged_run(w)
+    assert max_err(o1, o) > 1e-3
+
+
+@pytest.mark.parametrize("H,q_len", [(16, 1), (48, 2), (64, 4), (128, 8)])
+def test_paged_fp8_query_head_and_query_counts(H, q_len):
+    say(f"paged fp8-query H={H} q_len={q_len}")
+    w = _fp8q(gen.make_paged(B=3, H=H, q_len=q_len, lo=8, hi=200, page_size=64, fmt=gen.FMT_FP8,
+                             seed=150 + H + q_len, max_blocks=4))
+    ro, rl = _paged_ref(w)
+    o, lse = _paged_run(w)
+    assert max_err(o, ro) <= TOL_O_QUANT and max_err(lse, rl) <= TOL_LSE
+
+
+def test_paged_fp8_query_rounding_ties_and_every_code():
+    """Every E4M3 code in the cache, and a query made of exact E4M3 midpoints (as bf16), so
+    the kernel's rounding of the query must break every tie as the oracle does."""
+    say("paged fp8-query ties")
+    w = _fp8q(gen.make_paged(B=1, H=16, q_len=1, lo=64, hi=64, page_size=64, fmt=gen.FMT_FP8, seed=163))
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    w.cache[:64 * 576] = np.resize(codes, 64 * 576)
+    w.block_tables[:] = 0
+    w.kv_scale = 1.0 / 128
+    v = oracle.decode_e4m3fn(np.arange(0x7F))
+    mids = ((v[:-1] + v[1:]) / 2)
+    mids = mids[(mids > 0.1) & (mids < 3)]  # keep the scores moderate
+    rng = np.random.default_rng(7)
+    vals = rng.choice(mids, size=w.q.size + w.qpe.size) * rng.choice([-1.0, 1.0], size=w.q.size + w.qpe.size)
+    bits = gen.to_bf16_bits(vals.astype(np.float32))
+    assert np.array_equal(gen.bf16_bits_to_f32(bits), vals.astype(np.float32))  # exact in bf16
+    w.q = bits[:w.q.size].reshape(w.q.shape)
+    w.qpe = bits[w.q.size:].reshape(w.qpe.shape)
+    ro, rl = _paged_ref(w)
+    o, lse = _paged_run(w)
+    assert max_err(o, ro) <= TOL_O_QUANT and max_err(lse, rl) <= TOL_LSE
+
+
+def test_paged_fp8_query_b64_h128_full_size_sampled():
+    say("paged_fp8_b64_h128 fp8-query full size")
+    w = _fp8q(gen.make_workload("paged_fp8_b64_h128_s1k_32k"))
+    o, lse = _paged_run(w, mla.plan_paged(256, w.B, w.q_len, w.H))
+    assert np.isfinite(o).all()
+    order = np.argsort(w.seq_lens)
+    pick = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
+    ro, rl = _paged_ref(w, requests=pick)
+    assert max_err(o[pick], ro) <= TOL_O_QUANT
+    assert max_err(lse[pick], rl) <= TOL_LSE
+
+
 @pytest.mark.slow
 def test_paged_nvfp4_b128_h128_q2_full_size_sampled():
     say("paged_nvfp4_b128_h128_q2 full size")

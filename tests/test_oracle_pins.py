@@ -554,3 +554,32 @@ def test_quantiser_pins_catch_planted_mistakes(kind, monkeypatch):
         except (AssertionError, IndexError):
             failed += 1
     assert failed >= 1
+
+
+def test_fp8_query_decode_matches_torch():
+    """The FP8-query decode (format 3) against torch in float64: the query is cast with
+    torch's own float8_e4m3fn (round to nearest even; N(0,1) queries stay far below its
+    overflow), the cache codes decoded by torch, then a max-shifted softmax, with the
+    causal verify rows of q_len 2."""
+    w = gen.make_paged(B=2, H=16, q_len=2, lo=5, hi=90, page_size=32, fmt=gen.FMT_FP8, seed=91, max_blocks=4)
+    q, qpe = w.q_f64()
+    ro, rl = oracle.paged_decode(q, qpe, w.cache, oracle.FMT_FP8_QFP8, w.kv_scale, w.page_size, w.page_stride,
+                                 w.block_tables, w.seq_lens, w.sm_scale)
+    f8 = torch.float8_e4m3fn
+    for b in range(w.B):
+        n = int(w.seq_lens[b])
+        pages = [int(w.block_tables[b, i]) for i in range(-(-n // w.page_size))]
+        kv = torch.cat([torch.from_numpy(w.cache[p * w.page_stride: p * w.page_stride + w.page_size * 576].copy())
+                        .view(f8).to(torch.float64).reshape(w.page_size, 576) for p in pages])[:n] * w.kv_scale
+        qt = torch.from_numpy(np.concatenate([q[b], qpe[b]], -1).astype(np.float32)).to(f8).to(torch.float64)
+        for i in range(w.q_len):
+            vis = n - w.q_len + i + 1
+            s = (qt[i] @ kv[:vis].T) * w.sm_scale
+            lse = torch.logsumexp(s, -1)
+            o = torch.softmax(s, -1) @ kv[:vis, :512]
+            assert np.max(np.abs(o.numpy() - ro[b, i])) < 1e-9
+            assert np.max(np.abs(lse.numpy() - rl[b, i])) < 1e-9
+    # and it is not the bf16-query result
+    r1, _ = oracle.paged_decode(q, qpe, w.cache, oracle.FMT_FP8, w.kv_scale, w.page_size, w.page_stride,
+                                w.block_tables, w.seq_lens, w.sm_scale)
+    assert np.max(np.abs(r1 - ro)) > 1e-4
