@@ -107,6 +107,41 @@ def copy_calibration(torch, dev, nbytes: int, steps: int):
     print(json.dumps({"copy_calibration_bytes": nbytes, "steps": steps}), flush=True)
 
 
+# Score flops run at the FP8 rate and output flops at the bf16 rate in the FP8-query
+# variant: per (row, token) pair 1152 flops at 5.0 PFLOP/s and 1024 at 2.5 PFLOP/s.
+MFMA_FP8_PEAK_TFLOPS = 5000.0
+MIXED_PEAK_TFLOPS = 2176.0 / (1152.0 / MFMA_FP8_PEAK_TFLOPS + 1024.0 / MFMA_BF16_PEAK_TFLOPS)
+
+
+def time_fp8_query_variant(mla, torch, w, q, qpe, cache, bt, sl, G, args, flops):
+    """The same pages decoded as format 3 (query rounded to E4M3, FP8-MFMA scores): same
+    steps, same timing, reported beside the headline (which is the bf16-query path)."""
+    call = mla.PagedCall(q, qpe, cache, mla.MLA_KV_FP8_E4M3_QFP8, bt, sl, w.page_size, w.page_stride, w.kv_scale,
+                         w.sm_scale, num_splits=G)
+    for _ in range(args.warmup):
+        call.partials()
+        call.combine()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record()
+        call.partials()
+        ev[k][1].record()
+        call.combine()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
+    dec = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    dec_tflops = flops / (dec * 1e-3) / 1e12
+    log(f"[bench] fp8-query variant: {ms_step:.4f} ms/step, decode {dec:.4f} ms")
+    return {"kv_format": "fp8_e4m3, query rounded to e4m3 (FP8-MFMA scores, bf16 output product)",
+            "ms_per_step": round(ms_step, 5), "value": round(flops / (ms_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+            "decode_ms": round(dec, 5),
+            "roofline": {"bound": "mfma", "achieved": round(dec_tflops, 3), "peak": round(MIXED_PEAK_TFLOPS, 1),
+                         "unit": "TFLOP/s", "frac": round(dec_tflops / MIXED_PEAK_TFLOPS, 4),
+                         "peak_note": "score flops at the fp8 peak, output flops at the bf16 peak"}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +151,8 @@ def main():
     ap.add_argument("--num-splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-variant", action="store_true",
+                    help="skip the extra timing of the FP8-query variant on FP8 workloads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the decode, run torch's fill and copy kernels on buffers of this many MiB "
                          "(known HBM bytes, used to scale the FETCH_SIZE / WRITE_SIZE counters)")
@@ -203,6 +240,8 @@ def main():
                    "kernel_source_sha": src_hash},
         "roofline": roof,
     }
+    if w.fmt == gen.FMT_FP8 and not args.no_variant:
+        out["fp8_query_variant"] = time_fp8_query_variant(mla, torch, w, q, qpe, cache, bt, sl, G, args, flops)
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

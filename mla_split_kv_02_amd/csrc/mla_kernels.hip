@@ -37,6 +37,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
@@ -579,6 +580,64 @@ __device__ __forceinline__ void pv_tile(f32x16* o, uint32_t tile, const unsigned
   }
 }
 
+// FP8 query: the bf16 tile holds V^T, dim-major: dim d's 32 tokens as four 16-byte
+// chunks (8 tokens each) of a 64-byte row, chunk x at position x ^ fswz(d).  The output
+// MFMA's A operand (dims 32 db + l % 32, tokens 16 ks + 8 (l / 32) ..) is then one
+// 16-byte read at 2048 db + vq[2 ks + (db & 1)] (fswz(32 db + r) = fswz(r) ^ 2 (db & 1));
+// 16 consecutive dims at one chunk, and 32 mod 32, fall into different bank slots.
+__device__ __forceinline__ bf16x8 vt_read(uint32_t vt, const int* vq, int db, int ks) {
+  return *at<bf16x8>(vt + 2048 * db + vq[2 * ks + (db & 1)]);
+}
+
+__device__ __forceinline__ void pv_tile_vt(f32x16* o, uint32_t vt, const unsigned* pp, const int* vq) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pp[4 * ks], pp[4 * ks + 1], pp[4 * ks + 2], pp[4 * ks + 3]});
+#pragma unroll
+    for (int db = 0; db < kDimBlocks; ++db)
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_read(vt, vq, db, ks), pb, o[db], 0, 0, 0);
+  }
+}
+
+// FP8 query: raw FP8 staging (swizzled, token-major) -> V^T (dim-major, above).  Wave w,
+// step m (0..7) covers dims 128 w + 16 m .. + 15 of all 32 tokens with one 8-bit transpose
+// read: in each 16-lane group g, lane s addresses token 8 g + s / 2, dims + 8 (s % 2) .. + 8
+// (8 code bytes), and lane j receives dim + j of those 8 tokens (byte b = token 8 g + b);
+// four converts give its 8 bf16 values, written as chunk g of the dim's row.
+struct DqVt {
+  uint32_t rd;     // raw read base of this lane (+ 4096 w + 64 tok + 8 (s % 2))
+  int ro[4];       // + 16 ((m % 4) ^ fswz(tok)), by m % 4; + 2048 (m / 4)
+  uint32_t wr;     // V^T write base (+ 8192 w + 64 j)
+  int wo[4];       // + 16 ((g ^ (j / 4) ^ m) % 4), by m % 4; + 1024 m
+};
+__device__ __forceinline__ DqVt dq_vt_offsets(int tid) {
+  const int w = tid >> 6, l = tid & 63, g = l >> 4, j = l & 15;
+  const int tok = 8 * g + (j >> 1), f = fswz(tok);
+  DqVt d;
+  d.rd = 4096 * w + 64 * tok + 8 * (j & 1);
+  d.wr = 8192 * w + 64 * j;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    d.ro[m] = 16 * (m ^ f);
+    d.wo[m] = 16 * ((g ^ (j >> 2) ^ m) & 3);
+  }
+  return d;
+}
+__device__ __forceinline__ i32x2 dq_vt_read(uint32_t st, const DqVt& d, int m) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(at<i32x2>(st + d.rd + 2048 * (m >> 2) + d.ro[m & 3]));
+}
+__device__ __forceinline__ void dq_vt_write(uint32_t vt, const DqVt& d, int m, i32x2 raw) {
+  unsigned t[4];
+  fp8x4_to_bf16((unsigned)raw[0], t[0], t[1]);
+  fp8x4_to_bf16((unsigned)raw[1], t[2], t[3]);
+  *at<u32x4>(vt + d.wr + 1024 * m + d.wo[m & 3]) = u32x4{t[0], t[1], t[2], t[3]};
+}
+__device__ __forceinline__ void dequant_fp8q(uint32_t st, uint32_t vt, int tid) {
+  const DqVt d = dq_vt_offsets(tid);
+#pragma unroll
+  for (int m = 0; m < 8; ++m) dq_vt_write(vt, d, m, dq_vt_read(st, d, m));
+}
+
 // o *= alpha in place in the accumulation registers, one value at a time through one
 // vector register.
 __device__ __forceinline__ void rescale(f32x16* o, float alpha) {
@@ -721,18 +780,30 @@ __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const un
   const bf16x8 pb0 = __builtin_bit_cast(bf16x8, u32x4{pp[0], pp[1], pp[2], pp[3]});
   const bf16x8 pb1 = __builtin_bit_cast(bf16x8, u32x4{pp[4], pp[5], pp[6], pp[7]});
   auto tr = [&](int k) {  // V^T operand of output MFMA k (dims block k % 16, K-step k / 16)
+    if constexpr (FMT == kFmtFp8Q) return *at<bf16x8>(base[2 * (k >> 4) + (k & 1)] + 2048 * (k & 15));
     const int db = k & 15, ks = k >> 4, flip = (db & 1) ^ ks;
     const uint32_t off = kGroupBytes * (db >> 1) + 16 * 128 * ks;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at<s16x4>(base[flip] + off));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at<s16x4>(base[2 + flip] + off));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  constexpr bool kDq = (FMT == kFmtFp8 || FMT == kFmtFp8Q);
-  constexpr int kNg = (FMT == kFmtFp8Q) ? 8 : 9;  // groups to dequantise (latent only for the FP8 query)
+  constexpr bool kDq = (FMT == kFmtFp8);
   const int r = tid >> 3, t7 = tid & 7;
-  const uint32_t rd = st + fp8_dq_read_offset<FMT == kFmtFp8Q>(tid);  // FP8 dequantisation (see dequant_fp8)
+  const uint32_t rd = st + fp8_dq_read_offset<false>(tid);  // FP8 dequantisation (see dequant_fp8)
   const uint32_t wr = dtile + 128 * r + ((t7 ^ swz(r)) << 4);
   u32x2 raw[9];
+  // FP8 query: dim-major dequantisation (see dequant_fp8q), with the per-lane parts of
+  // the addresses added once so that each access only adds an immediate offset
+  uint32_t qrd[4], qwr[4];
+  i32x2 rawq[8];
+  if constexpr (FMT == kFmtFp8Q) {
+    const DqVt dq = dq_vt_offsets(tid);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      qrd[x] = st + dq.rd + dq.ro[x];
+      qwr[x] = dtile + dq.wr + dq.wo[x];
+    }
+  }
   SoftmaxPieces w;
   bf16x8 va[2 * kDimBlocks];
 #pragma unroll
@@ -743,9 +814,22 @@ __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const un
     o[k & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k], (k < kDimBlocks) ? pb0 : pb1, o[k & 15], 0, 0, 0);
     if (k + kAhead < 2 * kDimBlocks) va[k + kAhead] = tr(k + kAhead);
     softmax_piece(k, S, x, c, w, pn, alpha);
+    if constexpr (FMT == kFmtFp8Q) {
+      if ((k & 1) == 0 && k / 2 < 8) {
+        const int m = k / 2;
+        rawq[m] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(at<i32x2>(qrd[m & 3] + 2048 * (m >> 2)));
+      }
+      if ((k & 1) == 0 && k >= 2 && k / 2 - 1 < 8) {
+        const int m = k / 2 - 1;
+        unsigned t[4];
+        fp8x4_to_bf16((unsigned)rawq[m][0], t[0], t[1]);
+        fp8x4_to_bf16((unsigned)rawq[m][1], t[2], t[3]);
+        *at<u32x4>(qwr[m & 3] + 1024 * m) = u32x4{t[0], t[1], t[2], t[3]};
+      }
+    }
     if (kDq) {
-      if ((k & 1) == 0 && k / 2 < kNg) raw[k / 2] = *at<u32x2>(rd + 2048 * (k / 2));
-      if ((k & 1) == 0 && k >= 2 && k / 2 - 1 < kNg) {
+      if ((k & 1) == 0 && k / 2 < 9) raw[k / 2] = *at<u32x2>(rd + 2048 * (k / 2));
+      if ((k & 1) == 0 && k >= 2 && k / 2 - 1 < 9) {
         const int m = k / 2 - 1;
         unsigned t[4];
         fp8x4_to_bf16(raw[m][0], t[0], t[1]);
@@ -829,8 +913,11 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
   // transpose reads: in a group of 16 lanes (g = l / 16, j = l % 16), lane j addresses
   // token 8 (g >> 1) + 4e + j / 4 and dims 16 (g & 1) + 4 (j % 4) .. + 4; lane i of the
   // group then receives dim 16 (g & 1) + i of those four tokens
-  int vb[4];  // transpose-read offsets [e][db & 1] (see pv_tile)
-  {
+  int vb[4];  // transpose-read offsets [e][db & 1] (see pv_tile); FP8 query: V^T read offsets (see vt_read)
+  if constexpr (FMT == kFmtFp8Q) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) vb[x] = 64 * lr + 16 * (((2 * (x >> 1) + lh) ^ fswz(lr) ^ (2 * (x & 1))) & 3);
+  } else {
     const int g = lane >> 4, j = lane & 15;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -873,7 +960,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
   int e_next = 0;  // block-table entry of tile i + kAhead, read one tile early
   auto dequant = [&](int i) {  // raw tile i -> its bf16 buffer
     if (FMT == kFmtFp8) dequant_fp8<false, 9>(raw_buf(i), tile_buf(i), tid);
-    else if (FMT == kFmtFp8Q) dequant_fp8<true, 8>(raw_buf(i), tile_buf(i), tid);
+    else if (FMT == kFmtFp8Q) dequant_fp8q(raw_buf(i), tile_buf(i), tid);
     else if (FMT == kFmtNvfp4) dequant_nvfp4(raw_buf(i), tile_buf(i), tid);
   };
 
@@ -933,7 +1020,8 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
     body(0, std::true_type{});
     for (int i = 1; i < nt; ++i) body(i, std::false_type{});
     if (__any(alpha_prev != 1.f)) rescale(o, alpha_prev);
-    pv_tile(o, tile_buf(nt - 1), pp, vb);
+    if constexpr (FMT == kFmtFp8Q) pv_tile_vt(o, tile_buf(nt - 1), pp, vb);
+    else pv_tile(o, tile_buf(nt - 1), pp, vb);
   }
 
   // ---- epilogue: normalised partial O and its lse ----
