@@ -145,8 +145,10 @@ def time_fp8_query_variant(mla, torch, w, q, qpe, cache, bt, sl, G, args, flops)
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the clocks take a few tens of milliseconds of load to settle (the first ~20 launches
+    # run ~20% slower), so the default warm-up is ~0.2 s of steps; the whole run stays < 1 s
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="paged_fp8_b64_h128_s1k_32k")
     ap.add_argument("--num-splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
