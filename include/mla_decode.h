@@ -186,6 +186,26 @@ int mla_paged_decode(const uint16_t* q, const uint16_t* qpe, const void* kv_cach
                      int num_splits, void* workspace, size_t workspace_bytes, uint16_t* o,
                      float* lse, void* stream);
 
+/* mla_paged_decode with a sliding window and per-head attention sinks (metrale page,
+ * mla_paged_decode_fp8: sliding_window and sinks arguments, sinks "per-head, FP32, may be
+ * null").  The page names them without defining them; this library reads them as:
+ *   sliding_window  W >= 0.  W > 0: query i of request b (position seq_lens[b] - q_len + i)
+ *                   sees only tokens max(0, position - W + 1) .. position.  0: no window
+ *                   (the same result as mla_paged_decode).
+ *   sinks           [H] fp32, device, or NULL.  sinks[h] is one more logit of head h, in the
+ *                   units of the scaled scores, that joins the softmax denominator and has
+ *                   no value: LSE = ln(exp(sinks[h]) + sum_t exp(s_t)),
+ *                   O = sum_t exp(s_t - LSE) * latent_t.  A row that sees no token gets O = 0
+ *                   and LSE = sinks[h].
+ * Every other argument, and every check, is that of mla_paged_decode; in addition
+ * sliding_window < 0 or a misaligned sinks pointer returns MLA_ERR_INVALID_ARG. */
+int mla_paged_decode_ext(const uint16_t* q, const uint16_t* qpe, const void* kv_cache, int fmt,
+                         float kv_scale, int num_pages, int page_size, int64_t page_stride_bytes,
+                         const int32_t* block_tables, int max_blocks_per_seq,
+                         const int32_t* seq_lens, int B, int q_len, int H, float sm_scale,
+                         int sliding_window, const float* sinks, int num_splits, void* workspace,
+                         size_t workspace_bytes, uint16_t* o, float* lse, void* stream);
+
 /* KV-cache append: store T new tokens into the paged pool before decoding them
  * (TokenSpeed page, forward_decode: each new token's latent and rope key are written into
  * the paged pool at its cache location before attention; metrale page,

@@ -41,6 +41,7 @@ EXPORTED_SYMBOLS = (
     "mla_paged_decode_partials",
     "mla_paged_combine",
     "mla_paged_decode",
+    "mla_paged_decode_ext",
     "mla_kv_append",
 )
 
@@ -86,6 +87,9 @@ def lib() -> ctypes.CDLL:
     L.mla_paged_decode.restype = c_int
     L.mla_paged_decode.argtypes = [vp, vp, vp, c_int, c_float, c_int, c_int, c_i64, vp, c_int, vp, c_int, c_int,
                                    c_int, c_float, c_int, vp, c_size, vp, vp, vp]
+    L.mla_paged_decode_ext.restype = c_int
+    L.mla_paged_decode_ext.argtypes = [vp, vp, vp, c_int, c_float, c_int, c_int, c_i64, vp, c_int, vp, c_int, c_int,
+                                       c_int, c_float, c_int, vp, c_int, vp, c_size, vp, vp, vp]
     L.mla_kv_append.restype = c_int
     L.mla_kv_append.argtypes = [vp, vp, vp, c_int, vp, c_int, c_float, c_int, c_int, c_i64, vp]
     _lib = L
@@ -217,7 +221,8 @@ class PagedCall:
     ``combine()`` enqueue its two launches, ``run()`` both through mla_paged_decode."""
 
     def __init__(self, q, qpe, kv_cache, fmt, block_tables, seq_lens, page_size, page_stride=None, kv_scale=1.0,
-                 sm_scale=None, num_splits=None, workspace=None, o=None, lse=None, want_lse=True, num_cus=None):
+                 sm_scale=None, num_splits=None, workspace=None, o=None, lse=None, want_lse=True, num_cus=None,
+                 window=0, sinks=None):
         B, q_len, H, _ = q.shape
         dev = q.device
         _need(q, "q", torch.bfloat16, (B, q_len, H, LATENT))
@@ -256,28 +261,45 @@ class PagedCall:
                            float(sm_scale), int(num_splits), _ptr(workspace), workspace.numel())
         self.combine_args = (_ptr(workspace), workspace.numel(), _ptr(seq_lens), B, q_len, H, int(num_splits),
                              int(block_tables.shape[1]), int(page_size), _ptr(o), _ptr(lse))
-        self._keep = (q, qpe, kv_cache, block_tables, seq_lens)
+        if sinks is not None:
+            _need(sinks, "sinks", torch.float32, (H,), dev)
+        self.window, self.sinks = int(window), sinks
+        self._keep = (q, qpe, kv_cache, block_tables, seq_lens, sinks)
+
+    def _plain(self):
+        return self.window == 0 and self.sinks is None
 
     def run(self):
-        _check(lib().mla_paged_decode(*self.cache_args, self.combine_args[-2], self.combine_args[-1],
-                                      _stream(self.dev)), "mla_paged_decode")
+        if self._plain():
+            _check(lib().mla_paged_decode(*self.cache_args, self.combine_args[-2], self.combine_args[-1],
+                                          _stream(self.dev)), "mla_paged_decode")
+        else:  # sliding window and / or sinks
+            a = self.cache_args
+            _check(lib().mla_paged_decode_ext(*a[:15], self.window, _ptr(self.sinks), *a[15:],
+                                              self.combine_args[-2], self.combine_args[-1], _stream(self.dev)),
+                   "mla_paged_decode_ext")
         return self.o, self.lse
 
     def partials(self):
+        if not self._plain():
+            raise ValueError("the separate launches take no window or sinks; use run()")
         _check(lib().mla_paged_decode_partials(*self.cache_args, _stream(self.dev)), "mla_paged_decode_partials")
 
     def combine(self):
+        if not self._plain():
+            raise ValueError("the separate launches take no window or sinks; use run()")
         _check(lib().mla_paged_combine(*self.combine_args, _stream(self.dev)), "mla_paged_combine")
         return self.o, self.lse
 
 
 def paged_decode(q, qpe, kv_cache, fmt, block_tables, seq_lens, page_size, page_stride=None, kv_scale=1.0,
-                 sm_scale=None, num_splits=None, workspace=None, o=None, lse=None, want_lse=True, num_cus=None):
+                 sm_scale=None, num_splits=None, workspace=None, o=None, lse=None, want_lse=True, num_cus=None,
+                 window=0, sinks=None):
     """Paged decode.  q [B,q_len,H,512], qpe [B,q_len,H,64] bf16; kv_cache uint8 page pool
     (num_pages * page_stride bytes); block_tables [B,max_blocks] int32; seq_lens [B] int32
     (device).  Returns (o [B,q_len,H,512] bf16, lse [B,q_len,H] f32 or None)."""
     return PagedCall(q, qpe, kv_cache, fmt, block_tables, seq_lens, page_size, page_stride, kv_scale, sm_scale,
-                     num_splits, workspace, o, lse, want_lse, num_cus).run()
+                     num_splits, workspace, o, lse, want_lse, num_cus, window, sinks).run()
 
 
 def kv_append(latent, rope, slots, kv_cache, fmt, page_size, page_stride=None, kv_scale=1.0):

@@ -187,7 +187,8 @@ int check_paged_shape(int B, int q_len, int H, int num_splits, const void* works
 int paged_partials(const uint16_t* q, const uint16_t* qpe, const void* kv_cache, int fmt, float kv_scale,
                    int num_pages, int page_size, int64_t page_stride_bytes, const int32_t* block_tables,
                    int max_blocks_per_seq, const int32_t* seq_lens, int B, int q_len, int H, float sm_scale,
-                   int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+                   int window, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (window < 0) return MLA_ERR_INVALID_ARG;
   if (!q || !qpe || !kv_cache || !block_tables || !seq_lens) return MLA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(qpe, 16) || !aligned(kv_cache, 16) || !aligned(block_tables, 4) ||
       !aligned(seq_lens, 4))
@@ -224,6 +225,7 @@ int paged_partials(const uint16_t* q, const uint16_t* qpe, const void* kv_cache,
   p.rows = q_len * H;
   p.row_groups = (p.rows + kRowsPerGroup - 1) / kRowsPerGroup;
   p.num_splits = num_splits;
+  p.window = window;
   p.score_scale = sm_scale * vs * kLog2e;
   p.v_scale = vs;
   p.o_part = reinterpret_cast<float*>(ws + L.o_off);
@@ -240,8 +242,10 @@ int paged_partials(const uint16_t* q, const uint16_t* qpe, const void* kv_cache,
 }
 
 int paged_combine(const void* workspace, size_t workspace_bytes, const int32_t* seq_lens, int B, int q_len, int H,
-                  int num_splits, int max_blocks_per_seq, int page_size, uint16_t* o, float* lse, void* stream) {
-  if (!seq_lens || !o || !aligned(seq_lens, 4) || !aligned(o, 16) || (lse && !aligned(lse, 4)))
+                  int num_splits, int max_blocks_per_seq, int page_size, const float* sinks, uint16_t* o,
+                  float* lse, void* stream) {
+  if (!seq_lens || !o || !aligned(seq_lens, 4) || !aligned(o, 16) || (lse && !aligned(lse, 4)) ||
+      (sinks && !aligned(sinks, 4)))
     return MLA_ERR_INVALID_ARG;
   PagedLayout L;
   const int st = check_paged_shape(B, q_len, H, num_splits, workspace, workspace_bytes, &L);
@@ -263,6 +267,8 @@ int paged_combine(const void* workspace, size_t workspace_bytes, const int32_t* 
   c.seg_last = reinterpret_cast<const int32_t*>(ws + L.last_off);
   c.info = reinterpret_cast<const int32_t*>(ws + L.info_off);
   c.max_len = max_blocks_per_seq * page_size;
+  c.sinks = sinks;
+  c.H = H;
   if (launch_combine_paged(c, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }
@@ -276,15 +282,15 @@ int mla_paged_decode_partials(const uint16_t* q, const uint16_t* qpe, const void
                               int max_blocks_per_seq, const int32_t* seq_lens, int B, int q_len, int H,
                               float sm_scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
   return paged_partials(q, qpe, kv_cache, fmt, kv_scale, num_pages, page_size, page_stride_bytes, block_tables,
-                        max_blocks_per_seq, seq_lens, B, q_len, H, sm_scale, num_splits, workspace, workspace_bytes,
-                        stream);
+                        max_blocks_per_seq, seq_lens, B, q_len, H, sm_scale, 0, num_splits, workspace,
+                        workspace_bytes, stream);
 }
 
 int mla_paged_combine(const void* workspace, size_t workspace_bytes, const int32_t* seq_lens, int B, int q_len,
                       int H, int num_splits, int max_blocks_per_seq, int page_size, uint16_t* o, float* lse,
                       void* stream) {
   return paged_combine(workspace, workspace_bytes, seq_lens, B, q_len, H, num_splits, max_blocks_per_seq, page_size,
-                       o, lse, stream);
+                       nullptr, o, lse, stream);
 }
 
 int mla_paged_decode(const uint16_t* q, const uint16_t* qpe, const void* kv_cache, int fmt, float kv_scale,
@@ -292,14 +298,25 @@ int mla_paged_decode(const uint16_t* q, const uint16_t* qpe, const void* kv_cach
                      int max_blocks_per_seq, const int32_t* seq_lens, int B, int q_len, int H, float sm_scale,
                      int num_splits, void* workspace, size_t workspace_bytes, uint16_t* o, float* lse,
                      void* stream) {
-  // both launches are checked before either is enqueued
-  if (!o || !aligned(o, 16) || (lse && !aligned(lse, 4))) return MLA_ERR_INVALID_ARG;
+  return mla_paged_decode_ext(q, qpe, kv_cache, fmt, kv_scale, num_pages, page_size, page_stride_bytes, block_tables,
+                              max_blocks_per_seq, seq_lens, B, q_len, H, sm_scale, 0, nullptr, num_splits, workspace,
+                              workspace_bytes, o, lse, stream);
+}
+
+int mla_paged_decode_ext(const uint16_t* q, const uint16_t* qpe, const void* kv_cache, int fmt, float kv_scale,
+                         int num_pages, int page_size, int64_t page_stride_bytes, const int32_t* block_tables,
+                         int max_blocks_per_seq, const int32_t* seq_lens, int B, int q_len, int H, float sm_scale,
+                         int sliding_window, const float* sinks, int num_splits, void* workspace,
+                         size_t workspace_bytes, uint16_t* o, float* lse, void* stream) {
+  // the combine's own checks (beyond the decode's) are made before either launch is enqueued
+  if (!o || !aligned(o, 16) || (lse && !aligned(lse, 4)) || (sinks && !aligned(sinks, 4)))
+    return MLA_ERR_INVALID_ARG;
   int st = paged_partials(q, qpe, kv_cache, fmt, kv_scale, num_pages, page_size, page_stride_bytes, block_tables,
-                          max_blocks_per_seq, seq_lens, B, q_len, H, sm_scale, num_splits, workspace,
+                          max_blocks_per_seq, seq_lens, B, q_len, H, sm_scale, sliding_window, num_splits, workspace,
                           workspace_bytes, stream);
   if (st != MLA_OK) return st;
   return paged_combine(workspace, workspace_bytes, seq_lens, B, q_len, H, num_splits, max_blocks_per_seq, page_size,
-                       o, lse, stream);
+                       sinks, o, lse, stream);
 }
 
 }  // extern "C"

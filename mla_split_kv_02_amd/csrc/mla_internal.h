@@ -45,6 +45,7 @@ struct DecodeParams {
   int rows;           // q_len * H
   int row_groups;     // ceil(rows / kRowsPerGroup)
   int num_splits;     // contiguous: splits per request; paged: token-balanced ranges
+  int window;         // paged: query at position p sees tokens p - window + 1 .. p (0: all)
   float score_scale;  // sm_scale * kv_scale * log2(e)
   float v_scale;      // kv_scale (FP8) or 1
   // partial outputs: element (slot, row, d) at o_part[slot*o_slot + row*o_row + d]
@@ -69,6 +70,8 @@ struct CombineParams {
   const int32_t* seg_last;
   const int32_t* info;
   int max_len;     // paged: max_blocks * page_size (clamp for seq_lens)
+  const float* sinks;  // paged: per-head sink logits [H] (null: none)
+  int H;
 };
 
 // One cache append launch: token j's row [latent_j | rope_j] goes to flat slot slots[j].

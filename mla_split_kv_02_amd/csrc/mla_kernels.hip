@@ -895,11 +895,17 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
       }
     }
   }
-  // query i of a request sees tokens 0 .. n - q_len + i
+  // query i of a request sees tokens lo .. vis - 1: vis = n - q_len + i + 1, and lo = 0, or
+  // vis - window with a sliding window
   const int vis = max(n - p.q_len + rc / p.H + 1, 0);
+  const int lo = p.window > 0 ? max(vis - p.window, 0) : 0;
   int min_vis = vis;  // fewest tokens any row of this wavefront sees: tiles below it need no mask
+  int max_lo = lo;    // and the latest first token: tiles from it on need no mask
 #pragma unroll
-  for (int o = 1; o < 32; o <<= 1) min_vis = min(min_vis, __shfl_xor(min_vis, o));
+  for (int o = 1; o < 32; o <<= 1) {
+    min_vis = min(min_vis, __shfl_xor(min_vis, o));
+    max_lo = max(max_lo, __shfl_xor(max_lo, o));
+  }
 
   int ab[4];  // score operand offsets, a_base ^ 32x (see qk_tile)
   {
@@ -980,10 +986,14 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
 #pragma unroll
     for (int v = 0; v < 16; ++v) x[v] = s[v];
     const int tbase = (lt0 + i) * kTileTokens;
-    if (tbase + kTileTokens > min_vis) {
-      const int lim = vis - tbase - 4 * lh;  // value v (token 8 (v/4) + v%4 of the lane) visible iff < lim
+    if (tbase + kTileTokens > min_vis || tbase < max_lo) {
+      // value v (token tbase + 4 (l / 32) + 8 (v/4) + v%4 of the lane) visible iff in [flo, lim)
+      const int lim = vis - tbase - 4 * lh, flo = lo - tbase - 4 * lh;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) x[v] = (8 * (v >> 2) + (v & 3) < lim) ? x[v] : -INFINITY;
+      for (int v = 0; v < 16; ++v) {
+        const int t = 8 * (v >> 2) + (v & 3);
+        x[v] = (t < lim && t >= flo) ? x[v] : -INFINITY;
+      }
     }
     unsigned pn[8];
     float alpha;
@@ -1073,7 +1083,13 @@ void decode_paged_kernel(const DecodeParams p) {
   __shared__ int found[2];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int max_len = p.max_blocks * p.page_size;
-  auto tiles_of = [&](int b) { return (min(max(p.seq_lens[b], 0), max_len) + kTileTokens - 1) / kTileTokens; };
+  // with a window, a request's tiles start at the one holding its first visible token
+  // (query 0 at position n - q_len sees from n - q_len - window + 1)
+  auto first_tile = [&](int n) { return p.window > 0 ? max(n - p.q_len - p.window + 1, 0) / kTileTokens : 0; };
+  auto tiles_of = [&](int b) {
+    const int n = min(max(p.seq_lens[b], 0), max_len);
+    return n > 0 ? (n + kTileTokens - 1) / kTileTokens - first_tile(n) : 0;
+  };
 
   // workgroup id -> (range w, row group rg); the row groups of one range sit 8 ids
   // apart so that they land on the same XCD (ids are dealt round-robin over 8 XCDs)
@@ -1125,7 +1141,12 @@ void decode_paged_kernel(const DecodeParams p) {
     }
     const int seg_end = min(t1, base + nb);
     const int n = min(max(p.seq_lens[b], 0), max_len);
-    run_range<FMT, true>(p, lds_addr((lds_ptr)smem), b, n, rg, t - base, seg_end - base, (int64_t)w + b);
+    const int tf = first_tile(n);  // run_range counts tiles from the request's token 0
+    // these are the same in every lane (read from LDS words and tables that all lanes
+    // share); saying so keeps the page addresses in scalar registers
+    auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+    run_range<FMT, true>(p, lds_addr((lds_ptr)smem), uni(b), uni(n), rg, uni(t - base + tf), uni(seg_end - base + tf),
+                         (int64_t)w + uni(b));
     if (tid == 0 && rg == 0) {
       if (t == base) p.seg_first[b] = w;
       if (seg_end == base + nb) p.seg_last[b] = w;
@@ -1146,17 +1167,20 @@ struct PartRef {
 };
 
 // Merge ns partials of one row; part(j) returns (lse_j, pointer to O_j).
+// sink: an extra logit of the row that joins the denominator and carries no value
+// (-inf: none).
 template <class Part>
-__device__ __forceinline__ void combine_row(int ns, Part part, uint16_t* orow, float* lse_out, int lane) {
+__device__ __forceinline__ void combine_row(int ns, Part part, uint16_t* orow, float* lse_out, int lane,
+                                            float sink = -INFINITY) {
   float M = -INFINITY;
   for (int j = lane; j < ns; j += 64) M = fmaxf(M, part(j).lse);
-  M = wave_max(M);
+  M = fmaxf(wave_max(M), sink);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float LSE = -INFINITY;
   if (M != -INFINITY) {
     float den = 0.f;
     for (int j = lane; j < ns; j += 64) den += expf(part(j).lse - M);
-    den = wave_sum(den);
+    den = wave_sum(den) + (sink != -INFINITY ? expf(sink - M) : 0.f);
     LSE = M + logf(den);
     for (int j = 0; j < ns; ++j) {
       const PartRef pj = part(j);
@@ -1208,7 +1232,8 @@ __global__ __launch_bounds__(256) void combine_paged_kernel(const CombineParams 
     const int64_t slot = (int64_t)wj + b;
     return PartRef{live ? p.lse_part[slot * p.rows + r] : -INFINITY, p.o_part + (slot * p.rows + r) * kLatent};
   };
-  combine_row(w1 - w0 + 1, part, p.o + grow * kLatent, p.lse ? p.lse + grow : nullptr, lane);
+  const float sink = p.sinks ? p.sinks[r % p.H] : -INFINITY;
+  combine_row(w1 - w0 + 1, part, p.o + grow * kLatent, p.lse ? p.lse + grow : nullptr, lane, sink);
 }
 
 // ------------------------------------------------------------------------------------

@@ -228,6 +228,40 @@ def attend(qfull: np.ndarray, kv: np.ndarray, visible, sm_scale: float):
     return O, lse
 
 
+def attend_window_sink(qfull: np.ndarray, kv: np.ndarray, first, visible, sm_scale: float, sink):
+    """``attend`` with a lower bound and a sink: row r attends tokens first[r] ..
+    visible[r]-1, and sink[r] (a logit in the units of the scaled scores, -inf for none)
+    joins the softmax denominator only:
+        lse[r] = log(exp(sink[r]) + sum_t exp(s[r, t]));  O[r] = sum_t exp(s[r, t] - lse[r]) * latent[t].
+    metrale page, ``mla_paged_decode_fp8``: a ``sliding_window`` argument and per-head fp32
+    ``sinks`` (may be null).  The page does not define them; this is the reading that the
+    window bounds the visible range from below and a sink is an extra logit with no value.
+    """
+    qfull = np.asarray(qfull, dtype=np.float64)
+    kv = np.asarray(kv, dtype=np.float64)
+    R, n = qfull.shape[0], kv.shape[0]
+    first = np.broadcast_to(np.asarray(first, dtype=np.int64), (R,))
+    visible = np.broadcast_to(np.asarray(visible, dtype=np.int64), (R,))
+    sink = np.broadcast_to(np.asarray(sink, dtype=np.float64), (R,))
+    O = np.zeros((R, LATENT))
+    lse = np.full(R, -np.inf)
+    s = sm_scale * (qfull[:, :LATENT] @ kv[:, :LATENT].T + qfull[:, LATENT:] @ kv[:, LATENT:].T) if n else None
+    for r in range(R):
+        hi = int(min(max(visible[r], 0), n))
+        lo = int(min(max(first[r], 0), hi))
+        terms = [] if hi == lo else list(s[r, lo:hi])
+        if sink[r] != -np.inf:
+            terms.append(sink[r])
+        if not terms:
+            continue
+        t = np.array(terms)
+        m = t.max()
+        lse[r] = m + math.log(np.exp(t - m).sum())
+        if hi > lo:
+            O[r] = np.exp(s[r, lo:hi] - lse[r]) @ kv[lo:hi, :LATENT]
+    return O, lse
+
+
 def attend_range(qfull, kv, visible, sm_scale, start: int, stop: int):
     """Split partial: ``attend`` restricted to tokens [start, stop).  Returns the
     normalised partial output O_j and its lse_j; an empty range (or one this row cannot
@@ -322,7 +356,8 @@ def visible_counts(n: int, q_len: int) -> np.ndarray:
 
 
 def paged_decode_request(q_b, qpe_b, cache, fmt: int, kv_scale: float, page_size: int,
-                         page_stride: int, block_row, n: int, sm_scale: float, heads=None):
+                         page_stride: int, block_row, n: int, sm_scale: float, heads=None,
+                         window: int = 0, sinks=None):
     """One request of the paged op.  q_b [q_len,H,512], qpe_b [q_len,H,64] (float64
     values).  Returns O [q_len,H',512] and LSE [q_len,H'] for the chosen heads (all by
     default).
@@ -342,12 +377,20 @@ def paged_decode_request(q_b, qpe_b, cache, fmt: int, kv_scale: float, page_size
     kv = gather_request(cache, fmt, kv_scale, page_size, page_stride, block_row, n)
     vis = visible_counts(n, q_len)
     qf = _qfull(q_b[:, hs], qpe_b[:, hs]).reshape(q_len * len(hs), ROW)
-    O, LSE = attend(qf, kv, np.repeat(vis, len(hs)), sm_scale)
+    if window == 0 and sinks is None:
+        O, LSE = attend(qf, kv, np.repeat(vis, len(hs)), sm_scale)
+    else:
+        # window W > 0: query i (position n - q_len + i) sees its last W tokens
+        first = np.maximum(vis - window, 0) if window > 0 else np.zeros_like(vis)
+        sk = np.full(len(hs), -np.inf) if sinks is None else np.asarray(sinks, np.float64)[hs]
+        O, LSE = attend_window_sink(qf, kv, np.repeat(first, len(hs)), np.repeat(vis, len(hs)), sm_scale,
+                                    np.tile(sk, q_len))
     return O.reshape(q_len, len(hs), LATENT), LSE.reshape(q_len, len(hs))
 
 
 def paged_decode(q, qpe, cache, fmt: int, kv_scale: float, page_size: int, page_stride: int,
-                 block_tables, seq_lens, sm_scale: float, requests=None, heads=None):
+                 block_tables, seq_lens, sm_scale: float, requests=None, heads=None, window: int = 0,
+                 sinks=None):
     """Paged absorbed-MLA decode.  q [B,q_len,H,512], qpe [B,q_len,H,64]; cache is the
     raw page pool (uint8, num_pages * page_stride bytes); block_tables [B, max_blocks]
     int; seq_lens [B] int.  Returns O [B',q_len,H',512] and LSE [B',q_len,H'] for the
@@ -356,7 +399,7 @@ def paged_decode(q, qpe, cache, fmt: int, kv_scale: float, page_size: int, page_
     outs, lses = [], []
     for b in bs:
         o, l = paged_decode_request(q[b], qpe[b], cache, fmt, kv_scale, page_size, page_stride,
-                                    block_tables[b], int(seq_lens[b]), sm_scale, heads)
+                                    block_tables[b], int(seq_lens[b]), sm_scale, heads, window, sinks)
         outs.append(o)
         lses.append(l)
     return np.stack(outs), np.stack(lses)

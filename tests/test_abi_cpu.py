@@ -227,3 +227,27 @@ def test_kv_append_no_tokens_enqueues_nothing():
     assert _append(T=0, lat=0, rope=0, slots=0, cache=0) == mla.MLA_OK
     # kv_scale only matters for FP8
     assert _append(T=0, fmt=2, stride=64 * 324, kv_scale=0.0) == mla.MLA_OK
+
+
+def _ext(**kw):
+    a = dict(q=F, qpe=F, cache=F, fmt=1, kv_scale=1.0, num_pages=10, page_size=64, stride=64 * 576, bt=F, mb=4,
+             sl=F, B=2, q_len=1, H=128, sm=0.07, win=0, sinks=0, ns=8, ws=F, ws_bytes=1 << 30, o=F, lse=F)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return mla.lib().mla_paged_decode_ext(vp(a["q"]), vp(a["qpe"]), vp(a["cache"]), a["fmt"], a["kv_scale"],
+                                          a["num_pages"], a["page_size"], a["stride"], vp(a["bt"]), a["mb"],
+                                          vp(a["sl"]), a["B"], a["q_len"], a["H"], a["sm"], a["win"],
+                                          vp(a["sinks"]), a["ns"], vp(a["ws"]), a["ws_bytes"], vp(a["o"]),
+                                          vp(a["lse"]), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(win=-1), mla.MLA_ERR_INVALID_ARG),
+    (dict(sinks=F + 2), mla.MLA_ERR_INVALID_ARG),
+    (dict(q=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(fmt=4), mla.MLA_ERR_UNSUPPORTED),
+    (dict(ws_bytes=1000), mla.MLA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(o=F + 4), mla.MLA_ERR_INVALID_ARG),
+])
+def test_paged_decode_ext_rejects(kw, status):
+    assert _ext(**kw) == status

@@ -245,6 +245,58 @@ def test_paged_fp8_b64_h128_full_size_sampled():
 
 
 # ----------------------------------------------------------------------------------
+# sliding window and attention sinks (mla_paged_decode_ext)
+# ----------------------------------------------------------------------------------
+
+def _paged_run_ext(w, window, sinks, num_splits=None):
+    d = paged_device_inputs(w)
+    sk = None if sinks is None else torch.from_numpy(np.asarray(sinks, dtype=np.float32)).to(DEV)
+    o, lse = mla.paged_decode(d["q"], d["qpe"], d["cache"], w.fmt, d["bt"], d["sl"], w.page_size, w.page_stride,
+                              w.kv_scale, w.sm_scale, num_splits=num_splits, window=window, sinks=sk)
+    torch.cuda.synchronize()
+    return host(o), host(lse)
+
+
+@pytest.mark.parametrize("fmt", [gen.FMT_BF16, gen.FMT_FP8, gen.FMT_NVFP4, oracle.FMT_FP8_QFP8])
+@pytest.mark.parametrize("q_len", [1, 3])
+def test_paged_window_and_sinks_match_oracle(fmt, q_len):
+    say(f"paged window+sinks fmt={fmt} q_len={q_len}")
+    base_fmt = gen.FMT_FP8 if fmt == oracle.FMT_FP8_QFP8 else fmt
+    w = gen.make_paged(B=4, H=64, q_len=q_len, lo=1, hi=400, page_size=32, fmt=base_fmt, seed=170 + fmt + q_len,
+                       seq_lens=[1, 63, 290, 97], max_blocks=16, poison_tail=True)
+    w.fmt = fmt
+    q, qpe = w.q_f64()
+    sinks = (np.random.default_rng(fmt + q_len).standard_normal(w.H) * 2).astype(np.float32)
+    for window, sk in ((1, None), (2, sinks), (33, sinks), (100, None), (1000, sinks), (0, sinks)):
+        ro, rl = oracle.paged_decode(q, qpe, w.cache, w.fmt, w.kv_scale, w.page_size, w.page_stride,
+                                     w.block_tables, w.seq_lens, w.sm_scale, window=window,
+                                     sinks=None if sk is None else sk.astype(np.float64))
+        for ns in (None, 1, 7):
+            o, lse = _paged_run_ext(w, window, sk, ns)
+            assert max_err(o, ro) <= _tol_o(base_fmt), (window, ns)
+            assert max_err(lse, rl) <= TOL_LSE, (window, ns)
+
+
+def test_paged_ext_without_window_or_sinks_is_the_plain_path():
+    w = gen.make_paged(B=3, H=32, q_len=2, lo=10, hi=300, page_size=64, fmt=gen.FMT_FP8, seed=181, max_blocks=5)
+    o1, l1 = _paged_run(w)
+    d = paged_device_inputs(w)
+    call = mla.PagedCall(d["q"], d["qpe"], d["cache"], w.fmt, d["bt"], d["sl"], w.page_size, w.page_stride,
+                         w.kv_scale, w.sm_scale, window=0, sinks=None)
+    o2, l2 = call.run()
+    torch.cuda.synchronize()
+    assert np.array_equal(o1, host(o2)) and np.array_equal(l1, host(l2))
+    # window 1: every query sees its own token only, so O is that token's latent row (bf16)
+    o3, _ = _paged_run_ext(w, 1, None)
+    for b in range(w.B):
+        n = int(w.seq_lens[b])
+        kv = oracle.gather_request(w.cache, w.fmt, w.kv_scale, w.page_size, w.page_stride, w.block_tables[b], n)
+        for i in range(w.q_len):
+            pos = n - w.q_len + i
+            assert np.max(np.abs(o3[b, i] - kv[pos, :512][None, :])) <= TOL_O_QUANT
+
+
+# ----------------------------------------------------------------------------------
 # FP8 query (format 3): same FP8 pages, query rounded to E4M3, scores on FP8 MFMA
 # ----------------------------------------------------------------------------------
 

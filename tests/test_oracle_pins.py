@@ -583,3 +583,82 @@ def test_fp8_query_decode_matches_torch():
     r1, _ = oracle.paged_decode(q, qpe, w.cache, oracle.FMT_FP8, w.kv_scale, w.page_size, w.page_stride,
                                 w.block_tables, w.seq_lens, w.sm_scale)
     assert np.max(np.abs(r1 - ro)) > 1e-4
+
+
+# ----------------------------------------------------------------------------------
+# sliding window and attention sinks (the reading: the window bounds the visible range
+# from below; a sink is an extra logit in the denominator with no value)
+# ----------------------------------------------------------------------------------
+
+def _ws_workload(fmt=gen.FMT_BF16):
+    return gen.make_paged(B=3, H=16, q_len=2, lo=3, hi=150, page_size=32, fmt=fmt, seed=95, max_blocks=5)
+
+
+def test_window_and_sink_degenerate_cases_equal_plain_attention():
+    w = _ws_workload()
+    q, qpe = w.q_f64()
+    args = (q, qpe, w.cache, w.fmt, w.kv_scale, w.page_size, w.page_stride, w.block_tables, w.seq_lens, w.sm_scale)
+    ro, rl = oracle.paged_decode(*args)
+    for window, sinks in ((0, np.full(16, -np.inf)), (int(w.seq_lens.max()) + 5, None)):
+        o, l = oracle.paged_decode(*args, window=window, sinks=sinks)
+        assert np.array_equal(o, ro) and np.array_equal(l, rl)
+
+
+def test_window_of_one_is_the_query_token():
+    # W = 1: query i sees only its own position n - q_len + i: O = that latent row, LSE = its score
+    w = _ws_workload()
+    q, qpe = w.q_f64()
+    o, l = oracle.paged_decode(q, qpe, w.cache, w.fmt, w.kv_scale, w.page_size, w.page_stride, w.block_tables,
+                               w.seq_lens, w.sm_scale, window=1)
+    for b in range(w.B):
+        n = int(w.seq_lens[b])
+        kv = oracle.gather_request(w.cache, w.fmt, w.kv_scale, w.page_size, w.page_stride, w.block_tables[b], n)
+        for i in range(w.q_len):
+            pos = n - w.q_len + i
+            if pos < 0:
+                assert np.all(np.isneginf(l[b, i])) and not o[b, i].any()
+                continue
+            s = w.sm_scale * (q[b, i] @ kv[pos, :512] + qpe[b, i] @ kv[pos, 512:])
+            assert np.allclose(o[b, i], kv[pos, :512][None, :], rtol=0, atol=1e-12)
+            assert np.allclose(l[b, i], s, rtol=0, atol=1e-12)
+
+
+def test_sink_closed_form_and_empty_rows():
+    # one visible token t and sink sigma: LSE = log(e^s + e^sigma), O = e^(s - LSE) v_t;
+    # no visible token: LSE = sigma, O = 0
+    qf = np.array([[0.3] * 576])
+    kv = np.zeros((3, 576))
+    kv[1, :] = 0.01
+    s = 0.5 * 0.3 * 0.01 * 576
+    o, l = oracle.attend_window_sink(qf, kv, [1], [2], 0.5, [0.7])
+    assert np.isclose(l[0], np.log(np.exp(s) + np.exp(0.7)), rtol=0, atol=1e-14)
+    assert np.allclose(o[0], np.exp(s - l[0]) * 0.01, rtol=0, atol=1e-15)
+    o, l = oracle.attend_window_sink(qf, kv, [0], [0], 0.5, [0.7])
+    assert l[0] == 0.7 and not o.any()
+
+
+def test_window_and_sink_match_torch_float64():
+    """A banded causal mask and a sink column (zero value) through torch's float64 softmax."""
+    w = _ws_workload(gen.FMT_FP8)
+    q, qpe = w.q_f64()
+    rng = np.random.default_rng(4)
+    sinks = rng.standard_normal(16) * 2
+    for window in (1, 7, 40):
+        ro, rl = oracle.paged_decode(q, qpe, w.cache, w.fmt, w.kv_scale, w.page_size, w.page_stride,
+                                     w.block_tables, w.seq_lens, w.sm_scale, window=window, sinks=sinks)
+        for b in range(w.B):
+            n = int(w.seq_lens[b])
+            kv = torch.from_numpy(oracle.gather_request(w.cache, w.fmt, w.kv_scale, w.page_size, w.page_stride,
+                                                        w.block_tables[b], n))
+            qt = torch.from_numpy(np.concatenate([q[b], qpe[b]], -1))  # [q_len, H, 576]
+            for i in range(w.q_len):
+                pos = n - w.q_len + i
+                t = torch.arange(n)
+                band = (t <= pos) & (t > pos - window)
+                sc = (qt[i] @ kv.T) * w.sm_scale  # [H, n]
+                sc = torch.where(band[None, :], sc, torch.tensor(-np.inf, dtype=torch.float64))
+                full = torch.cat([sc, torch.from_numpy(sinks)[:, None]], 1)
+                lse = torch.logsumexp(full, -1)
+                o = torch.softmax(full, -1)[:, :n] @ kv[:, :512]
+                assert np.max(np.abs(o.numpy() - ro[b, i])) < 1e-10, (window, b, i)
+                assert np.max(np.abs(lse.numpy() - rl[b, i])) < 1e-10, (window, b, i)
