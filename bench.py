@@ -142,6 +142,54 @@ def time_fp8_query_variant(mla, torch, w, q, qpe, cache, bt, sl, G, args, flops)
                          "peak_note": "score flops at the fp8 peak, output flops at the bf16 peak"}}
 
 
+def run_contig(args, w, mla, torch, np, gen):
+    """Contiguous split-KV decode (bf16 cache, q_len 1): one step is mla_decode_splitkv
+    followed by mla_splitkv_combine, with the planner's split (fixed at 128 tokens for the
+    tiny workload, as its definition states)."""
+    dev = torch.device("cuda:0")
+    t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, qpe, kv, kpe = (t16(a) for a in (w.q, w.qpe, w.kv, w.kpe))
+    L = gen.WORKLOADS[args.workload].get("kv_len_per_split")
+    op, lp, L = mla.decode_splitkv(q, qpe, kv, kpe, w.sm_scale, L)
+    o, lse = mla.splitkv_combine(op, lp)
+    flops = 2.0 * (576 + 512) * w.H * w.B * w.S
+    kvb = 2.0 * 576 * w.B * w.S
+    nbytes = kvb + w.B * w.H * (576 * 2 + 512 * 2 + 4)
+    for _ in range(args.warmup):
+        mla.decode_splitkv(q, qpe, kv, kpe, w.sm_scale, L, o_part=op, lse_part=lp)
+        mla.splitkv_combine(op, lp, o=o, lse=lse)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record()
+        mla.decode_splitkv(q, qpe, kv, kpe, w.sm_scale, L, o_part=op, lse_part=lp)
+        ev[k][1].record()
+        mla.splitkv_combine(op, lp, o=o, lse=lse)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
+    dec = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if flops / nbytes >= ridge:
+        a = flops / (dec * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(a, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        a = nbytes / (dec * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBPS, 4), "traffic": None}
+    out = {
+        "metric": METRIC, "value": round(flops / (ms_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "B": w.B, "H": w.H, "S_kv": w.S, "q_len": 1, "kv_format": "bf16",
+                   "kv_len_per_split": L, "num_splits": int(op.shape[2]), "decode_ms": round(dec, 5),
+                   "kv_GBps": round(kvb / (ms_step * 1e-3) / 1e9, 1), "kernel_source_sha": kernel_source_hash()},
+        "roofline": roof,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,7 +225,7 @@ def main():
     log(f"[bench] generating {args.workload}")
     w = gen.make_workload(args.workload)
     if w.__class__.__name__ != "PagedInputs":
-        raise SystemExit("bench.py times the paged decode workloads")
+        return run_contig(args, w, mla, torch, np, gen)
     t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
     q, qpe = t16(w.q), t16(w.qpe)
     cache = torch.from_numpy(w.cache).to(dev)

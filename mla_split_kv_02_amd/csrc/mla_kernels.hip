@@ -140,6 +140,14 @@ __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
 
 // Values of lanes l and l ^ 32 combined with one cross-half lane swap (r[0] holds the low
 // half's value in both halves, r[1] the high half's).
+// max of three scores.  Scores are finite or -inf (masked), never NaN, so the operands need
+// no quieting; written out because the compiler cannot know that of values produced by the
+// score block and would quiet every operand first (one extra instruction each).
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -667,7 +675,8 @@ struct Softmax {
 __device__ __forceinline__ float softmax_tile(Softmax& S, float* x, float c, unsigned* pp) {
   float mt = x[0];
 #pragma unroll
-  for (int v = 1; v < 16; ++v) mt = fmaxf(mt, x[v]);
+  for (int v = 1; v < 15; v += 2) mt = max3(mt, x[v], x[v + 1]);
+  mt = max3(mt, x[15], x[15]);
   mt = pair_max(mt) * c;  // -inf stays -inf (c > 0)
   const bool need = mt > S.m_used + kTau;
   const float m_new = need ? mt : S.m_used;
@@ -722,9 +731,9 @@ struct SoftmaxPieces {
 __device__ __forceinline__ void softmax_piece(int k, Softmax& S, float* x, float c, SoftmaxPieces& w, unsigned* pp,
                                               float& alpha) {
   if (k == 0) {
-    w.mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    w.mt = max3(max3(max3(x[0], x[1], x[2]), x[3], x[4]), x[5], x[6]);
   } else if (k == 1) {
-    w.mt = fmaxf(w.mt, fmaxf(fmaxf(fmaxf(x[8], x[9]), fmaxf(x[10], x[11])), fmaxf(fmaxf(x[12], x[13]), fmaxf(x[14], x[15]))));
+    w.mt = max3(max3(max3(max3(w.mt, x[7], x[8]), x[9], x[10]), x[11], x[12]), x[13], max3(x[14], x[15], x[15]));
   } else if (k == 2) {
     w.mt = pair_max(w.mt) * c;  // -inf stays -inf (c > 0)
   } else if (k == 3) {
