@@ -23,8 +23,17 @@
 // work while the vector work runs (NVFP4 dequantises tile i+1 just before); then one
 // barrier.
 //
+// FP8 query (cache format kFmtFp8Q, the TokenSpeed page's FP8 decode): the query is
+// rounded to E4M3 once per range (72 registers), the scores run on 9 FP8 MFMA 32x32x64
+// straight from the raw FP8 tile, and the bf16 tile holds only V^T, dim-major, filled with
+// the 8-bit LDS transpose read so that each output MFMA reads its V operand at once.
+//
+// A sliding window (paged) starts each request's tiles at the one holding its first
+// visible token and masks below the window; attention sinks enter in the combine.
+//
 // Combine kernels.  One wavefront per output row merges the partials with the split-K
-// log-sum-exp reduce (TileGym page, forward: splitk_reduce).
+// log-sum-exp reduce (TileGym page, forward: splitk_reduce), plus the row's sink logit
+// when there is one.
 
 #include "mla_fp8.h"
 #include "mla_internal.h"
@@ -184,9 +193,6 @@ __device__ __forceinline__ void dma16_s(const uint8_t* base, uint32_t voff, uint
 }
 __device__ __forceinline__ void dma4_s(const uint8_t* base, uint32_t voff, uint32_t lds) {
   asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
-}
-__device__ __forceinline__ void dma16_v(const void* src, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
 
 // Wait until at most n of this wavefront's vector-memory operations are outstanding
