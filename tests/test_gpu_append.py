@@ -14,7 +14,7 @@ from gpu_util import TOL_LSE, TOL_O_BF16, TOL_O_QUANT, bf16_dev, host, i32_dev, 
 
 pytestmark = pytest.mark.gpu
 
-FORMATS = [gen.FMT_BF16, gen.FMT_FP8, gen.FMT_NVFP4]
+FORMATS = [gen.FMT_BF16, gen.FMT_FP8, gen.FMT_NVFP4, oracle.FMT_FP8_QFP8]  # format 3: FP8 pages
 
 
 def _append_gpu(cache, bits, slots, fmt, kv_scale, page_size, stride):
@@ -37,7 +37,7 @@ def _same_bytes(got, want):
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("page_size", [32, 64])
 def test_append_matches_oracle_bytes(fmt, page_size):
-    say(f"append fmt={gen.FMT_NAMES[fmt]} page={page_size}")
+    say(f"append fmt={fmt} page={page_size}")
     rng = np.random.default_rng(70 + 3 * fmt + page_size)
     num_pages = 23
     stride = page_size * oracle.page_row_bytes(fmt) + (48 if page_size == 32 else 0)
@@ -107,7 +107,7 @@ def test_append_nvfp4_ties_and_scales():
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_append_then_decode(fmt):
     # a cache written only by the append kernel, read back by the paged decode
-    say(f"append then decode fmt={gen.FMT_NAMES[fmt]}")
+    say(f"append then decode fmt={fmt}")
     rng = np.random.default_rng(80 + fmt)
     page_size, B, H = 64, 3, 16
     seq = np.array([100, 1, 200], dtype=np.int32)
@@ -125,7 +125,8 @@ def test_append_then_decode(fmt):
     bits = gen.to_bf16_bits(x)
     slots = np.concatenate([bt[b, np.arange(n) // page_size] * page_size + np.arange(n) % page_size
                             for b, n in enumerate(seq)]).astype(np.int32)
-    kv_scale = float(np.float32(np.abs(x).max()) / np.float32(448)) if fmt == gen.FMT_FP8 else 1.0
+    fp8 = fmt in (gen.FMT_FP8, oracle.FMT_FP8_QFP8)
+    kv_scale = float(np.float32(np.abs(x).max()) / np.float32(448)) if fp8 else 1.0
     c_gpu = _append_gpu(cache, bits, slots, fmt, kv_scale, page_size, stride)
     c_ref = _append_ref(cache, bits, slots, fmt, kv_scale, page_size, stride, num_pages)
     _same_bytes(c_gpu, c_ref)
@@ -137,5 +138,5 @@ def test_append_then_decode(fmt):
     qf = gen.bf16_bits_to_f32(q).astype(np.float64)
     qpf = gen.bf16_bits_to_f32(qpe).astype(np.float64)
     ro, rl = oracle.paged_decode(qf, qpf, c_ref, fmt, kv_scale, page_size, stride, bt, seq, gen.SM_SCALE_192)
-    assert max_err(host(o), ro) <= (TOL_O_BF16 if fmt == gen.FMT_BF16 else TOL_O_QUANT)
+    assert max_err(host(o), ro) <= (TOL_O_BF16 if fmt == gen.FMT_BF16 else TOL_O_QUANT)  # noqa: E501
     assert max_err(host(lse), rl) <= TOL_LSE

@@ -630,10 +630,10 @@ def test_sink_closed_form_and_empty_rows():
     kv = np.zeros((3, 576))
     kv[1, :] = 0.01
     s = 0.5 * 0.3 * 0.01 * 576
-    o, l = oracle.attend_window_sink(qf, kv, [1], [2], 0.5, [0.7])
+    o, l = oracle.mla_oracle.attend_window_sink(qf, kv, [1], [2], 0.5, [0.7])
     assert np.isclose(l[0], np.log(np.exp(s) + np.exp(0.7)), rtol=0, atol=1e-14)
     assert np.allclose(o[0], np.exp(s - l[0]) * 0.01, rtol=0, atol=1e-15)
-    o, l = oracle.attend_window_sink(qf, kv, [0], [0], 0.5, [0.7])
+    o, l = oracle.mla_oracle.attend_window_sink(qf, kv, [0], [0], 0.5, [0.7])
     assert l[0] == 0.7 and not o.any()
 
 
@@ -662,3 +662,31 @@ def test_window_and_sink_match_torch_float64():
                 o = torch.softmax(full, -1)[:, :n] @ kv[:, :512]
                 assert np.max(np.abs(o.numpy() - ro[b, i])) < 1e-10, (window, b, i)
                 assert np.max(np.abs(lse.numpy() - rl[b, i])) < 1e-10, (window, b, i)
+
+
+@pytest.mark.parametrize("kind", ["window_off_by_one", "sink_in_value", "sink_ignored"])
+def test_window_sink_pins_catch_planted_mistakes(kind, monkeypatch):
+    """Plant a plausible mistake in a copy of attend_window_sink and check that the torch
+    pin or a closed-form pin fails."""
+    good = oracle.mla_oracle.attend_window_sink
+
+    def bad(qfull, kv, first, visible, sm_scale, sink):
+        first = np.asarray(first)
+        sink = np.broadcast_to(np.asarray(sink, dtype=np.float64), (np.asarray(qfull).shape[0],))
+        if kind == "window_off_by_one":
+            return good(qfull, kv, np.maximum(first - 1, 0), visible, sm_scale, sink)
+        if kind == "sink_ignored":
+            return good(qfull, kv, first, visible, sm_scale, np.full_like(sink, -np.inf))
+        O, lse = good(qfull, kv, first, visible, sm_scale, sink)  # sink_in_value: sink row adds v = 1
+        return O + np.where(np.isfinite(sink), np.exp(sink - lse), 0.0)[:, None], lse
+
+    monkeypatch.setattr(oracle.mla_oracle, "attend_window_sink", bad)
+    failed = 0
+    for test in (test_window_and_sink_match_torch_float64, test_window_of_one_is_the_query_token,
+                 test_sink_closed_form_and_empty_rows):
+        try:
+            test()
+        except AssertionError:
+            failed += 1
+    assert failed >= 1
+
