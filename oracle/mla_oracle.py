@@ -26,7 +26,10 @@ ones this module depends on are restated at each function.
 
 Parity status: every public function here is pinned by tests under ``tests/``
 (brute force, torch's float64 SDPA, closed forms, invariances, torch's float8 decode
-and the OCP MX E2M1 value table).  None is "parity unpinned".
+and cast, the OCP MX E2M1 value table, the input recipe's separate encoders, and planted
+mistakes that the pins must catch).  That covers the cache append (``quantize_e4m3``,
+``quantize_e2m1``, ``encode_row``, ``kv_append``), the FP8-query format and the sliding
+window with sinks (``attend_window_sink``).  None is "parity unpinned".
 """
 
 from __future__ import annotations
