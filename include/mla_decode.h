@@ -100,11 +100,14 @@ int mla_device_num_cus(int device, int* num_cus);
  * Host-only integer work.  num_cus, B, S_kv >= 1. */
 int mla_plan_contig(int num_cus, int B, int S_kv, int* kv_len_per_split, int* num_splits);
 
-/* Paged split planner.  The paged op cuts the whole batch's token tiles into
- * `num_splits` equal contiguous ranges, one workgroup each, whatever the per-request
- * lengths (so no host copy of seq_lens is needed: the TokenSpeed page avoids a
- * device-to-host sync for the same reason, _init_prefill_metadata).  This returns the
- * range count that fills the device once: num_cus / ceil(q_len * H / 128), at least 1. */
+/* Paged split planner.  The paged op cuts the whole batch's 32-token tiles into
+ * `num_splits` contiguous ranges, one workgroup each, on the device from device
+ * seq_lens (so no host copy of them is needed: the TokenSpeed page avoids a
+ * device-to-host sync for the same reason, _init_prefill_metadata).  The ranges are of
+ * about equal cost, where a request costs its tiles plus a fixed overhead of 10 tiles
+ * (what starting a request in a workgroup costs: query load, pipeline fill, partial
+ * store).  This returns the range count that fills the device once:
+ * num_cus / ceil(q_len * H / 128), at least 1. */
 int mla_plan_paged(int num_cus, int B, int q_len, int H, int* num_splits);
 
 /* Bytes of workspace mla_paged_decode needs: (num_splits + B - 1) partial slots of
@@ -138,7 +141,7 @@ int mla_splitkv_combine(const float* o_part, const float* lse_part, int rows, in
 
 /* First launch of the paged decode alone: writes the split partials of every request
  * into `workspace` (same arguments and checks as mla_paged_decode, without the
- * outputs).  Range w of the num_splits equal ranges of the batch's 32-token tiles
+ * outputs).  Range w of the num_splits ranges of the batch's 32-token tiles
  * writes, for each request b it touches, the normalised partial O and its lse into
  * slot w + b of the workspace; the workspace also records, per request, the first and
  * last range that touch it.  Useful to a caller that merges partials itself, or times

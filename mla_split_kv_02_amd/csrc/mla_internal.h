@@ -54,7 +54,7 @@ struct DecodeParams {
   int64_t o_slot, o_row, l_slot, l_row;
   int32_t* seg_first;  // paged: first / last range index that covers request b
   int32_t* seg_last;
-  int32_t* info;       // paged: info[0] = total tile count of the batch
+  int32_t* info;       // paged: info[0] = total cost of the batch's ranges (tiles + per-request overhead)
 };
 
 struct CombineParams {
