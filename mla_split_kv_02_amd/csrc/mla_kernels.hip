@@ -722,6 +722,243 @@ __device__ __forceinline__ float softmax_tile(Softmax& S, float* x, float c, uns
   return alpha;
 }
 
+// Scores of tile i as in qk_tile, with the online softmax of tile i-1 (the same steps
+// as softmax_tile) spread over the MFMA chain: vector ALU work on registers the chain
+// does not touch, which issues while the matrix core is busy.  x: the raw scores of
+// tile i-1 (masked), used up (P^T is formed in x[0..7]); S: the row state; pp: P^T of
+// tile i-1 in the output product's B layout; alpha: the factor for the accumulators before
+// that tile's product.  Hazards are covered by the instruction order: a transcendental
+// result is read three or more instructions later, a cross-half swap reads registers
+// written two or more instructions earlier, and vcc is written and read only by these
+// steps.
+__device__ __forceinline__ f32x16 qk_softmax_tile(const bf16x8* q, uint32_t tile, const int* ab, float* x,
+                                                  Softmax& S, float c, unsigned* pp, float& alpha) {
+  const uint32_t b0 = tile + ab[0], b1 = tile + ab[1], b2 = tile + ab[2], b3 = tile + ab[3];
+  f32x16 s;
+  bf16x8 a0, a1, a2, a3, a4, a5, a6;
+  float t0, t1, t2;
+  asm volatile(
+      "ds_read_b128 %[a0], %[b0] offset:0\n\t"
+      "ds_read_b128 %[a1], %[b1] offset:0\n\t"
+      "ds_read_b128 %[a2], %[b2] offset:0\n\t"
+      "ds_read_b128 %[a3], %[b3] offset:0\n\t"
+      "ds_read_b128 %[a4], %[b0] offset:4096\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q0], 0\n\t"
+      "ds_read_b128 %[a5], %[b1] offset:4096\n\t"
+      "v_max3_f32 %[t0], %[x0], %[x1], %[x2]\n\t"
+      "v_max3_f32 %[t0], %[t0], %[x3], %[x4]\n\t"
+      "v_max3_f32 %[t0], %[t0], %[x5], %[x6]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q1], %[s]\n\t"
+      "ds_read_b128 %[a6], %[b2] offset:4096\n\t"
+      "v_max3_f32 %[t0], %[t0], %[x7], %[x8]\n\t"
+      "v_max3_f32 %[t0], %[t0], %[x9], %[x10]\n\t"
+      "v_max3_f32 %[t0], %[t0], %[x11], %[x12]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q2], %[s]\n\t"
+      "ds_read_b128 %[a0], %[b3] offset:4096\n\t"
+      "v_max3_f32 %[t0], %[t0], %[x13], %[x14]\n\t"
+      "v_max_f32 %[t0], %[t0], %[x15]\n\t"
+      "v_mov_b32 %[t1], %[t0]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q3], %[s]\n\t"
+      "ds_read_b128 %[a1], %[b0] offset:8192\n\t"
+      "v_permlane32_swap_b32 %[t0], %[t1]\n\t"
+      "v_max_f32 %[t0], %[t0], %[t1]\n\t"
+      "v_mul_f32 %[t0], %[c], %[t0]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q4], %[s]\n\t"
+      "ds_read_b128 %[a2], %[b1] offset:8192\n\t"
+      "v_add_f32 %[t1], 0x41000000, %[m]\n\t"
+      "v_cmp_gt_f32 vcc, %[t0], %[t1]\n\t"
+      "v_cndmask_b32 %[t1], %[m], %[t0], vcc\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q5], %[s]\n\t"
+      "ds_read_b128 %[a3], %[b2] offset:8192\n\t"
+      "v_sub_f32 %[t2], %[m], %[t1]\n\t"
+      "v_exp_f32 %[t2], %[t2]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q6], %[s]\n\t"
+      "ds_read_b128 %[a4], %[b3] offset:8192\n\t"
+      "v_cndmask_b32 %[al], 1.0, %[t2], vcc\n\t"
+      "v_cmp_eq_f32 vcc, 0xff800000, %[m]\n\t"
+      "v_cndmask_b32_e64 %[al], %[al], 1.0, vcc\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q7], %[s]\n\t"
+      "ds_read_b128 %[a5], %[b0] offset:12288\n\t"
+      "v_mul_f32 %[ls], %[ls], %[al]\n\t"
+      "v_mul_f32 %[lr], %[lr], %[al]\n\t"
+      "v_mov_b32 %[m], %[t1]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q8], %[s]\n\t"
+      "ds_read_b128 %[a6], %[b1] offset:12288\n\t"
+      "v_cmp_eq_f32 vcc, 0xff800000, %[t1]\n\t"
+      "v_cndmask_b32_e64 %[t2], -%[t1], 0, vcc\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q9], %[s]\n\t"
+      "ds_read_b128 %[a0], %[b2] offset:12288\n\t"
+      "v_fma_f32 %[x0], %[x0], %[c], %[t2]\n\t"
+      "v_exp_f32 %[x0], %[x0]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q10], %[s]\n\t"
+      "ds_read_b128 %[a1], %[b3] offset:12288\n\t"
+      "v_fma_f32 %[x1], %[x1], %[c], %[t2]\n\t"
+      "v_exp_f32 %[x1], %[x1]\n\t"
+      "v_add_f32 %[t0], 0, %[x0]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q11], %[s]\n\t"
+      "ds_read_b128 %[a2], %[b0] offset:16384\n\t"
+      "v_fma_f32 %[x2], %[x2], %[c], %[t2]\n\t"
+      "v_exp_f32 %[x2], %[x2]\n\t"
+      "v_add_f32 %[t0], %[t0], %[x1]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q12], %[s]\n\t"
+      "ds_read_b128 %[a3], %[b1] offset:16384\n\t"
+      "v_fma_f32 %[x3], %[x3], %[c], %[t2]\n\t"
+      "v_exp_f32 %[x3], %[x3]\n\t"
+      "v_add_f32 %[t0], %[t0], %[x2]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q13], %[s]\n\t"
+      "ds_read_b128 %[a4], %[b2] offset:16384\n\t"
+      "v_fma_f32 %[x4], %[x4], %[c], %[t2]\n\t"
+      "v_exp_f32 %[x4], %[x4]\n\t"
+      "v_add_f32 %[t0], %[t0], %[x3]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q14], %[s]\n\t"
+      "ds_read_b128 %[a5], %[b3] offset:16384\n\t"
+      "v_fma_f32 %[x5], %[x5], %[c], %[t2]\n\t"
+      "v_exp_f32 %[x5], %[x5]\n\t"
+      "v_add_f32 %[t0], %[t0], %[x4]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q15], %[s]\n\t"
+      "ds_read_b128 %[a6], %[b0] offset:20480\n\t"
+      "v_fma_f32 %[x6], %[x6], %[c], %[t2]\n\t"
+      "v_exp_f32 %[x6], %[x6]\n\t"
+      "v_add_f32 %[t0], %[t0], %[x5]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q16], %[s]\n\t"
+      "ds_read_b128 %[a0], %[b1] offset:20480\n\t"
+      "v_fma_f32 %[x7], %[x7], %[c], %[t2]\n\t"
+      "v_exp_f32 %[x7], %[x7]\n\t"
+      "v_add_f32 %[t0], %[t0], %[x6]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q17], %[s]\n\t"
+      "ds_read_b128 %[a1], %[b2] offset:20480\n\t"
+      "v_fma_f32 %[x8], %[x8], %[c], %[t2]\n\t"
+      "v_exp_f32 %[x8], %[x8]\n\t"
+      "v_add_f32 %[t0], %[t0], %[x7]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q18], %[s]\n\t"
+      "ds_read_b128 %[a2], %[b3] offset:20480\n\t"
+      "v_fma_f32 %[x9], %[x9], %[c], %[t2]\n\t"
+      "v_exp_f32 %[x9], %[x9]\n\t"
+      "v_add_f32 %[t0], %[t0], %[x8]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q19], %[s]\n\t"
+      "ds_read_b128 %[a3], %[b0] offset:24576\n\t"
+      "v_fma_f32 %[x10], %[x10], %[c], %[t2]\n\t"
+      "v_exp_f32 %[x10], %[x10]\n\t"
+      "v_add_f32 %[t0], %[t0], %[x9]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q20], %[s]\n\t"
+      "ds_read_b128 %[a4], %[b1] offset:24576\n\t"
+      "v_fma_f32 %[x11], %[x11], %[c], %[t2]\n\t"
+      "v_exp_f32 %[x11], %[x11]\n\t"
+      "v_add_f32 %[t0], %[t0], %[x10]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q21], %[s]\n\t"
+      "ds_read_b128 %[a5], %[b2] offset:24576\n\t"
+      "v_fma_f32 %[x12], %[x12], %[c], %[t2]\n\t"
+      "v_exp_f32 %[x12], %[x12]\n\t"
+      "v_add_f32 %[t0], %[t0], %[x11]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q22], %[s]\n\t"
+      "ds_read_b128 %[a6], %[b3] offset:24576\n\t"
+      "v_fma_f32 %[x13], %[x13], %[c], %[t2]\n\t"
+      "v_exp_f32 %[x13], %[x13]\n\t"
+      "v_add_f32 %[t0], %[t0], %[x12]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q23], %[s]\n\t"
+      "ds_read_b128 %[a0], %[b0] offset:28672\n\t"
+      "v_fma_f32 %[x14], %[x14], %[c], %[t2]\n\t"
+      "v_exp_f32 %[x14], %[x14]\n\t"
+      "v_add_f32 %[t0], %[t0], %[x13]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q24], %[s]\n\t"
+      "ds_read_b128 %[a1], %[b1] offset:28672\n\t"
+      "v_fma_f32 %[x15], %[x15], %[c], %[t2]\n\t"
+      "v_exp_f32 %[x15], %[x15]\n\t"
+      "v_add_f32 %[t0], %[t0], %[x14]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q25], %[s]\n\t"
+      "ds_read_b128 %[a2], %[b2] offset:28672\n\t"
+      "v_add_f32 %[t0], %[t0], %[x15]\n\t"
+      "v_add_f32 %[ls], %[ls], %[t0]\n\t"
+      "v_cvt_pk_bf16_f32 %[x0], %[x0], %[x1]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q26], %[s]\n\t"
+      "ds_read_b128 %[a3], %[b3] offset:28672\n\t"
+      "v_dot2c_f32_bf16 %[lr], 0x3f803f80, %[x0]\n\t"
+      "v_cvt_pk_bf16_f32 %[x1], %[x2], %[x3]\n\t"
+      "v_dot2c_f32_bf16 %[lr], 0x3f803f80, %[x1]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q27], %[s]\n\t"
+      "ds_read_b128 %[a4], %[b0] offset:32768\n\t"
+      "v_cvt_pk_bf16_f32 %[x2], %[x4], %[x5]\n\t"
+      "v_dot2c_f32_bf16 %[lr], 0x3f803f80, %[x2]\n\t"
+      "v_cvt_pk_bf16_f32 %[x3], %[x6], %[x7]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q28], %[s]\n\t"
+      "ds_read_b128 %[a5], %[b1] offset:32768\n\t"
+      "v_dot2c_f32_bf16 %[lr], 0x3f803f80, %[x3]\n\t"
+      "v_cvt_pk_bf16_f32 %[x4], %[x8], %[x9]\n\t"
+      "v_dot2c_f32_bf16 %[lr], 0x3f803f80, %[x4]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q29], %[s]\n\t"
+      "ds_read_b128 %[a6], %[b2] offset:32768\n\t"
+      "v_cvt_pk_bf16_f32 %[x5], %[x10], %[x11]\n\t"
+      "v_dot2c_f32_bf16 %[lr], 0x3f803f80, %[x5]\n\t"
+      "v_cvt_pk_bf16_f32 %[x6], %[x12], %[x13]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q30], %[s]\n\t"
+      "ds_read_b128 %[a0], %[b3] offset:32768\n\t"
+      "v_dot2c_f32_bf16 %[lr], 0x3f803f80, %[x6]\n\t"
+      "v_cvt_pk_bf16_f32 %[x7], %[x14], %[x15]\n\t"
+      "v_dot2c_f32_bf16 %[lr], 0x3f803f80, %[x7]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q31], %[s]\n\t"
+      "v_permlane32_swap_b32 %[x0], %[x2]\n\t"
+      "v_permlane32_swap_b32 %[x1], %[x3]\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q32], %[s]\n\t"
+      "v_permlane32_swap_b32 %[x4], %[x6]\n\t"
+      "v_permlane32_swap_b32 %[x5], %[x7]\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q33], %[s]\n\t"
+      "s_waitcnt lgkmcnt(1)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q34], %[s]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q35], %[s]\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : [s] "=&v"(s), [a0] "=&v"(a0), [a1] "=&v"(a1), [a2] "=&v"(a2), [a3] "=&v"(a3), [a4] "=&v"(a4), [a5] "=&v"(a5),
+        [a6] "=&v"(a6), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [al] "=&v"(alpha), [x0] "+v"(x[0]), [x1] "+v"(x[1]), [x2] "+v"(x[2]),
+        [x3] "+v"(x[3]), [x4] "+v"(x[4]), [x5] "+v"(x[5]), [x6] "+v"(x[6]), [x7] "+v"(x[7]), [x8] "+v"(x[8]),
+        [x9] "+v"(x[9]), [x10] "+v"(x[10]), [x11] "+v"(x[11]), [x12] "+v"(x[12]), [x13] "+v"(x[13]),
+        [x14] "+v"(x[14]), [x15] "+v"(x[15]), [m] "+v"(S.m_used), [ls] "+v"(S.l_sum), [lr] "+v"(S.l_rnd)
+      : [b0] "v"(b0), [b1] "v"(b1), [b2] "v"(b2), [b3] "v"(b3), [c] "v"(c),
+        [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]), [q5] "v"(q[5]),
+        [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8]), [q9] "v"(q[9]), [q10] "v"(q[10]), [q11] "v"(q[11]),
+        [q12] "v"(q[12]), [q13] "v"(q[13]), [q14] "v"(q[14]), [q15] "v"(q[15]), [q16] "v"(q[16]), [q17] "v"(q[17]),
+        [q18] "v"(q[18]), [q19] "v"(q[19]), [q20] "v"(q[20]), [q21] "v"(q[21]), [q22] "v"(q[22]), [q23] "v"(q[23]),
+        [q24] "v"(q[24]), [q25] "v"(q[25]), [q26] "v"(q[26]), [q27] "v"(q[27]), [q28] "v"(q[28]), [q29] "v"(q[29]),
+        [q30] "v"(q[30]), [q31] "v"(q[31]), [q32] "v"(q[32]), [q33] "v"(q[33]), [q34] "v"(q[34]), [q35] "v"(q[35])
+      : "vcc", "memory");
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pp[j] = __float_as_uint(x[j]);  // P^T went into x[0..7]
+  return s;
+}
+
 // The output phase of a tile as 32 steps, one output MFMA each, fenced by scheduling
 // barriers so that the work between the MFMAs stays spread out: the transpose reads
 // run four MFMAs ahead (the LDS read latency is about four MFMA issue intervals), and
@@ -803,6 +1040,7 @@ __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const un
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   constexpr bool kDq = (FMT == kFmtFp8);
+  constexpr bool kSmHere = (FMT == kFmtFp8Q);  // other formats: the softmax runs in the score block
   const int r = tid >> 3, t7 = tid & 7;
   const uint32_t rd = st + fp8_dq_read_offset<false>(tid);  // FP8 dequantisation (see dequant_fp8)
   const uint32_t wr = dtile + 128 * r + ((t7 ^ swz(r)) << 4);
@@ -828,7 +1066,7 @@ __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const un
   for (int k = 0; k < 2 * kDimBlocks; ++k) {
     o[k & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k], (k < kDimBlocks) ? pb0 : pb1, o[k & 15], 0, 0, 0);
     if (k + kAhead < 2 * kDimBlocks) va[k + kAhead] = tr(k + kAhead);
-    softmax_piece(k, S, x, c, w, pn, alpha);
+    if constexpr (kSmHere) softmax_piece(k, S, x, c, w, pn, alpha);
     if constexpr (FMT == kFmtFp8Q) {
       if ((k & 1) == 0 && k / 2 < 8) {
         const int m = k / 2;
@@ -985,6 +1223,10 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
     else if (FMT == kFmtNvfp4) dequant_nvfp4(raw_buf(i), tile_buf(i), tid);
   };
 
+  // Scores of the latest tile (masked); except with the FP8 query, their softmax runs
+  // in the next tile's score block, so they stay in registers until then.
+  float x[16];
+
   // one tile; FIRST: there is no previous tile to multiply
   auto body = [&](int i, auto FIRST) {
     constexpr bool first = decltype(FIRST)::value;
@@ -993,11 +1235,18 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
       issue(i + PP::kAhead, e_next);
       e_next = entry(i + PP::kAhead + 1);
     }
-    if (!first && __any(alpha_prev != 1.f)) rescale(o, alpha_prev);
     f32x16 s;
-    if constexpr (kQ8) s = qk_tile_f8(q8, raw_buf(i), fq);  // the raw tile itself
-    else s = qk_tile(q, tile_buf(i), ab);
-    float x[16];
+    if constexpr (kQ8) {
+      if (!first && __any(alpha_prev != 1.f)) rescale(o, alpha_prev);
+      s = qk_tile_f8(q8, raw_buf(i), fq);  // the raw tile itself
+    } else if (first) {
+      s = qk_tile(q, tile_buf(i), ab);
+    } else {
+      // scores of tile i, softmax of tile i-1 (x) -> P^T in pp and its factor
+      float alpha;
+      s = qk_softmax_tile(q, tile_buf(i), ab, x, S, c, pp, alpha);
+      if (__any(alpha != 1.f)) rescale(o, alpha);
+    }
 #pragma unroll
     for (int v = 0; v < 16; ++v) x[v] = s[v];
     const int tbase = (lt0 + i) * kTileTokens;
@@ -1011,19 +1260,21 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
       }
     }
     unsigned pn[8];
-    float alpha;
+    float alpha = 1.f;
     // past the last tile the dequantisation only rewrites an unused buffer
     if (first || FMT == kFmtNvfp4) {
       if (FMT != kFmtBf16) dequant(i + 1);
     }
     if (first) {
-      alpha = softmax_tile(S, x, c, pn);
+      if constexpr (kQ8) alpha = softmax_tile(S, x, c, pn);
     } else {
       output_phase<FMT>(o, tile_buf(i - 1), pp, vb, x, S, c, pn, alpha, raw_buf(i + 1), tile_buf(i + 1), tid);
     }
+    if constexpr (kQ8) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) pp[k] = pn[k];
-    alpha_prev = alpha;
+      for (int k = 0; k < 8; ++k) pp[k] = pn[k];
+      alpha_prev = alpha;
+    }
     // the loads the next tile depends on: bf16 tile i+1 (issued one tile ago), raw tile
     // i+2 (issued now for FP8, one tile ago for NVFP4)
     if (FMT == kFmtFp8 || FMT == kFmtFp8Q) wait_vmcnt(0);
@@ -1044,9 +1295,14 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
     }
     body(0, std::true_type{});
     for (int i = 1; i < nt; ++i) body(i, std::false_type{});
-    if (__any(alpha_prev != 1.f)) rescale(o, alpha_prev);
-    if constexpr (FMT == kFmtFp8Q) pv_tile_vt(o, tile_buf(nt - 1), pp, vb);
-    else pv_tile(o, tile_buf(nt - 1), pp, vb);
+    if constexpr (kQ8) {
+      if (__any(alpha_prev != 1.f)) rescale(o, alpha_prev);
+      pv_tile_vt(o, tile_buf(nt - 1), pp, vb);
+    } else {
+      const float alpha = softmax_tile(S, x, c, pp);  // the last tile's softmax
+      if (__any(alpha != 1.f)) rescale(o, alpha);
+      pv_tile(o, tile_buf(nt - 1), pp, vb);
+    }
   }
 
   // ---- epilogue: normalised partial O and its lse ----
