@@ -667,6 +667,14 @@ __device__ __forceinline__ void rescale(f32x16* o, float alpha) {
     }
 }
 
+// e * f for an accumulator e, read from its accumulation register into a vector
+// register without writing it back (the compiler would otherwise stage all of them).
+__device__ __forceinline__ float scaled(float e, float f) {
+  float t;
+  asm volatile("v_accvgpr_read_b32 %0, %1\n\tv_mul_f32 %0, %0, %2" : "=&v"(t) : "a"(e), "v"(f));
+  return t;
+}
+
 struct Softmax {
   float m_used;  // reference max of the row (log2 domain), equal in lanes l and l ^ 32
   float l_sum;   // this lane's share of sum p (unrounded): for the LSE
@@ -1313,14 +1321,15 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
     const int row = row0 + my_row;
     if (lh == 0)
       p.lse_part[slot * p.l_slot + (int64_t)row * p.l_row] = ok ? (S.m_used + __log2f(l_tot)) * kLn2 : -INFINITY;
-    rescale(o, ok ? p.v_scale / l_rnd : 0.f);  // normalise in place
+    const float f = ok ? p.v_scale / l_rnd : 0.f;  // normalisation, applied on the way out
     float* orow = p.o_part + slot * p.o_slot + (int64_t)row * p.o_row + 4 * lh;
 #pragma unroll
     for (int db = 0; db < kDimBlocks; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
         *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * q4) =
-            f32x4{o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]};
+            f32x4{scaled(o[db][4 * q4], f), scaled(o[db][4 * q4 + 1], f), scaled(o[db][4 * q4 + 2], f),
+                  scaled(o[db][4 * q4 + 3], f)};
   }
   __syncthreads();  // the next range reuses the LDS buffers
 }
