@@ -1048,7 +1048,7 @@ __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const un
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   constexpr bool kDq = (FMT == kFmtFp8);
-  constexpr bool kSmHere = (FMT == kFmtFp8Q);  // other formats: the softmax runs in the score block
+  constexpr bool kSmHere = (FMT == kFmtFp8Q || FMT == kFmtBf16);  // else in the next score block
   const int r = tid >> 3, t7 = tid & 7;
   const uint32_t rd = st + fp8_dq_read_offset<false>(tid);  // FP8 dequantisation (see dequant_fp8)
   const uint32_t wr = dtile + 128 * r + ((t7 ^ swz(r)) << 4);
@@ -1124,6 +1124,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
   // of dims 64k + 32 (l / 32) .. + 32, byte j of the operand holding dim 64k + 32 (l / 32)
   // + j (TokenSpeed page, forward_decode: the query is cast to the FP8 cache type).
   constexpr bool kQ8 = (FMT == kFmtFp8Q);
+  constexpr bool kSmQk = (FMT == kFmtFp8 || FMT == kFmtNvfp4);
   bf16x8 q[kQ8 ? 1 : kKSteps];
   i32x8 q8[kQ8 ? 9 : 1];
   {
@@ -1231,22 +1232,28 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
     else if (FMT == kFmtNvfp4) dequant_nvfp4(raw_buf(i), tile_buf(i), tid);
   };
 
-  // Scores of the latest tile (masked); except with the FP8 query, their softmax runs
-  // in the next tile's score block, so they stay in registers until then.
-  float x[16];
+  // Scores of the latest tile (masked).  FP8 and NVFP4 caches (kSmQk): their softmax runs
+  // in the next tile's score block, so they stay in registers until then.  bf16 cache and
+  // FP8 query: the softmax runs in pieces between the output MFMAs of the same iteration
+  // (with a bf16 cache, measured faster so: its score block already carries the tile loads'
+  // LDS writes).
+  float x_keep[kSmQk ? 16 : 1];
 
   // one tile; FIRST: there is no previous tile to multiply
   auto body = [&](int i, auto FIRST) {
     constexpr bool first = decltype(FIRST)::value;
+    float x_loc[kSmQk ? 1 : 16];
+    float* x = kSmQk ? x_keep : x_loc;
     const bool more = i + PP::kAhead < nt;
     if (more) {
       issue(i + PP::kAhead, e_next);
       e_next = entry(i + PP::kAhead + 1);
     }
     f32x16 s;
-    if constexpr (kQ8) {
+    if constexpr (!kSmQk) {
       if (!first && __any(alpha_prev != 1.f)) rescale(o, alpha_prev);
-      s = qk_tile_f8(q8, raw_buf(i), fq);  // the raw tile itself
+      if constexpr (kQ8) s = qk_tile_f8(q8, raw_buf(i), fq);  // the raw tile itself
+      else s = qk_tile(q, tile_buf(i), ab);
     } else if (first) {
       s = qk_tile(q, tile_buf(i), ab);
     } else {
@@ -1274,11 +1281,11 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
       if (FMT != kFmtBf16) dequant(i + 1);
     }
     if (first) {
-      if constexpr (kQ8) alpha = softmax_tile(S, x, c, pn);
+      if constexpr (!kSmQk) alpha = softmax_tile(S, x, c, pn);
     } else {
       output_phase<FMT>(o, tile_buf(i - 1), pp, vb, x, S, c, pn, alpha, raw_buf(i + 1), tile_buf(i + 1), tid);
     }
-    if constexpr (kQ8) {
+    if constexpr (!kSmQk) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) pp[k] = pn[k];
       alpha_prev = alpha;
@@ -1303,11 +1310,12 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
     }
     body(0, std::true_type{});
     for (int i = 1; i < nt; ++i) body(i, std::false_type{});
-    if constexpr (kQ8) {
+    if constexpr (!kSmQk) {
       if (__any(alpha_prev != 1.f)) rescale(o, alpha_prev);
-      pv_tile_vt(o, tile_buf(nt - 1), pp, vb);
+      if constexpr (kQ8) pv_tile_vt(o, tile_buf(nt - 1), pp, vb);
+      else pv_tile(o, tile_buf(nt - 1), pp, vb);
     } else {
-      const float alpha = softmax_tile(S, x, c, pp);  // the last tile's softmax
+      const float alpha = softmax_tile(S, x_keep, c, pp);  // the last tile's softmax
       if (__any(alpha != 1.f)) rescale(o, alpha);
       pv_tile(o, tile_buf(nt - 1), pp, vb);
     }
@@ -1323,13 +1331,20 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
       p.lse_part[slot * p.l_slot + (int64_t)row * p.l_row] = ok ? (S.m_used + __log2f(l_tot)) * kLn2 : -INFINITY;
     const float f = ok ? p.v_scale / l_rnd : 0.f;  // normalisation, applied on the way out
     float* orow = p.o_part + slot * p.o_slot + (int64_t)row * p.o_row + 4 * lh;
+    // four dim blocks at a time: 64 values scaled into vector registers, then 16 stores
+    // issued back to back
 #pragma unroll
-    for (int db = 0; db < kDimBlocks; ++db)
+    for (int g = 0; g < kDimBlocks; g += 4) {
+      f32x4 t[16];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * q4) =
-            f32x4{scaled(o[db][4 * q4], f), scaled(o[db][4 * q4 + 1], f), scaled(o[db][4 * q4 + 2], f),
-                  scaled(o[db][4 * q4 + 3], f)};
+      for (int j = 0; j < 16; ++j) {
+        const int db = g + j / 4, q4 = j % 4;
+        t[j] = f32x4{scaled(o[db][4 * q4], f), scaled(o[db][4 * q4 + 1], f), scaled(o[db][4 * q4 + 2], f),
+                     scaled(o[db][4 * q4 + 3], f)};
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) *reinterpret_cast<f32x4*>(orow + 32 * (g + j / 4) + 8 * (j % 4)) = t[j];
+    }
   }
   __syncthreads();  // the next range reuses the LDS buffers
 }
