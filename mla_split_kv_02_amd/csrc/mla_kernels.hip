@@ -1048,7 +1048,7 @@ __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const un
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   constexpr bool kDq = (FMT == kFmtFp8);
-  constexpr bool kSmHere = (FMT == kFmtFp8Q || FMT == kFmtBf16);  // else in the next score block
+  constexpr bool kSmHere = (FMT == kFmtFp8Q);  // other formats: the softmax runs in the score block
   const int r = tid >> 3, t7 = tid & 7;
   const uint32_t rd = st + fp8_dq_read_offset<false>(tid);  // FP8 dequantisation (see dequant_fp8)
   const uint32_t wr = dtile + 128 * r + ((t7 ^ swz(r)) << 4);
@@ -1124,7 +1124,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
   // of dims 64k + 32 (l / 32) .. + 32, byte j of the operand holding dim 64k + 32 (l / 32)
   // + j (TokenSpeed page, forward_decode: the query is cast to the FP8 cache type).
   constexpr bool kQ8 = (FMT == kFmtFp8Q);
-  constexpr bool kSmQk = (FMT == kFmtFp8 || FMT == kFmtNvfp4);
+  constexpr bool kSmQk = !kQ8;
   bf16x8 q[kQ8 ? 1 : kKSteps];
   i32x8 q8[kQ8 ? 9 : 1];
   {
@@ -1232,11 +1232,10 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
     else if (FMT == kFmtNvfp4) dequant_nvfp4(raw_buf(i), tile_buf(i), tid);
   };
 
-  // Scores of the latest tile (masked).  FP8 and NVFP4 caches (kSmQk): their softmax runs
-  // in the next tile's score block, so they stay in registers until then.  bf16 cache and
-  // FP8 query: the softmax runs in pieces between the output MFMAs of the same iteration
-  // (with a bf16 cache, measured faster so: its score block already carries the tile loads'
-  // LDS writes).
+  // Scores of the latest tile (masked).  Except with the FP8 query, their softmax runs in
+  // the next tile's score block (kSmQk), so they stay in registers until then.  With the
+  // FP8 query it runs in pieces between the output MFMAs of the same iteration: its score
+  // block has only nine (FP8) MFMAs to hide it under, and measured slower so.
   float x_keep[kSmQk ? 16 : 1];
 
   // one tile; FIRST: there is no previous tile to multiply
