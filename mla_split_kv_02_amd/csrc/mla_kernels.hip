@@ -18,15 +18,21 @@
 // one workgroup barrier per tile hands them over.
 //
 // Per tile i: the global->LDS loads of a later tile are issued first; then the scores of
-// tile i; then the softmax of tile i, with the output product of tile i-1 and (FP8) the
-// dequantisation of tile i+1 in the same instruction stream, so the matrix cores have
-// work while the vector work runs (NVFP4 dequantises tile i+1 just before); then one
-// barrier.
+// tile i, with the softmax of tile i-1 (whose scores stayed in registers) spread between
+// the score MFMAs, so the vector work issues while the matrix core is busy; then the
+// output product of tile i-1, with (FP8) the dequantisation of tile i+1 in the same
+// instruction stream (NVFP4 dequantises tile i+1 just before); then one barrier.  The
+// first tile's softmax and the last tile's output product come after the loop.
+//
+// Paged ranges are balanced by cost: a request costs its tiles plus a fixed overhead for
+// its segment's query load, pipeline fill and partial store (decode_paged_kernel).
 //
 // FP8 query (cache format kFmtFp8Q, the TokenSpeed page's FP8 decode): the query is
 // rounded to E4M3 once per range (72 registers), the scores run on 9 FP8 MFMA 32x32x64
 // straight from the raw FP8 tile, and the bf16 tile holds only V^T, dim-major, filled with
-// the 8-bit LDS transpose read so that each output MFMA reads its V operand at once.
+// the 8-bit LDS transpose read so that each output MFMA reads its V operand at once.  Its
+// softmax runs between the output MFMAs of the same iteration instead (nine FP8 MFMAs
+// hide less of it).
 //
 // A sliding window (paged) starts each request's tiles at the one holding its first
 // visible token and masks below the window; attention sinks enter in the combine.
