@@ -287,11 +287,12 @@ __device__ __forceinline__ void load_fp8_raw(const Src& S, int tb, const uint8_t
   const int tok = min(tb + r, S.n - 1);
   const int c4 = SWZ ? ((lane & 3) ^ fswz(r)) : (lane & 3);
   const uint32_t voff = (uint32_t)((rip + tok - tb) * kRow + 16 * (4 * (wave >> 1) + c4));
+  // 18 instructions: four from every wavefront, a fifth from wavefronts 0 and 1 (a
+  // wavefront-uniform branch, so the condition stays in scalar registers)
+  static_assert(kFp8Loads > 16 && kFp8Loads <= 20, "four or five loads per wavefront");
 #pragma unroll
-  for (int m = 0; m < 5; ++m) {
-    if (4 * m + wave >= kFp8Loads) break;
-    dma16_s(pg + 128 * m, voff, st + 1024 * (4 * m + wave));
-  }
+  for (int m = 0; m < 4; ++m) dma16_s(pg + 128 * m, voff, st + 1024 * (4 * m + wave));
+  if (wave < kFp8Loads - 16) dma16_s(pg + 512, voff, st + 1024 * (16 + wave));
 }
 
 // NVFP4 rows, raw.  Data: chunk c (32 codes) of row r at 1024 (c / 2) + 32 r + 16 (c % 2);
