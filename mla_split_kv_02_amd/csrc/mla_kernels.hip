@@ -307,19 +307,19 @@ __device__ __forceinline__ void load_nvfp4_raw(const Src& S, int tb, const uint8
   const int tok = min(tb + r, S.n - 1);
   const int prow = rip + tok - tb;
   const uint32_t dvoff = (uint32_t)(prow * kNvDataBytes + 16 * (lane & 1));
+  auto scales = [&](int sidx) {  // scale instruction sidx (0..4)
+    const int q = min(2 * sidx + (lane & 1), kNvScaleBytes / 4 - 1);
+    dma4_s(pg, (uint32_t)(p.page_size * kNvDataBytes + prow * kNvScaleBytes + 4 * q), st + kNvRawData + 256 * sidx);
+  };
+  // instruction j = 4m + wave as above, with wavefront-uniform branches (so the conditions
+  // stay in scalar registers): m = 0, 1 data; m = 2 data 8 (wavefront 0) or scales 0..2;
+  // m = 3 scales 3, 4 (wavefronts 0, 1)
+  static_assert(kNvDataLoads == 9 && kNvScaleLoads == 5, "load split below");
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int j = 4 * m + wave;
-    if (j >= kNvDataLoads + kNvScaleLoads) break;
-    if (j < kNvDataLoads) {
-      dma16_s(pg + 32 * j, dvoff, st + 1024 * j);
-    } else {
-      const int sidx = j - kNvDataLoads;
-      const int q = min(2 * sidx + (lane & 1), kNvScaleBytes / 4 - 1);
-      dma4_s(pg, (uint32_t)(p.page_size * kNvDataBytes + prow * kNvScaleBytes + 4 * q),
-             st + kNvRawData + 256 * sidx);
-    }
-  }
+  for (int m = 0; m < 2; ++m) dma16_s(pg + 32 * (4 * m + wave), dvoff, st + 1024 * (4 * m + wave));
+  if (wave == 0) dma16_s(pg + 32 * 8, dvoff, st + 1024 * 8);
+  else scales(wave - 1);
+  if (wave < 2) scales(3 + wave);
 }
 
 // Raw FP8 staging -> bf16 tile.  Thread t writes chunk t % 8 of group m (m < NG) of
