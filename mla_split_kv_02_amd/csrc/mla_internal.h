@@ -18,7 +18,7 @@ constexpr int kWaveRows = 32;      // query rows one wavefront owns
 constexpr int kRowsPerGroup = kWaveRows * kWaves;  // query rows (query x head) per workgroup: 128
 
 constexpr int kFmtBf16 = 0;
-constexpr int kFmtFp8 = 1;
+constexpr int kFmtFp8 = 1;   // FP8 cache: query and softmax weights split into two E4M3 operands each
 constexpr int kFmtNvfp4 = 2;
 constexpr int kFmtFp8Q = 3;  // FP8 cache, query rounded to E4M3, score product on FP8 MFMA
 

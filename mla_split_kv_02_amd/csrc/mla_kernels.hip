@@ -17,12 +17,22 @@
 // re-reads it once per group of 16 heads).  The tile buffers are the only shared state:
 // one workgroup barrier per tile hands them over.
 //
-// Per tile i: the global->LDS loads of a later tile are issued first; then the scores of
-// tile i, with the softmax of tile i-1 (whose scores stayed in registers) spread between
-// the score MFMAs, so the vector work issues while the matrix core is busy; then the
-// output product of tile i-1, with (FP8) the dequantisation of tile i+1 in the same
-// instruction stream (NVFP4 dequantises tile i+1 just before); then one barrier.  The
-// first tile's softmax and the last tile's output product come after the loop.
+// Per tile i (bf16, NVFP4): the global->LDS loads of a later tile are issued first; then
+// the scores of tile i, with the softmax of tile i-1 (whose scores stayed in registers)
+// spread between the score MFMAs, so the vector work issues while the matrix core is
+// busy; then the output product of tile i-1 (NVFP4 dequantises tile i+1 just before);
+// then one barrier.  The first tile's softmax and the last tile's output product come
+// after the loop.
+//
+// FP8 cache (run_range_split): no tile is converted to bf16.  The bf16 query of each row
+// is split exactly into two E4M3 operands (hi + lo, after a power-of-two row scale), so
+// the scores run on FP8 MFMA 32x32x64 straight from the raw tile, each K operand read
+// once for both halves (18 MFMAs per tile).  The softmax weights are split the same way
+// (about 8 significant bits, like bf16), and the output product takes the raw tile's V^T
+// through the 8-bit LDS transpose read: one MFMA 32x32x64 per 32 dims whose K = 64 holds
+// the tile's 32 tokens twice, with P_hi in the low lane half and P_lo in the high half
+// (16 MFMAs per tile).  The matrix-core time per token is that of the bf16 path; the LDS
+// traffic per tile drops from about 290 to 200 KiB and the dequantisation pass is gone.
 //
 // Paged ranges are balanced by cost: a request costs its tiles plus a fixed overhead for
 // its segment's query load, pipeline fill and partial store (decode_paged_kernel).
@@ -85,13 +95,10 @@ constexpr float kLn2 = 0.69314718055994531f;
 // iteration i the loads of tile i + kAhead are issued.  With the FP8 query the scores
 // read the raw FP8 tile itself, so it stays until its own iteration (three staging
 // buffers) and the bf16 tile holds only the 512 latent dims the output product needs.
+// The FP8 cache's split path has no bf16 tiles at all.
 template <int FMT> struct Pipe;
 template <> struct Pipe<kFmtBf16> {
   static constexpr int kTiles = 4, kStride = kTileBytes, kRaw = 0, kRawBytes = 0, kAhead = 2, kLoads = kBf16Loads;
-};
-template <> struct Pipe<kFmtFp8> {
-  static constexpr int kTiles = 3, kStride = kTileBytes, kRaw = 2, kRawBytes = kFp8RawBytes, kAhead = 2,
-                       kLoads = kFp8Loads;
 };
 template <> struct Pipe<kFmtNvfp4> {
   static constexpr int kTiles = 3, kStride = kTileBytes, kRaw = 3, kRawBytes = kNvRawBytes, kAhead = 3,
@@ -100,6 +107,12 @@ template <> struct Pipe<kFmtNvfp4> {
 template <> struct Pipe<kFmtFp8Q> {
   static constexpr int kTiles = 3, kStride = 8 * kGroupBytes, kRaw = 3, kRawBytes = kFp8RawBytes, kAhead = 2,
                        kLoads = kFp8Loads;
+};
+// FP8 cache (split path): raw tiles only (no bf16 copy); a tile is read by its score
+// block and by the next iteration's output product, and the loads run four tiles ahead:
+// six buffers.
+template <> struct Pipe<kFmtFp8> {
+  static constexpr int kTiles = 0, kStride = 0, kRaw = 6, kRawBytes = kFp8RawBytes, kAhead = 4, kLoads = kFp8Loads;
 };
 template <int FMT> constexpr int smem_bytes() {
   return Pipe<FMT>::kTiles * Pipe<FMT>::kStride + Pipe<FMT>::kRaw * Pipe<FMT>::kRawBytes;
@@ -273,19 +286,28 @@ __device__ __forceinline__ void load_bf16_tile(const Src& S, int tb, const uint8
 }
 
 // FP8 rows, raw.  Staging layout: chunk c (16 codes) of row r at 2048 (c / 4) + 64 r +
-// 16 p, p = (c % 4) ^ fswz(r) when SWZ, else c % 4.  Instruction j = 4m + w covers chunk
+// 16 p, p = (c % 4) ^ f(r) with f = fswz (SW = 1), sswz (SW = 2) or 0.  Instruction j = 4m + w covers chunk
 // group j / 2 of rows 16 (j % 2) ..: lane l takes row 16 (w % 2) + l / 4 and the chunk
 // 4 (w / 2 + 2m) + c % 4 that belongs at position l % 4.  The swizzle serves the FP8
 // score reads (two 16-byte chunks of one row per lane and step): any 16 consecutive rows
 // at one logical chunk hit 16 different 16-byte bank slots, and so do 32 rows mod 32.
 __device__ __forceinline__ int fswz(int r) { return ((r >> 2) ^ (r >> 4)) & 3; }
+// The FP8 split path's swizzle: row bit 2 flips position bit 1 and row bit 3 position
+// bit 0 (fswz has them the other way round).  Its score reads stay conflict-free (rows
+// r, r+4, r+8, r+12 take four different positions), and so do its 8-bit transpose reads,
+// where one half-wavefront reads two adjacent chunks (lane groups g = 0, 1) of rows
+// 8t .. 8t+7: rows u and u+4 share a bank row (256 bytes apart), and their positions
+// differ in bit 1 while the two chunks differ in bit 0, so the four (row, chunk) pairs of
+// a bank row take four different positions.
+__device__ __forceinline__ int sswz(int r) { return (((r >> 1) & 2) | ((r >> 3) & 1)) ^ ((r >> 4) & 1); }
 
-template <bool SWZ>
+// SW: 0 no swizzle, 1 fswz, 2 sswz
+template <int SW>
 __device__ __forceinline__ void load_fp8_raw(const Src& S, int tb, const uint8_t* pg, uint32_t st, int wave, int lane) {
   const int rip = tb & (S.p->page_size - 1);
   const int r = 16 * (wave & 1) + (lane >> 2);
   const int tok = min(tb + r, S.n - 1);
-  const int c4 = SWZ ? ((lane & 3) ^ fswz(r)) : (lane & 3);
+  const int c4 = (lane & 3) ^ (SW == 1 ? fswz(r) : SW == 2 ? sswz(r) : 0);
   const uint32_t voff = (uint32_t)((rip + tok - tb) * kRow + 16 * (4 * (wave >> 1) + c4));
   // 18 instructions: four from every wavefront, a fifth from wavefronts 0 and 1 (a
   // wavefront-uniform branch, so the condition stays in scalar registers)
@@ -320,30 +342,6 @@ __device__ __forceinline__ void load_nvfp4_raw(const Src& S, int tb, const uint8
   if (wave == 0) dma16_s(pg + 32 * 8, dvoff, st + 1024 * 8);
   else scales(wave - 1);
   if (wave < 2) scales(3 + wave);
-}
-
-// Raw FP8 staging -> bf16 tile.  Thread t writes chunk t % 8 of group m (m < NG) of
-// row t / 8: eight codes read as 8 bytes (raw chunk (t % 8) / 2 of the row, half t % 2),
-// four converts, one 16-byte write.  Sixteen lanes cover two rows x one whole group.
-template <bool SWZ>
-__device__ __forceinline__ uint32_t fp8_dq_read_offset(int tid) {  // + 2048 m
-  const int r = tid >> 3, t7 = tid & 7;
-  return 64 * r + 16 * (SWZ ? ((t7 >> 1) ^ fswz(r)) : (t7 >> 1)) + 8 * (t7 & 1);
-}
-template <bool SWZ, int NG>
-__device__ __forceinline__ void dequant_fp8(uint32_t st, uint32_t tile, int tid) {
-  const int r = tid >> 3, t7 = tid & 7;
-  const uint32_t rd = st + fp8_dq_read_offset<SWZ>(tid);     // + 2048 m
-  const uint32_t wr = tile + 128 * r + ((t7 ^ swz(r)) << 4);  // + 4096 m
-#pragma unroll
-  for (int m = 0; m < NG; ++m) {
-    typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
-    const u32x2 v = *at<u32x2>(rd + 2048 * m);
-    unsigned t[4];
-    fp8x4_to_bf16(v[0], t[0], t[1]);
-    fp8x4_to_bf16(v[1], t[2], t[3]);
-    *at<u32x4>(wr + kGroupBytes * m) = u32x4{t[0], t[1], t[2], t[3]};
-  }
 }
 
 // Raw NVFP4 staging -> bf16 tile.  Thread t writes chunk t % 8 of group m of row t / 8:
@@ -1031,16 +1029,15 @@ __device__ __forceinline__ void softmax_piece(int k, Softmax& S, float* x, float
   }
 }
 
-// Output product of tile i-1 (vtile, P^T in pp) with, between its MFMAs, the softmax of
-// tile i (raw scores x -> P^T in pn, factor alpha) and, for FP8, the dequantisation of
-// raw tile i+1 (staging st -> bf16 tile dtile; the same work as dequant_fp8, latent
-// groups only for the FP8 query).
+// Output product of tile i-1 (vtile, P^T in pp) with, between its MFMAs, for the FP8
+// query the softmax of tile i (raw scores x -> P^T in pn, factor alpha) and the
+// dim-major dequantisation of raw tile i+1 (staging st -> V^T tile dtile, as in
+// dequant_fp8q).
 template <int FMT>
 __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const unsigned* pp, const int* vb, float* x,
                                              Softmax& S, float c, unsigned* pn, float& alpha, uint32_t st,
                                              uint32_t dtile, int tid) {
   constexpr int kAhead = 4;
-  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
   uint32_t base[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) base[v] = vtile + vb[v];
@@ -1054,12 +1051,7 @@ __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const un
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at<s16x4>(base[2 + flip] + off));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  constexpr bool kDq = (FMT == kFmtFp8);
   constexpr bool kSmHere = (FMT == kFmtFp8Q);  // other formats: the softmax runs in the score block
-  const int r = tid >> 3, t7 = tid & 7;
-  const uint32_t rd = st + fp8_dq_read_offset<false>(tid);  // FP8 dequantisation (see dequant_fp8)
-  const uint32_t wr = dtile + 128 * r + ((t7 ^ swz(r)) << 4);
-  u32x2 raw[9];
   // FP8 query: dim-major dequantisation (see dequant_fp8q), with the per-lane parts of
   // the addresses added once so that each access only adds an immediate offset
   uint32_t qrd[4], qwr[4];
@@ -1095,18 +1087,305 @@ __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const un
         *at<u32x4>(qwr[m & 3] + 1024 * m) = u32x4{t[0], t[1], t[2], t[3]};
       }
     }
-    if (kDq) {
-      if ((k & 1) == 0 && k / 2 < 9) raw[k / 2] = *at<u32x2>(rd + 2048 * (k / 2));
-      if ((k & 1) == 0 && k >= 2 && k / 2 - 1 < 9) {
-        const int m = k / 2 - 1;
-        unsigned t[4];
-        fp8x4_to_bf16(raw[m][0], t[0], t[1]);
-        fp8x4_to_bf16(raw[m][1], t[2], t[3]);
-        *at<u32x4>(wr + kGroupBytes * m) = u32x4{t[0], t[1], t[2], t[3]};
-      }
-    }
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// ------------------------------------------------------------------------------------
+// FP8 cache: the split path.  The FP8 matrix core multiplies E4M3 codes exactly and
+// accumulates in fp32, so a bf16 operand can ride on it as two E4M3 operands whose sum
+// is that operand exactly: x = hi + lo with hi = E4M3(x) and lo = E4M3(x - hi).  A bf16
+// value has 8 significant bits and hi takes the top 4 (rounded), so x - hi is an integer
+// multiple of x's last bit of at most 4 bits, which E4M3 holds exactly while it stays
+// above the E4M3 subnormal step 2^-9.  Each row of the query is first scaled by a power
+// of two 2^sh that puts its largest magnitude in [128, 256) (the factor 2^-sh goes into
+// the row's score scale), so every element of magnitude at least 2^-2 after scaling, i.e.
+// 2^-9 of the row's largest, is split exactly; smaller ones keep an absolute error of at
+// most 2^-10 after scaling, under 2^-17 of the row's largest.
+//   scores  S^T = K . (Q_hi + Q_lo)^T: 9 K-steps of 64 dims, each raw K operand read from
+//           LDS once and used by two MFMA 32x32x64 (hi, then lo)
+//   output  O^T += V^T . (P_hi + P_lo)^T over a 32-token tile: one MFMA 32x32x64 per 32
+//           dims, whose K = 64 is the tile's 32 tokens twice: the low lane half carries
+//           V^T with P_hi, the high half the same V^T with P_lo.  V^T is read from the raw
+//           tile with the 8-bit LDS transpose read, so no tile is ever converted to bf16.
+// The softmax weights are split the same way (P = hi + lo to about 8 significant bits,
+// like bf16); they are kept at most 2^8 (lazy rescale), within E4M3's range.
+// ------------------------------------------------------------------------------------
+
+// two floats -> two E4M3 codes (nearest, ties to even) in half-word `hw` of w
+// Written as inline assembly: the compiler's handling of these converts' half-word
+// select (the other half kept from the destination) merges unrelated conversions.
+template <bool HW>
+__device__ __forceinline__ unsigned e4m3_pair(unsigned w, float a, float b) {
+  if (HW) asm("v_cvt_scalef32_pk_fp8_f32 %0, %1, %2, 1.0 op_sel:[0,0,0,1]" : "+v"(w) : "v"(a), "v"(b));
+  else asm("v_cvt_scalef32_pk_fp8_f32 %0, %1, %2, 1.0" : "+v"(w) : "v"(a), "v"(b));
+  return w;
+}
+template <bool HW>
+__device__ __forceinline__ f32x2 e4m3_pair_value(unsigned w) {
+  f32x2 r;
+  if (HW) asm("v_cvt_scalef32_pk_f32_fp8 %0, %1, 1.0 op_sel:[1,0,0]" : "=v"(r) : "v"(w));
+  else asm("v_cvt_scalef32_pk_f32_fp8 %0, %1, 1.0" : "=v"(r) : "v"(w));
+  return r;
+}
+// both: E4M3 codes of (a, b) into half-word HW of *hc, of the remainders into *lc
+template <bool HW>
+__device__ __forceinline__ void e4m3_split_pair(unsigned& hc, unsigned& lc, float a, float b) {
+  hc = e4m3_pair<HW>(hc, a, b);
+  const f32x2 hv = e4m3_pair_value<HW>(hc);
+  lc = e4m3_pair<HW>(lc, a - hv[0], b - hv[1]);
+}
+
+// Query row of this lane as the split operands of the score product: K-step k covers dims
+// 64k .. 64k+63, lane half h dims 64k + 32h .. + 31 as bytes 0..31 (as in qk_tile_f8).
+// Returns sh (the row's values were multiplied by 2^sh).  Two passes over the row: its
+// largest magnitude (of lanes l and l ^ 32), then the conversion.
+__device__ __forceinline__ int q_split(const uint16_t* qrow, const uint16_t* prow, int lh, i32x8* qh, i32x8* ql) {
+  auto src = [&](int k) {
+    const int d = 64 * k + 32 * lh;
+    return reinterpret_cast<const u32x4*>((d < kLatent) ? qrow + d : prow + (d - kLatent));
+  };
+  unsigned amax = 0;  // largest |bf16| bit pattern (ordered like the magnitudes)
+#pragma unroll
+  for (int k = 0; k < 9; ++k) {
+    const u32x4* s = src(k);
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) {
+      const u32x4 raw = s[w4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) amax = max(amax, max(raw[e] & 0x7FFFu, (raw[e] >> 16) & 0x7FFFu));
+    }
+  }
+  {
+    auto r = __builtin_amdgcn_permlane32_swap(amax, amax, false, false);
+    amax = max(r[0], r[1]);
+  }
+  // 2^sh * amax in [128, 256) (bounded so that 2^sh and 2^-sh stay normal floats)
+  const int sh = amax ? min(max(7 - ((int)(amax >> 7) - 127), -100), 100) : 0;
+  const float sc = __uint_as_float((unsigned)(sh + 127) << 23);
+#pragma unroll
+  for (int k = 0; k < 9; ++k) {
+    const u32x4* s = src(k);
+    i32x8 h = {}, l = {};
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) {
+      const u32x4 raw = s[w4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {  // dims 8 w4 + 2e, 8 w4 + 2e + 1 -> bytes of dword 2 w4 + e / 2
+        const float a = __uint_as_float(raw[e] << 16) * sc, b = __uint_as_float(raw[e] & 0xFFFF0000u) * sc;
+        const int dw = 2 * w4 + (e >> 1);
+        unsigned hc = (unsigned)h[dw], lc = (unsigned)l[dw];
+        if (e & 1) e4m3_split_pair<true>(hc, lc, a, b);
+        else e4m3_split_pair<false>(hc, lc, a, b);
+        h[dw] = (int)hc;
+        l[dw] = (int)lc;
+      }
+    }
+    qh[k] = h;
+    ql[k] = l;
+  }
+  return sh;
+}
+
+// Scores of one tile on the split query: S^T = K . Q_hi^T + K . Q_lo^T.  K-step k's raw
+// operand (chunks 2h, 2h+1 of token row l % 32, at f[e] + 2048 k) goes into one of three
+// fixed 8-register buffers (v232..v255), read two K-steps ahead; a buffer is refilled one
+// K-step after its last MFMA.  Every wait counts the reads issued after the ones it needs
+// (LDS reads complete in order).  Accumulation is in vector registers (the accumulation
+// registers hold O); the closing s_nop run covers the wait states before a vector
+// instruction may read the result of this 16-pass MFMA.
+__device__ __forceinline__ f32x16 qk_tile_split(const i32x8* qh, const i32x8* ql, uint32_t raw, const uint32_t* f) {
+  const uint32_t f0 = raw + f[0], f1 = raw + f[1];
+  f32x16 s;
+  asm volatile(
+      "ds_read_b128 v[232:235], %[f0] offset:0\n\t"
+      "ds_read_b128 v[236:239], %[f1] offset:0\n\t"
+      "ds_read_b128 v[240:243], %[f0] offset:2048\n\t"
+      "ds_read_b128 v[244:247], %[f1] offset:2048\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[232:239], %[h0], 0\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[232:239], %[l0], %[s]\n\t"
+      "ds_read_b128 v[248:251], %[f0] offset:4096\n\t"
+      "ds_read_b128 v[252:255], %[f1] offset:4096\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[240:247], %[h1], %[s]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[240:247], %[l1], %[s]\n\t"
+      "ds_read_b128 v[232:235], %[f0] offset:6144\n\t"
+      "ds_read_b128 v[236:239], %[f1] offset:6144\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[248:255], %[h2], %[s]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[248:255], %[l2], %[s]\n\t"
+      "ds_read_b128 v[240:243], %[f0] offset:8192\n\t"
+      "ds_read_b128 v[244:247], %[f1] offset:8192\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[232:239], %[h3], %[s]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[232:239], %[l3], %[s]\n\t"
+      "ds_read_b128 v[248:251], %[f0] offset:10240\n\t"
+      "ds_read_b128 v[252:255], %[f1] offset:10240\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[240:247], %[h4], %[s]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[240:247], %[l4], %[s]\n\t"
+      "ds_read_b128 v[232:235], %[f0] offset:12288\n\t"
+      "ds_read_b128 v[236:239], %[f1] offset:12288\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[248:255], %[h5], %[s]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[248:255], %[l5], %[s]\n\t"
+      "ds_read_b128 v[240:243], %[f0] offset:14336\n\t"
+      "ds_read_b128 v[244:247], %[f1] offset:14336\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[232:239], %[h6], %[s]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[232:239], %[l6], %[s]\n\t"
+      "ds_read_b128 v[248:251], %[f0] offset:16384\n\t"
+      "ds_read_b128 v[252:255], %[f1] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[240:247], %[h7], %[s]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[240:247], %[l7], %[s]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[248:255], %[h8], %[s]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[248:255], %[l8], %[s]\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : [s] "=&v"(s)
+      : [f0] "v"(f0), [f1] "v"(f1),
+        [h0] "v"(qh[0]), [h1] "v"(qh[1]), [h2] "v"(qh[2]), [h3] "v"(qh[3]), [h4] "v"(qh[4]),
+        [h5] "v"(qh[5]), [h6] "v"(qh[6]), [h7] "v"(qh[7]), [h8] "v"(qh[8]),
+        [l0] "v"(ql[0]), [l1] "v"(ql[1]), [l2] "v"(ql[2]), [l3] "v"(ql[3]), [l4] "v"(ql[4]),
+        [l5] "v"(ql[5]), [l6] "v"(ql[6]), [l7] "v"(ql[7]), [l8] "v"(ql[8])
+      : "memory", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243",
+        "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255");
+  return s;
+}
+
+// V^T operand of output MFMA db from the raw tile: dims 32 db + l % 32, tokens 0..31 as
+// bytes 0..31, in both lane halves.  Four 8-bit transpose reads, read t covering tokens
+// 8t .. 8t+7: in each 16-lane group g, lane s addresses token 8t + s / 2 and dims
+// 32 db + 16 (g % 2) + 8 (s % 2) .. + 8 (raw chunk 2 db + g % 2, whose position in the
+// row is swizzled with sswz), and lane j receives dim 32 db + 16 (g % 2) + j of the 8
+// tokens.  vs[2t + (db & 1)] is the lane's offset inside chunk group db / 2 (odd blocks
+// flip position bit 1, byte-offset bit 5).
+__device__ __forceinline__ void split_vt_offsets(int lane, int* vs) {
+  const int g = lane >> 4, s = lane & 15;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int tok = 8 * t + (s >> 1);
+    const int off = 64 * tok + 16 * ((g & 1) ^ sswz(tok)) + 8 * (s & 1);
+    vs[2 * t] = off;
+    vs[2 * t + 1] = off ^ 32;
+  }
+}
+__device__ __forceinline__ i32x8 split_vt_read(const uint32_t* base, int db) {
+  i32x2 r[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    r[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(at<i32x2>(base[2 * t + (db & 1)] + 2048 * (db >> 1)));
+  return i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+}
+
+__device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Online softmax of one tile for the split path, in 16 pieces (one per output MFMA).  x:
+// raw scores of this lane (row l % 32, tokens 8 (v / 4) + 4 (l / 32) + v % 4), masked ones
+// -inf; c > 0 the row's score scale in log2 units.  Weights are p = 2^(x c - m) with the
+// reference m moved only when the tile's max exceeds it by more than 8, and then to
+// that max - 1, so p <= 2^8 and the row's max may grow by 7 before the accumulators
+// need rescaling (any row of the wavefront then rescales all 256 accumulators).  Output: alpha (factor for the accumulators before this tile's
+// product) and P^T in pn: dwords 2j, 2j+1 hold tokens 8j .. 8j+3, 8j+4 .. 8j+7, as the
+// codes of P_hi in the low lane half and of P_lo in the high half.
+struct SplitPieces {
+  float mt, m_new, ex, nm, acc;
+  bool need;
+  unsigned h[4], l[4];  // dword j: codes of values 4j .. 4j+3
+};
+__device__ __forceinline__ void split_piece(int k, Softmax& S, float* x, float c, SplitPieces& w, unsigned* pn,
+                                            float& alpha) {
+  auto split4 = [&](int j) {  // values 4j .. 4j+3 -> dword j of the hi and lo codes
+    unsigned hc = 0, lc = 0;
+    e4m3_split_pair<false>(hc, lc, x[4 * j], x[4 * j + 1]);
+    e4m3_split_pair<true>(hc, lc, x[4 * j + 2], x[4 * j + 3]);
+    w.h[j] = hc;
+    w.l[j] = lc;
+  };
+  if (k == 0) {
+    w.mt = max3(max3(max3(x[0], x[1], x[2]), x[3], x[4]), x[5], x[6]);
+  } else if (k == 1) {
+    w.mt = max3(max3(max3(max3(w.mt, x[7], x[8]), x[9], x[10]), x[11], x[12]), x[13], max3(x[14], x[15], x[15]));
+  } else if (k == 2) {
+    w.mt = pair_max(w.mt) * c;  // -inf stays -inf (c > 0)
+  } else if (k == 3) {
+    w.need = w.mt > S.m_used + 8.0f;
+    w.m_new = w.need ? w.mt - 1.0f : S.m_used;
+    w.ex = __builtin_amdgcn_exp2f(S.m_used - w.m_new);
+  } else if (k == 4) {
+    // (while no token has been seen the accumulators are zero and need no factor)
+    alpha = (w.need && S.m_used != -INFINITY) ? w.ex : 1.0f;
+    S.l_sum *= alpha;
+    S.m_used = w.m_new;
+    w.nm = (w.m_new == -INFINITY) ? 0.f : -w.m_new;
+    w.acc = 0.f;
+  } else if (k >= 5 && k < 13) {
+    const int v = 2 * (k - 5);
+    x[v] = __builtin_amdgcn_exp2f(fmaf(x[v], c, w.nm));
+    x[v + 1] = __builtin_amdgcn_exp2f(fmaf(x[v + 1], c, w.nm));
+    w.acc += x[v];
+    w.acc += x[v + 1];
+    if (k == 8) split4(0);   // values 0..3 are done from step 6 on
+    if (k == 10) split4(1);
+    if (k == 12) split4(2);
+  } else if (k == 13) {
+    split4(3);
+    S.l_sum += w.acc;
+  } else if (k == 14 || k == 15) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = 2 * (k - 14) + jj;
+      const auto r = __builtin_amdgcn_permlane32_swap(w.h[j], w.l[j], false, false);
+      pn[2 * j] = r[0];
+      pn[2 * j + 1] = r[1];
+    }
+  }
+}
+
+// Output product of tile i-1 (raw tile `raw`, P^T in pp) for the split path, with the
+// softmax of tile i in pieces between its 16 MFMAs; V^T reads run kAhead MFMAs ahead.
+template <int kAhead>
+__device__ __forceinline__ void output_phase_split(f32x16* o, uint32_t raw, const unsigned* pp, const int* vs,
+                                                   float* x, Softmax& S, float c, unsigned* pn, float& alpha) {
+  uint32_t base[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) base[v] = raw + vs[v];
+  const i32x8 pb = {(int)pp[0], (int)pp[1], (int)pp[2], (int)pp[3], (int)pp[4], (int)pp[5], (int)pp[6], (int)pp[7]};
+  SplitPieces w;
+  i32x8 va[kDimBlocks];
+#pragma unroll
+  for (int k = 0; k < kAhead; ++k) va[k] = split_vt_read(base, k);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < kDimBlocks; ++k) {
+    o[k] = mfma_f8(va[k], pb, o[k]);
+    if (k + kAhead < kDimBlocks) va[k + kAhead] = split_vt_read(base, k + kAhead);
+    split_piece(k, S, x, c, w, pn, alpha);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The softmax of one tile on its own (the first tile of a range).
+__device__ __forceinline__ float softmax_split(Softmax& S, float* x, float c, unsigned* pn) {
+  SplitPieces w;
+  float alpha = 1.f;
+#pragma unroll
+  for (int k = 0; k < kDimBlocks; ++k) split_piece(k, S, x, c, w, pn, alpha);
+  return alpha;
+}
+
+// The output product of one tile on its own (the last tile of a range).
+__device__ __forceinline__ void pv_split(f32x16* o, uint32_t raw, const unsigned* pp, const int* vs) {
+  uint32_t base[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) base[v] = raw + vs[v];
+  const i32x8 pb = {(int)pp[0], (int)pp[1], (int)pp[2], (int)pp[3], (int)pp[4], (int)pp[5], (int)pp[6], (int)pp[7]};
+#pragma unroll
+  for (int db = 0; db < kDimBlocks; ++db) o[db] = mfma_f8(split_vt_read(base, db), pb, o[db]);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1229,13 +1508,12 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
     const int tb = (lt0 + i) * kTileTokens;
     const uint8_t* pg = PAGED ? page_start(src, e) : nullptr;
     if (FMT == kFmtBf16) load_bf16_tile<PAGED>(src, tb, pg, tile_buf(i), wave, lane);
-    else if (FMT == kFmtFp8 || FMT == kFmtFp8Q) load_fp8_raw<FMT == kFmtFp8Q>(src, tb, pg, raw_buf(i), wave, lane);
+    else if (FMT == kFmtFp8Q) load_fp8_raw<1>(src, tb, pg, raw_buf(i), wave, lane);
     else load_nvfp4_raw(src, tb, pg, raw_buf(i), wave, lane);
   };
   int e_next = 0;  // block-table entry of tile i + kAhead, read one tile early
   auto dequant = [&](int i) {  // raw tile i -> its bf16 buffer
-    if (FMT == kFmtFp8) dequant_fp8<false, 9>(raw_buf(i), tile_buf(i), tid);
-    else if (FMT == kFmtFp8Q) dequant_fp8q(raw_buf(i), tile_buf(i), tid);
+    if (FMT == kFmtFp8Q) dequant_fp8q(raw_buf(i), tile_buf(i), tid);
     else if (FMT == kFmtNvfp4) dequant_nvfp4(raw_buf(i), tile_buf(i), tid);
   };
 
@@ -1297,8 +1575,8 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
       alpha_prev = alpha;
     }
     // the loads the next tile depends on: bf16 tile i+1 (issued one tile ago), raw tile
-    // i+2 (issued now for FP8, one tile ago for NVFP4)
-    if (FMT == kFmtFp8 || FMT == kFmtFp8Q) wait_vmcnt(0);
+    // i+2 (issued now for the FP8 query, one tile ago for NVFP4)
+    if (FMT == kFmtFp8Q) wait_vmcnt(0);
     else wait_vmcnt(more ? nloads : 0);
     __syncthreads();
   };
@@ -1355,6 +1633,138 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
   __syncthreads();  // the next range reuses the LDS buffers
 }
 
+// One token range of one request on the FP8 split path (paged FP8 cache): the same
+// schedule as run_range (scores of tile i, then the output product of tile i-1 with the
+// softmax of tile i between its MFMAs), on raw tiles only, loads four tiles ahead.
+__device__ __forceinline__ void run_range_split(const DecodeParams& p, uint32_t smem, int b, int n, int rg, int lt0,
+                                                int lt1, int64_t slot) {
+  using PP = Pipe<kFmtFp8>;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
+  const int row0 = rg * kRowsPerGroup;
+  const int rows_here = min(kRowsPerGroup, p.rows - row0);
+  const int my_row = kWaveRows * wave + lr;
+  const int rc = min(row0 + my_row, p.rows - 1);  // rows past the end repeat the last row
+  const int nt = lt1 - lt0;
+
+  i32x8 qh[9], ql[9];
+  const int sh = q_split(p.q + ((int64_t)b * p.rows + rc) * kLatent, p.qpe + ((int64_t)b * p.rows + rc) * kRope, lh,
+                         qh, ql);
+  // score scale of this row in log2 units, with the query's 2^sh taken out; kept positive
+  // (sm_scale = 0 gives the plain mean)
+  const float c = fmaxf(p.score_scale * __uint_as_float((unsigned)(127 - sh) << 23), 1e-37f);
+
+  const int vis = max(n - p.q_len + rc / p.H + 1, 0);
+  const int lo = p.window > 0 ? max(vis - p.window, 0) : 0;
+  int min_vis = vis, max_lo = lo;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) {
+    min_vis = min(min_vis, __shfl_xor(min_vis, o));
+    max_lo = max(max_lo, __shfl_xor(max_lo, o));
+  }
+
+  uint32_t fq[2];  // score reads: chunks 2h, 2h+1 of token row l % 32 (as in qk_tile_f8, swizzled with sswz)
+#pragma unroll
+  for (int e = 0; e < 2; ++e) fq[e] = 64 * lr + 16 * ((2 * lh + e) ^ sswz(lr));
+  int vs[8];
+  split_vt_offsets(lane, vs);
+
+  f32x16 o[kDimBlocks];
+#pragma unroll
+  for (int db = 0; db < kDimBlocks; ++db) o[db] = f32x16{};
+  Softmax S{-INFINITY, 0.f, 0.f};
+  unsigned pp[8];
+  float alpha_prev = 1.f;
+
+  const Src src{&p, b, n};
+  const int nloads = (PP::kLoads - wave + kWaves - 1) / kWaves;  // load instructions per tile here
+  auto raw_buf = [&](int i) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(smem + (uint32_t)((i % PP::kRaw) * PP::kRawBytes)));
+  };
+  auto entry = [&](int i) { return table_entry(src, (lt0 + min(i, nt - 1)) * kTileTokens); };
+  auto issue = [&](int i, int e) {
+    load_fp8_raw<2>(src, (lt0 + i) * kTileTokens, page_start(src, e), raw_buf(i), wave, lane);
+  };
+  int e_next = 0;
+
+  auto body = [&](int i, auto FIRST) {
+    constexpr bool first = decltype(FIRST)::value;
+    float x[16];
+    if (i + PP::kAhead < nt) {
+      issue(i + PP::kAhead, e_next);
+      e_next = entry(i + PP::kAhead + 1);
+    }
+    if (!first && __any(alpha_prev != 1.f)) rescale(o, alpha_prev);
+    const f32x16 s = qk_tile_split(qh, ql, raw_buf(i), fq);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) x[v] = s[v];
+    const int tbase = (lt0 + i) * kTileTokens;
+    if (tbase + kTileTokens > min_vis || tbase < max_lo) {
+      // value v (token tbase + 4 (l / 32) + 8 (v/4) + v%4 of the lane) visible iff in [flo, lim)
+      const int lim = vis - tbase - 4 * lh, flo = lo - tbase - 4 * lh;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int t = 8 * (v >> 2) + (v & 3);
+        x[v] = (t < lim && t >= flo) ? x[v] : -INFINITY;
+      }
+    }
+    unsigned pn[8];
+    float alpha = 1.f;
+    if (first) alpha = softmax_split(S, x, c, pn);
+    else output_phase_split<2>(o, raw_buf(i - 1), pp, vs, x, S, c, pn, alpha);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) pp[k] = pn[k];
+    alpha_prev = alpha;
+    // tile i+1 must have landed (its loads were issued kAhead - 1 tiles ago); the loads of
+    // the tiles after it may stay in flight (near the end of the range: wait for all)
+    static_assert(PP::kAhead == 4 && kFp8Loads == 18, "load counts below");
+    if (i + PP::kAhead < nt) {
+      if (wave < 2) asm volatile("s_waitcnt vmcnt(15)" ::: "memory");  // 3 tiles x 5 loads
+      else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");           // 3 tiles x 4 loads
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+  };
+
+  if (nt > 0) {
+    const int pro = min(nt, PP::kAhead);
+    for (int k = 0; k < pro; ++k) issue(k, entry(k));
+    e_next = entry(PP::kAhead);
+    wait_vmcnt((pro - 1) * nloads);  // tile 0
+    __syncthreads();
+    body(0, std::true_type{});
+    for (int i = 1; i < nt; ++i) body(i, std::false_type{});
+    if (__any(alpha_prev != 1.f)) rescale(o, alpha_prev);
+    pv_split(o, raw_buf(nt - 1), pp, vs);
+  }
+
+  // ---- epilogue: normalised partial O and its lse (normalised by the unrounded sum) ----
+  const float l_tot = pair_sum(S.l_sum);
+  const bool ok = l_tot > 0.f;
+  if (my_row < rows_here) {
+    const int row = row0 + my_row;
+    if (lh == 0)
+      p.lse_part[slot * p.l_slot + (int64_t)row * p.l_row] = ok ? (S.m_used + __log2f(l_tot)) * kLn2 : -INFINITY;
+    const float f = ok ? p.v_scale / l_tot : 0.f;
+    float* orow = p.o_part + slot * p.o_slot + (int64_t)row * p.o_row + 4 * lh;
+#pragma unroll
+    for (int g = 0; g < kDimBlocks; g += 4) {
+      f32x4 t[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int db = g + j / 4, q4 = j % 4;
+        t[j] = f32x4{scaled(o[db][4 * q4], f), scaled(o[db][4 * q4 + 1], f), scaled(o[db][4 * q4 + 2], f),
+                     scaled(o[db][4 * q4 + 3], f)};
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) *reinterpret_cast<f32x4*>(orow + 32 * (g + j / 4) + 8 * (j % 4)) = t[j];
+    }
+  }
+  __syncthreads();  // the next range reuses the LDS buffers
+}
+
 // ------------------------------------------------------------------------------------
 // decode kernels
 // ------------------------------------------------------------------------------------
@@ -1382,7 +1792,8 @@ void decode_contig_kernel(const DecodeParams p) {
 //
 // kSegmentCost is what a segment's fixed work costs in tiles: its query load, the
 // pipeline fill and drain, and the partial store.  Measured per workgroup on the
-// B=64, H=128 FP8 workload: about 17 us per extra segment against about 1.6 us per tile.
+// B=64, H=128 FP8 workload (with the bf16-dequantising kernel this path had before the
+// split one): about 17 us per extra segment against about 1.6 us per tile.
 // An empty range can only sit where one request ends and the next begins, so every
 // range between seg_first[b] and seg_last[b] holds tiles of b exactly when its cost
 // interval is not empty (the combine relies on this).
@@ -1485,8 +1896,12 @@ void decode_paged_kernel(const DecodeParams p) {
     // these are the same in every lane (read from LDS words and tables that all lanes
     // share); saying so keeps the page addresses in scalar registers
     auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
-    run_range<FMT, true>(p, lds_addr((lds_ptr)smem), uni(b), uni(n), rg, uni(t - base + tf), uni(seg_end - base + tf),
-                         (int64_t)w + uni(b));
+    if constexpr (FMT == kFmtFp8)
+      run_range_split(p, lds_addr((lds_ptr)smem), uni(b), uni(n), rg, uni(t - base + tf), uni(seg_end - base + tf),
+                      (int64_t)w + uni(b));
+    else
+      run_range<FMT, true>(p, lds_addr((lds_ptr)smem), uni(b), uni(n), rg, uni(t - base + tf),
+                           uni(seg_end - base + tf), (int64_t)w + uni(b));
     if (tid == 0 && rg == 0) {
       if (t == base) p.seg_first[b] = w;
       if (seg_end == base + nb) p.seg_last[b] = w;

@@ -244,6 +244,31 @@ def test_paged_fp8_b64_h128_full_size_sampled():
     assert max_err(lse[pick], rl) <= TOL_LSE
 
 
+def _scale_bf16(bits, k):
+    """bf16 bits times 2^k (exact for these magnitudes)."""
+    return gen.to_bf16_bits(gen.bf16_bits_to_f32(bits) * np.float32(2.0 ** k))
+
+
+@pytest.mark.parametrize("qexp,scale_exp", [(12, -12), (-24, 24), (2, 0), (0, 0)])
+def test_paged_fp8_query_magnitudes_and_peaked_rows(qexp, scale_exp):
+    """The FP8 cache path splits each query row into two E4M3 operands after a power-of-two
+    row scale, and the softmax weights likewise: query rows far from unit magnitude (the
+    score scale compensates, so the scores are unchanged), all-zero rows, and strongly
+    peaked rows (query x 4: most weights fall below E4M3's subnormal range) stay within
+    the FP8 tolerance of the oracle."""
+    say(f"paged fp8 query x 2^{qexp}, sm_scale x 2^{scale_exp}")
+    w = gen.make_paged(B=3, H=128, q_len=1, lo=200, hi=900, page_size=64, fmt=gen.FMT_FP8, seed=65)
+    w.q = _scale_bf16(w.q, qexp)
+    w.qpe = _scale_bf16(w.qpe, qexp)
+    w.q[:, :, :16] = 0
+    w.qpe[:, :, :16] = 0
+    w.sm_scale = w.sm_scale * 2.0 ** scale_exp
+    ro, rl = _paged_ref(w)
+    o, lse = _paged_run(w)
+    assert max_err(o, ro) <= TOL_O_QUANT
+    assert max_err(lse, rl) <= TOL_LSE
+
+
 # ----------------------------------------------------------------------------------
 # sliding window and attention sinks (mla_paged_decode_ext)
 # ----------------------------------------------------------------------------------
