@@ -1138,24 +1138,23 @@ __device__ __forceinline__ void e4m3_split_pair(unsigned& hc, unsigned& lc, floa
 
 // Query row of this lane as the split operands of the score product: K-step k covers dims
 // 64k .. 64k+63, lane half h dims 64k + 32h .. + 31 as bytes 0..31 (as in qk_tile_f8).
-// Returns sh (the row's values were multiplied by 2^sh).  Two passes over the row: its
-// largest magnitude (of lanes l and l ^ 32), then the conversion.
+// Returns sh (the row's values were multiplied by 2^sh).  The lane's 288 values are loaded
+// at once; their largest magnitude (of lanes l and l ^ 32) sets sh, then each K-step is
+// converted (its raw registers are free again once its codes exist).
 __device__ __forceinline__ int q_split(const uint16_t* qrow, const uint16_t* prow, int lh, i32x8* qh, i32x8* ql) {
-  auto src = [&](int k) {
-    const int d = 64 * k + 32 * lh;
-    return reinterpret_cast<const u32x4*>((d < kLatent) ? qrow + d : prow + (d - kLatent));
-  };
-  unsigned amax = 0;  // largest |bf16| bit pattern (ordered like the magnitudes)
+  u32x4 raw[36];
 #pragma unroll
   for (int k = 0; k < 9; ++k) {
-    const u32x4* s = src(k);
+    const int d = 64 * k + 32 * lh;
+    const u32x4* src = reinterpret_cast<const u32x4*>((d < kLatent) ? qrow + d : prow + (d - kLatent));
 #pragma unroll
-    for (int w4 = 0; w4 < 4; ++w4) {
-      const u32x4 raw = s[w4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) amax = max(amax, max(raw[e] & 0x7FFFu, (raw[e] >> 16) & 0x7FFFu));
-    }
+    for (int w4 = 0; w4 < 4; ++w4) raw[4 * k + w4] = src[w4];
   }
+  unsigned amax = 0;  // largest |bf16| bit pattern (ordered like the magnitudes)
+#pragma unroll
+  for (int j = 0; j < 36; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) amax = max(amax, max(raw[j][e] & 0x7FFFu, (raw[j][e] >> 16) & 0x7FFFu));
   {
     auto r = __builtin_amdgcn_permlane32_swap(amax, amax, false, false);
     amax = max(r[0], r[1]);
@@ -1165,14 +1164,13 @@ __device__ __forceinline__ int q_split(const uint16_t* qrow, const uint16_t* pro
   const float sc = __uint_as_float((unsigned)(sh + 127) << 23);
 #pragma unroll
   for (int k = 0; k < 9; ++k) {
-    const u32x4* s = src(k);
     i32x8 h = {}, l = {};
 #pragma unroll
     for (int w4 = 0; w4 < 4; ++w4) {
-      const u32x4 raw = s[w4];
+      const u32x4 r4 = raw[4 * k + w4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {  // dims 8 w4 + 2e, 8 w4 + 2e + 1 -> bytes of dword 2 w4 + e / 2
-        const float a = __uint_as_float(raw[e] << 16) * sc, b = __uint_as_float(raw[e] & 0xFFFF0000u) * sc;
+        const float a = __uint_as_float(r4[e] << 16) * sc, b = __uint_as_float(r4[e] & 0xFFFF0000u) * sc;
         const int dw = 2 * w4 + (e >> 1);
         unsigned hc = (unsigned)h[dw], lc = (unsigned)l[dw];
         if (e & 1) e4m3_split_pair<true>(hc, lc, a, b);
@@ -1647,13 +1645,8 @@ __device__ __forceinline__ void run_range_split(const DecodeParams& p, uint32_t 
   const int my_row = kWaveRows * wave + lr;
   const int rc = min(row0 + my_row, p.rows - 1);  // rows past the end repeat the last row
   const int nt = lt1 - lt0;
-
-  i32x8 qh[9], ql[9];
-  const int sh = q_split(p.q + ((int64_t)b * p.rows + rc) * kLatent, p.qpe + ((int64_t)b * p.rows + rc) * kRope, lh,
-                         qh, ql);
-  // score scale of this row in log2 units, with the query's 2^sh taken out; kept positive
-  // (sm_scale = 0 gives the plain mean)
-  const float c = fmaxf(p.score_scale * __uint_as_float((unsigned)(127 - sh) << 23), 1e-37f);
+  i32x8 qh[9], ql[9];  // the query row, split (q_split)
+  float c = 0.f;       // its score scale (set with the split)
 
   const int vis = max(n - p.q_len + rc / p.H + 1, 0);
   const int lo = p.window > 0 ? max(vis - p.window, 0) : 0;
@@ -1728,10 +1721,20 @@ __device__ __forceinline__ void run_range_split(const DecodeParams& p, uint32_t 
     __syncthreads();
   };
 
+  // the first tiles' loads go out before the query is read and split, so that their
+  // latency and the query's overlap
+  const int pro = min(nt, PP::kAhead);
   if (nt > 0) {
-    const int pro = min(nt, PP::kAhead);
     for (int k = 0; k < pro; ++k) issue(k, entry(k));
     e_next = entry(PP::kAhead);
+  }
+  const int sh = q_split(p.q + ((int64_t)b * p.rows + rc) * kLatent, p.qpe + ((int64_t)b * p.rows + rc) * kRope, lh,
+                         qh, ql);
+  // score scale of this row in log2 units, with the query's 2^sh taken out; kept positive
+  // (sm_scale = 0 gives the plain mean)
+  c = fmaxf(p.score_scale * __uint_as_float((unsigned)(127 - sh) << 23), 1e-37f);
+
+  if (nt > 0) {
     wait_vmcnt((pro - 1) * nloads);  // tile 0
     __syncthreads();
     body(0, std::true_type{});
