@@ -269,6 +269,36 @@ def test_paged_fp8_query_magnitudes_and_peaked_rows(qexp, scale_exp):
     assert max_err(lse, rl) <= TOL_LSE
 
 
+@pytest.mark.parametrize("q_len,page_size", [(1, 64), (2, 32)])
+def test_paged_fp8_rising_scores(q_len, page_size):
+    """Scores that rise along the sequence (positive queries, cache rows drifting along a
+    positive direction) move the softmax reference many times, so the accumulators are
+    rescaled on many tiles; the result still matches the oracle.  Also run with a single
+    range, so that one workgroup walks both requests."""
+    say(f"paged fp8 rising scores q_len={q_len} page={page_size}")
+    w = gen.make_paged(B=2, H=128, q_len=q_len, lo=2000, hi=2000, page_size=page_size, fmt=gen.FMT_FP8, seed=66)
+    rng = np.random.default_rng(4)
+    w.q = gen.to_bf16_bits(np.abs(gen.bf16_bits_to_f32(w.q)))
+    w.qpe = gen.to_bf16_bits(np.abs(gen.bf16_bits_to_f32(w.qpe)))
+    pages = w.cache.reshape(w.num_pages, w.page_stride)
+    rows = {}
+    for b in range(w.B):
+        n = int(w.seq_lens[b])
+        npg = (n + page_size - 1) // page_size
+        t = np.arange(npg * page_size, dtype=np.float32)
+        # the score of token t grows by about 28 (natural units) over the request
+        rows[b] = rng.standard_normal((npg * page_size, 576), dtype=np.float32) + (t / n)[:, None] * np.float32(0.85)
+    w.kv_scale = float(np.float32(max(float(np.abs(r).max()) for r in rows.values())) / np.float32(448.0))
+    for b in range(w.B):
+        npg = rows[b].shape[0] // page_size
+        pages[w.block_tables[b, :npg]] = gen.encode_pages(rows[b], w.fmt, page_size, w.page_stride, w.kv_scale)
+    ro, rl = _paged_ref(w)
+    for ns in (None, 1):
+        o, lse = _paged_run(w, ns)
+        assert max_err(o, ro) <= TOL_O_QUANT, ns
+        assert max_err(lse, rl) <= TOL_LSE, ns
+
+
 # ----------------------------------------------------------------------------------
 # sliding window and attention sinks (mla_paged_decode_ext)
 # ----------------------------------------------------------------------------------
