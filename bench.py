@@ -115,7 +115,8 @@ def copy_calibration(torch, dev, nbytes: int, steps: int):
 
 
 # Score flops run at the FP8 rate and output flops at the bf16 rate in the FP8-query
-# variant: per (row, token) pair 1152 flops at 5.0 PFLOP/s and 1024 at 2.5 PFLOP/s.
+# variant (its output product is two FP8 terms, the bf16 rate's time): per (row, token)
+# pair 1152 flops at 5.0 PFLOP/s and 1024 at 2.5 PFLOP/s.
 MFMA_FP8_PEAK_TFLOPS = 5000.0
 MIXED_PEAK_TFLOPS = 2176.0 / (1152.0 / MFMA_FP8_PEAK_TFLOPS + 1024.0 / MFMA_BF16_PEAK_TFLOPS)
 
@@ -141,12 +142,13 @@ def time_fp8_query_variant(mla, torch, w, q, qpe, cache, bt, sl, G, args, flops)
     dec = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     dec_tflops = flops / (dec * 1e-3) / 1e12
     log(f"[bench] fp8-query variant: {ms_step:.4f} ms/step, decode {dec:.4f} ms")
-    return {"kv_format": "fp8_e4m3, query rounded to e4m3 (FP8-MFMA scores, bf16 output product)",
+    return {"kv_format": "fp8_e4m3, query rounded to e4m3 (FP8-MFMA scores; output product as on the FP8 path: "
+                         "weights split into two E4M3 terms on FP8 MFMA)",
             "ms_per_step": round(ms_step, 5), "value": round(flops / (ms_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
             "decode_ms": round(dec, 5),
             "roofline": {"bound": "mfma", "achieved": round(dec_tflops, 3), "peak": round(MIXED_PEAK_TFLOPS, 1),
                          "unit": "TFLOP/s", "frac": round(dec_tflops / MIXED_PEAK_TFLOPS, 4),
-                         "peak_note": "score flops at the fp8 peak, output flops at the bf16 peak"}}
+                         "peak_note": "score flops at the fp8 peak, output flops at the bf16 peak (two FP8 terms)"}}
 
 
 def run_contig(args, w, mla, torch, np, gen):

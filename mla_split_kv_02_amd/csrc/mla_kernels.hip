@@ -37,12 +37,10 @@
 // Paged ranges are balanced by cost: a request costs its tiles plus a fixed overhead for
 // its segment's query load, pipeline fill and partial store (decode_paged_kernel).
 //
-// FP8 query (cache format kFmtFp8Q, the TokenSpeed page's FP8 decode): the query is
-// rounded to E4M3 once per range (72 registers), the scores run on 9 FP8 MFMA 32x32x64
-// straight from the raw FP8 tile, and the bf16 tile holds only V^T, dim-major, filled with
-// the 8-bit LDS transpose read so that each output MFMA reads its V operand at once.  Its
-// softmax runs between the output MFMAs of the same iteration instead (nine FP8 MFMAs
-// hide less of it).
+// FP8 query (cache format kFmtFp8Q, the TokenSpeed page's FP8 decode): the same split
+// loop with the query rounded to E4M3 once per range (72 registers) instead of split, so
+// its scores take 9 FP8 MFMA 32x32x64 per tile instead of 18; the weights and the output
+// product are the split path's.
 //
 // A sliding window (paged) starts each request's tiles at the one holding its first
 // visible token and masks below the window; attention sinks enter in the combine.
@@ -92,10 +90,8 @@ constexpr float kLn2 = 0.69314718055994531f;
 
 // Buffers and load distance per cache format.  Tile i sits in bf16 buffer i % kTiles
 // (kStride bytes apart); raw tile i (FP8 / NVFP4) in staging buffer i % kRaw.  In
-// iteration i the loads of tile i + kAhead are issued.  With the FP8 query the scores
-// read the raw FP8 tile itself, so it stays until its own iteration (three staging
-// buffers) and the bf16 tile holds only the 512 latent dims the output product needs.
-// The FP8 cache's split path has no bf16 tiles at all.
+// iteration i the loads of tile i + kAhead are issued.  The FP8 formats (split loop) have
+// no bf16 tiles at all.
 template <int FMT> struct Pipe;
 template <> struct Pipe<kFmtBf16> {
   static constexpr int kTiles = 4, kStride = kTileBytes, kRaw = 0, kRawBytes = 0, kAhead = 2, kLoads = kBf16Loads;
@@ -104,16 +100,14 @@ template <> struct Pipe<kFmtNvfp4> {
   static constexpr int kTiles = 3, kStride = kTileBytes, kRaw = 3, kRawBytes = kNvRawBytes, kAhead = 3,
                        kLoads = kNvDataLoads + kNvScaleLoads;
 };
-template <> struct Pipe<kFmtFp8Q> {
-  static constexpr int kTiles = 3, kStride = 8 * kGroupBytes, kRaw = 3, kRawBytes = kFp8RawBytes, kAhead = 2,
-                       kLoads = kFp8Loads;
-};
 // FP8 cache (split path): raw tiles only (no bf16 copy); a tile is read by its score
 // block and by the next iteration's output product, and the loads run four tiles ahead:
 // six buffers.
 template <> struct Pipe<kFmtFp8> {
   static constexpr int kTiles = 0, kStride = 0, kRaw = 6, kRawBytes = kFp8RawBytes, kAhead = 4, kLoads = kFp8Loads;
 };
+// The FP8 query runs the same loop on the same raw tiles.
+template <> struct Pipe<kFmtFp8Q> : Pipe<kFmtFp8> {};
 template <int FMT> constexpr int smem_bytes() {
   return Pipe<FMT>::kTiles * Pipe<FMT>::kStride + Pipe<FMT>::kRaw * Pipe<FMT>::kRawBytes;
 }
@@ -142,13 +136,6 @@ __device__ __forceinline__ int tile_off(int r, int c) {
 // ------------------------------------------------------------------------------------
 // Conversions
 // ------------------------------------------------------------------------------------
-
-// Four E4M3 codes (one dword) -> four bf16 (two dwords), exactly (hardware convert with
-// unit scale).
-__device__ __forceinline__ void fp8x4_to_bf16(unsigned w, unsigned& o0, unsigned& o1) {
-  o0 = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false));
-  o1 = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true));
-}
 
 __device__ __forceinline__ unsigned pack_hi16(float lo, float hi) {
   // bf16 pair from two floats whose low 16 bits are zero (exact conversion)
@@ -286,28 +273,24 @@ __device__ __forceinline__ void load_bf16_tile(const Src& S, int tb, const uint8
 }
 
 // FP8 rows, raw.  Staging layout: chunk c (16 codes) of row r at 2048 (c / 4) + 64 r +
-// 16 p, p = (c % 4) ^ f(r) with f = fswz (SW = 1), sswz (SW = 2) or 0.  Instruction j = 4m + w covers chunk
-// group j / 2 of rows 16 (j % 2) ..: lane l takes row 16 (w % 2) + l / 4 and the chunk
-// 4 (w / 2 + 2m) + c % 4 that belongs at position l % 4.  The swizzle serves the FP8
-// score reads (two 16-byte chunks of one row per lane and step): any 16 consecutive rows
-// at one logical chunk hit 16 different 16-byte bank slots, and so do 32 rows mod 32.
-__device__ __forceinline__ int fswz(int r) { return ((r >> 2) ^ (r >> 4)) & 3; }
-// The FP8 split path's swizzle: row bit 2 flips position bit 1 and row bit 3 position
-// bit 0 (fswz has them the other way round).  Its score reads stay conflict-free (rows
-// r, r+4, r+8, r+12 take four different positions), and so do its 8-bit transpose reads,
-// where one half-wavefront reads two adjacent chunks (lane groups g = 0, 1) of rows
-// 8t .. 8t+7: rows u and u+4 share a bank row (256 bytes apart), and their positions
-// differ in bit 1 while the two chunks differ in bit 0, so the four (row, chunk) pairs of
-// a bank row take four different positions.
+// 16 p, p = (c % 4) ^ sswz(r).  Instruction j = 4m + w covers chunk group j / 2 of rows
+// 16 (j % 2) ..: lane l takes row 16 (w % 2) + l / 4 and the chunk 4 (w / 2 + 2m) + c % 4
+// that belongs at position l % 4.
+// The swizzle: row bit 2 flips position bit 1 and row bit 3 position bit 0 (and row bit 4
+// position bit 0 again).  The score reads (two 16-byte chunks of one row per lane and
+// step) stay conflict-free: rows r, r+4, r+8, r+12 at one logical chunk take four
+// different positions.  So do the 8-bit transpose reads, where one half-wavefront reads
+// two adjacent chunks (lane groups g = 0, 1) of rows 8t .. 8t+7: rows u and u+4 share a
+// bank row (256 bytes apart), and their positions differ in bit 1 while the two chunks
+// differ in bit 0, so the four (row, chunk) pairs of a bank row take four different
+// positions.
 __device__ __forceinline__ int sswz(int r) { return (((r >> 1) & 2) | ((r >> 3) & 1)) ^ ((r >> 4) & 1); }
 
-// SW: 0 no swizzle, 1 fswz, 2 sswz
-template <int SW>
 __device__ __forceinline__ void load_fp8_raw(const Src& S, int tb, const uint8_t* pg, uint32_t st, int wave, int lane) {
   const int rip = tb & (S.p->page_size - 1);
   const int r = 16 * (wave & 1) + (lane >> 2);
   const int tok = min(tb + r, S.n - 1);
-  const int c4 = (lane & 3) ^ (SW == 1 ? fswz(r) : SW == 2 ? sswz(r) : 0);
+  const int c4 = (lane & 3) ^ sswz(r);
   const uint32_t voff = (uint32_t)((rip + tok - tb) * kRow + 16 * (4 * (wave >> 1) + c4));
   // 18 instructions: four from every wavefront, a fifth from wavefronts 0 and 1 (a
   // wavefront-uniform branch, so the condition stays in scalar registers)
@@ -597,64 +580,6 @@ __device__ __forceinline__ void pv_tile(f32x16* o, uint32_t tile, const unsigned
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[db], 0, 0, 0);
     }
   }
-}
-
-// FP8 query: the bf16 tile holds V^T, dim-major: dim d's 32 tokens as four 16-byte
-// chunks (8 tokens each) of a 64-byte row, chunk x at position x ^ fswz(d).  The output
-// MFMA's A operand (dims 32 db + l % 32, tokens 16 ks + 8 (l / 32) ..) is then one
-// 16-byte read at 2048 db + vq[2 ks + (db & 1)] (fswz(32 db + r) = fswz(r) ^ 2 (db & 1));
-// 16 consecutive dims at one chunk, and 32 mod 32, fall into different bank slots.
-__device__ __forceinline__ bf16x8 vt_read(uint32_t vt, const int* vq, int db, int ks) {
-  return *at<bf16x8>(vt + 2048 * db + vq[2 * ks + (db & 1)]);
-}
-
-__device__ __forceinline__ void pv_tile_vt(f32x16* o, uint32_t vt, const unsigned* pp, const int* vq) {
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pp[4 * ks], pp[4 * ks + 1], pp[4 * ks + 2], pp[4 * ks + 3]});
-#pragma unroll
-    for (int db = 0; db < kDimBlocks; ++db)
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_read(vt, vq, db, ks), pb, o[db], 0, 0, 0);
-  }
-}
-
-// FP8 query: raw FP8 staging (swizzled, token-major) -> V^T (dim-major, above).  Wave w,
-// step m (0..7) covers dims 128 w + 16 m .. + 15 of all 32 tokens with one 8-bit transpose
-// read: in each 16-lane group g, lane s addresses token 8 g + s / 2, dims + 8 (s % 2) .. + 8
-// (8 code bytes), and lane j receives dim + j of those 8 tokens (byte b = token 8 g + b);
-// four converts give its 8 bf16 values, written as chunk g of the dim's row.
-struct DqVt {
-  uint32_t rd;     // raw read base of this lane (+ 4096 w + 64 tok + 8 (s % 2))
-  int ro[4];       // + 16 ((m % 4) ^ fswz(tok)), by m % 4; + 2048 (m / 4)
-  uint32_t wr;     // V^T write base (+ 8192 w + 64 j)
-  int wo[4];       // + 16 ((g ^ (j / 4) ^ m) % 4), by m % 4; + 1024 m
-};
-__device__ __forceinline__ DqVt dq_vt_offsets(int tid) {
-  const int w = tid >> 6, l = tid & 63, g = l >> 4, j = l & 15;
-  const int tok = 8 * g + (j >> 1), f = fswz(tok);
-  DqVt d;
-  d.rd = 4096 * w + 64 * tok + 8 * (j & 1);
-  d.wr = 8192 * w + 64 * j;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    d.ro[m] = 16 * (m ^ f);
-    d.wo[m] = 16 * ((g ^ (j >> 2) ^ m) & 3);
-  }
-  return d;
-}
-__device__ __forceinline__ i32x2 dq_vt_read(uint32_t st, const DqVt& d, int m) {
-  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(at<i32x2>(st + d.rd + 2048 * (m >> 2) + d.ro[m & 3]));
-}
-__device__ __forceinline__ void dq_vt_write(uint32_t vt, const DqVt& d, int m, i32x2 raw) {
-  unsigned t[4];
-  fp8x4_to_bf16((unsigned)raw[0], t[0], t[1]);
-  fp8x4_to_bf16((unsigned)raw[1], t[2], t[3]);
-  *at<u32x4>(vt + d.wr + 1024 * m + d.wo[m & 3]) = u32x4{t[0], t[1], t[2], t[3]};
-}
-__device__ __forceinline__ void dequant_fp8q(uint32_t st, uint32_t vt, int tid) {
-  const DqVt d = dq_vt_offsets(tid);
-#pragma unroll
-  for (int m = 0; m < 8; ++m) dq_vt_write(vt, d, m, dq_vt_read(st, d, m));
 }
 
 // o *= alpha in place in the accumulation registers, one value at a time through one
@@ -972,71 +897,9 @@ __device__ __forceinline__ f32x16 qk_softmax_tile(const bf16x8* q, uint32_t tile
   return s;
 }
 
-// The output phase of a tile as 32 steps, one output MFMA each, fenced by scheduling
-// barriers so that the work between the MFMAs stays spread out: the transpose reads
-// run four MFMAs ahead (the LDS read latency is about four MFMA issue intervals), and
-// the online softmax of the current tile and the dequantisation of the next one are
-// cut into pieces of a few vector instructions per step.  The softmax pieces compute
-// exactly what softmax_tile does.
-struct SoftmaxPieces {
-  float mt, m_new, ex, nm, acc;
-  bool need;
-  unsigned d[8];
-};
-
-__device__ __forceinline__ void softmax_piece(int k, Softmax& S, float* x, float c, SoftmaxPieces& w, unsigned* pp,
-                                              float& alpha) {
-  if (k == 0) {
-    w.mt = max3(max3(max3(x[0], x[1], x[2]), x[3], x[4]), x[5], x[6]);
-  } else if (k == 1) {
-    w.mt = max3(max3(max3(max3(w.mt, x[7], x[8]), x[9], x[10]), x[11], x[12]), x[13], max3(x[14], x[15], x[15]));
-  } else if (k == 2) {
-    w.mt = pair_max(w.mt) * c;  // -inf stays -inf (c > 0)
-  } else if (k == 3) {
-    w.need = w.mt > S.m_used + kTau;
-    w.m_new = w.need ? w.mt : S.m_used;
-    w.ex = __builtin_amdgcn_exp2f(S.m_used - w.m_new);
-  } else if (k == 4) {
-    // (while no token has been seen the accumulators are zero and need no factor)
-    alpha = (w.need && S.m_used != -INFINITY) ? w.ex : 1.0f;
-    S.l_sum *= alpha;
-    S.l_rnd *= alpha;
-    S.m_used = w.m_new;
-    w.nm = (w.m_new == -INFINITY) ? 0.f : -w.m_new;
-    w.acc = 0.f;
-  } else if (k >= 5 && k < 21) {
-    const int v = k - 5;
-    x[v] = __builtin_amdgcn_exp2f(fmaf(x[v], c, w.nm));
-    w.acc += x[v];
-  } else if (k >= 21 && k < 25) {
-    const int j = k - 21;
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    const bf16x2 p0 = {(__bf16)x[4 * j], (__bf16)x[4 * j + 1]};
-    const bf16x2 p1 = {(__bf16)x[4 * j + 2], (__bf16)x[4 * j + 3]};
-    S.l_rnd = __builtin_amdgcn_fdot2_f32_bf16(p0, ones, S.l_rnd, false);
-    S.l_rnd = __builtin_amdgcn_fdot2_f32_bf16(p1, ones, S.l_rnd, false);
-    w.d[2 * j] = __builtin_bit_cast(unsigned, p0);
-    w.d[2 * j + 1] = __builtin_bit_cast(unsigned, p1);
-  } else if (k == 25 || k == 26) {
-    if (k == 25) S.l_sum += w.acc;
-    const int ks = k - 25;
-    const auto r02 = __builtin_amdgcn_permlane32_swap(w.d[4 * ks + 0], w.d[4 * ks + 2], false, false);
-    const auto r13 = __builtin_amdgcn_permlane32_swap(w.d[4 * ks + 1], w.d[4 * ks + 3], false, false);
-    pp[4 * ks + 0] = r02[0];
-    pp[4 * ks + 1] = r13[0];
-    pp[4 * ks + 2] = r02[1];
-    pp[4 * ks + 3] = r13[1];
-  }
-}
-
-// Output product of tile i-1 (vtile, P^T in pp) with, between its MFMAs, for the FP8
-// query the softmax of tile i (raw scores x -> P^T in pn, factor alpha) and the
-// dim-major dequantisation of raw tile i+1 (staging st -> V^T tile dtile, as in
-// dequant_fp8q).
-template <int FMT>
-__device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const unsigned* pp, const int* vb, float* x,
-                                             Softmax& S, float c, unsigned* pn, float& alpha, uint32_t st,
-                                             uint32_t dtile, int tid) {
+// Output product of tile i-1 (vtile, P^T in pp): 32 MFMAs, V^T from the transpose reads
+// four MFMAs ahead (bf16 and NVFP4 caches; the softmax ran in the score block).
+__device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const unsigned* pp, const int* vb) {
   constexpr int kAhead = 4;
   uint32_t base[4];
 #pragma unroll
@@ -1044,27 +907,12 @@ __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const un
   const bf16x8 pb0 = __builtin_bit_cast(bf16x8, u32x4{pp[0], pp[1], pp[2], pp[3]});
   const bf16x8 pb1 = __builtin_bit_cast(bf16x8, u32x4{pp[4], pp[5], pp[6], pp[7]});
   auto tr = [&](int k) {  // V^T operand of output MFMA k (dims block k % 16, K-step k / 16)
-    if constexpr (FMT == kFmtFp8Q) return *at<bf16x8>(base[2 * (k >> 4) + (k & 1)] + 2048 * (k & 15));
     const int db = k & 15, ks = k >> 4, flip = (db & 1) ^ ks;
     const uint32_t off = kGroupBytes * (db >> 1) + 16 * 128 * ks;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at<s16x4>(base[flip] + off));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at<s16x4>(base[2 + flip] + off));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  constexpr bool kSmHere = (FMT == kFmtFp8Q);  // other formats: the softmax runs in the score block
-  // FP8 query: dim-major dequantisation (see dequant_fp8q), with the per-lane parts of
-  // the addresses added once so that each access only adds an immediate offset
-  uint32_t qrd[4], qwr[4];
-  i32x2 rawq[8];
-  if constexpr (FMT == kFmtFp8Q) {
-    const DqVt dq = dq_vt_offsets(tid);
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      qrd[x] = st + dq.rd + dq.ro[x];
-      qwr[x] = dtile + dq.wr + dq.wo[x];
-    }
-  }
-  SoftmaxPieces w;
   bf16x8 va[2 * kDimBlocks];
 #pragma unroll
   for (int k = 0; k < kAhead; ++k) va[k] = tr(k);
@@ -1073,20 +921,6 @@ __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const un
   for (int k = 0; k < 2 * kDimBlocks; ++k) {
     o[k & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k], (k < kDimBlocks) ? pb0 : pb1, o[k & 15], 0, 0, 0);
     if (k + kAhead < 2 * kDimBlocks) va[k + kAhead] = tr(k + kAhead);
-    if constexpr (kSmHere) softmax_piece(k, S, x, c, w, pn, alpha);
-    if constexpr (FMT == kFmtFp8Q) {
-      if ((k & 1) == 0 && k / 2 < 8) {
-        const int m = k / 2;
-        rawq[m] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(at<i32x2>(qrd[m & 3] + 2048 * (m >> 2)));
-      }
-      if ((k & 1) == 0 && k >= 2 && k / 2 - 1 < 8) {
-        const int m = k / 2 - 1;
-        unsigned t[4];
-        fp8x4_to_bf16((unsigned)rawq[m][0], t[0], t[1]);
-        fp8x4_to_bf16((unsigned)rawq[m][1], t[2], t[3]);
-        *at<u32x4>(qwr[m & 3] + 1024 * m) = u32x4{t[0], t[1], t[2], t[3]};
-      }
-    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -1183,6 +1017,29 @@ __device__ __forceinline__ int q_split(const uint16_t* qrow, const uint16_t* pro
     ql[k] = l;
   }
   return sh;
+}
+
+// FP8 query (cache format 3): the query row rounded to E4M3 once per segment, in the
+// operand layout of qk_tile_f8 (K-step k: dims 64k + 32h .. + 31 as bytes 0..31), with the
+// same encoder as the cache append (nearest, ties to even, saturating).
+__device__ __forceinline__ void q_round_e4m3(const uint16_t* qrow, const uint16_t* prow, int lh, i32x8* q8) {
+#pragma unroll
+  for (int k = 0; k < 9; ++k) {
+    const int d = 64 * k + 32 * lh;
+    const u32x4* src = reinterpret_cast<const u32x4*>((d < kLatent) ? qrow + d : prow + (d - kLatent));
+    i32x8 v = {};
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) {
+      const u32x4 raw = src[w4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {  // dims 8 w4 + 2e, 8 w4 + 2e + 1
+        const unsigned lo = e4m3_code(__uint_as_float(raw[e] << 16));
+        const unsigned hi = e4m3_code(__uint_as_float(raw[e] & 0xFFFF0000u));
+        v[2 * w4 + (e >> 1)] |= (int)((lo | (hi << 8)) << (16 * (e & 1)));
+      }
+    }
+    q8[k] = v;
+  }
 }
 
 // Scores of one tile on the split query: S^T = K . Q_hi^T + K . Q_lo^T.  K-step k's raw
@@ -1404,41 +1261,16 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
   const float c = fmaxf(p.score_scale, 1e-30f);           // sm_scale = 0 gives the plain mean
   const int nt = lt1 - lt0;
 
-  // Q^T operand, row rc.  bf16: dims 16k + 8 (l / 32) .. + 8.  FP8 query: the E4M3 codes
-  // of dims 64k + 32 (l / 32) .. + 32, byte j of the operand holding dim 64k + 32 (l / 32)
-  // + j (TokenSpeed page, forward_decode: the query is cast to the FP8 cache type).
-  constexpr bool kQ8 = (FMT == kFmtFp8Q);
-  constexpr bool kSmQk = !kQ8;
-  bf16x8 q[kQ8 ? 1 : kKSteps];
-  i32x8 q8[kQ8 ? 9 : 1];
+  // Q^T operand, row rc: dims 16k + 8 (l / 32) .. + 8
+  bf16x8 q[kKSteps];
   {
     const uint16_t* qrow = p.q + ((int64_t)b * p.rows + rc) * kLatent;
     const uint16_t* prow = p.qpe + ((int64_t)b * p.rows + rc) * kRope;
-    if constexpr (kQ8) {
 #pragma unroll
-      for (int k = 0; k < 9; ++k) {
-        const int d = 64 * k + 32 * lh;
-        const u32x4* src = reinterpret_cast<const u32x4*>((d < kLatent) ? qrow + d : prow + (d - kLatent));
-        i32x8 v = {};
-#pragma unroll
-        for (int w4 = 0; w4 < 4; ++w4) {
-          const u32x4 raw = src[w4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {  // dims 8 w4 + 2e, 8 w4 + 2e + 1
-            const unsigned lo = e4m3_code(__uint_as_float(raw[e] << 16));
-            const unsigned hi = e4m3_code(__uint_as_float(raw[e] & 0xFFFF0000u));
-            v[2 * w4 + (e >> 1)] |= (int)((lo | (hi << 8)) << (16 * (e & 1)));
-          }
-        }
-        q8[k] = v;
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < kKSteps; ++k) {
-        const int d = 16 * k + 8 * lh;
-        const uint16_t* src = (d < kLatent) ? qrow + d : prow + (d - kLatent);
-        q[k] = *reinterpret_cast<const bf16x8*>(src);
-      }
+    for (int k = 0; k < kKSteps; ++k) {
+      const int d = 16 * k + 8 * lh;
+      const uint16_t* src = (d < kLatent) ? qrow + d : prow + (d - kLatent);
+      q[k] = *reinterpret_cast<const bf16x8*>(src);
     }
   }
   // query i of a request sees tokens lo .. vis - 1: vis = n - q_len + i + 1, and lo = 0, or
@@ -1459,17 +1291,11 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
 #pragma unroll
     for (int x = 0; x < 4; ++x) ab[x] = a_base ^ (32 * x);
   }
-  uint32_t fq[2];  // FP8-query score reads: chunks 2h, 2h+1 of token row l % 32 (see qk_tile_f8)
-#pragma unroll
-  for (int e = 0; e < 2; ++e) fq[e] = 64 * lr + 16 * ((2 * lh + e) ^ fswz(lr));
   // transpose reads: in a group of 16 lanes (g = l / 16, j = l % 16), lane j addresses
   // token 8 (g >> 1) + 4e + j / 4 and dims 16 (g & 1) + 4 (j % 4) .. + 4; lane i of the
   // group then receives dim 16 (g & 1) + i of those four tokens
-  int vb[4];  // transpose-read offsets [e][db & 1] (see pv_tile); FP8 query: V^T read offsets (see vt_read)
-  if constexpr (FMT == kFmtFp8Q) {
-#pragma unroll
-    for (int x = 0; x < 4; ++x) vb[x] = 64 * lr + 16 * (((2 * (x >> 1) + lh) ^ fswz(lr) ^ (2 * (x & 1))) & 3);
-  } else {
+  int vb[4];  // transpose-read offsets [e][db & 1] (see pv_tile)
+  {
     const int g = lane >> 4, j = lane & 15;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -1486,7 +1312,6 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
   for (int db = 0; db < kDimBlocks; ++db) o[db] = f32x16{};
   Softmax S{-INFINITY, 0.f, 0.f};
   unsigned pp[8];
-  float alpha_prev = 1.f;
 
   const Src src{&p, b, n};
   const int nloads = (PP::kLoads - wave + kWaves - 1) / kWaves;  // load instructions per tile here
@@ -1506,37 +1331,27 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
     const int tb = (lt0 + i) * kTileTokens;
     const uint8_t* pg = PAGED ? page_start(src, e) : nullptr;
     if (FMT == kFmtBf16) load_bf16_tile<PAGED>(src, tb, pg, tile_buf(i), wave, lane);
-    else if (FMT == kFmtFp8Q) load_fp8_raw<1>(src, tb, pg, raw_buf(i), wave, lane);
     else load_nvfp4_raw(src, tb, pg, raw_buf(i), wave, lane);
   };
   int e_next = 0;  // block-table entry of tile i + kAhead, read one tile early
   auto dequant = [&](int i) {  // raw tile i -> its bf16 buffer
-    if (FMT == kFmtFp8Q) dequant_fp8q(raw_buf(i), tile_buf(i), tid);
-    else if (FMT == kFmtNvfp4) dequant_nvfp4(raw_buf(i), tile_buf(i), tid);
+    if (FMT == kFmtNvfp4) dequant_nvfp4(raw_buf(i), tile_buf(i), tid);
   };
 
-  // Scores of the latest tile (masked).  Except with the FP8 query, their softmax runs in
-  // the next tile's score block (kSmQk), so they stay in registers until then.  With the
-  // FP8 query it runs in pieces between the output MFMAs of the same iteration: its score
-  // block has only nine (FP8) MFMAs to hide it under, and measured slower so.
-  float x_keep[kSmQk ? 16 : 1];
+  // Scores of the latest tile (masked); their softmax runs in the next tile's score block,
+  // so they stay in registers until then.
+  float x[16];
 
   // one tile; FIRST: there is no previous tile to multiply
   auto body = [&](int i, auto FIRST) {
     constexpr bool first = decltype(FIRST)::value;
-    float x_loc[kSmQk ? 1 : 16];
-    float* x = kSmQk ? x_keep : x_loc;
     const bool more = i + PP::kAhead < nt;
     if (more) {
       issue(i + PP::kAhead, e_next);
       e_next = entry(i + PP::kAhead + 1);
     }
     f32x16 s;
-    if constexpr (!kSmQk) {
-      if (!first && __any(alpha_prev != 1.f)) rescale(o, alpha_prev);
-      if constexpr (kQ8) s = qk_tile_f8(q8, raw_buf(i), fq);  // the raw tile itself
-      else s = qk_tile(q, tile_buf(i), ab);
-    } else if (first) {
+    if (first) {
       s = qk_tile(q, tile_buf(i), ab);
     } else {
       // scores of tile i, softmax of tile i-1 (x) -> P^T in pp and its factor
@@ -1556,26 +1371,12 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
         x[v] = (t < lim && t >= flo) ? x[v] : -INFINITY;
       }
     }
-    unsigned pn[8];
-    float alpha = 1.f;
     // past the last tile the dequantisation only rewrites an unused buffer
-    if (first || FMT == kFmtNvfp4) {
-      if (FMT != kFmtBf16) dequant(i + 1);
-    }
-    if (first) {
-      if constexpr (!kSmQk) alpha = softmax_tile(S, x, c, pn);
-    } else {
-      output_phase<FMT>(o, tile_buf(i - 1), pp, vb, x, S, c, pn, alpha, raw_buf(i + 1), tile_buf(i + 1), tid);
-    }
-    if constexpr (!kSmQk) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) pp[k] = pn[k];
-      alpha_prev = alpha;
-    }
-    // the loads the next tile depends on: bf16 tile i+1 (issued one tile ago), raw tile
-    // i+2 (issued now for the FP8 query, one tile ago for NVFP4)
-    if (FMT == kFmtFp8Q) wait_vmcnt(0);
-    else wait_vmcnt(more ? nloads : 0);
+    if (FMT == kFmtNvfp4) dequant(i + 1);
+    if (!first) output_phase(o, tile_buf(i - 1), pp, vb);
+    // the loads the next tile depends on: bf16 tile i+1 (issued one tile ago), raw NVFP4
+    // tile i+2 (one tile ago)
+    wait_vmcnt(more ? nloads : 0);
     __syncthreads();
   };
 
@@ -1592,15 +1393,9 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
     }
     body(0, std::true_type{});
     for (int i = 1; i < nt; ++i) body(i, std::false_type{});
-    if constexpr (!kSmQk) {
-      if (__any(alpha_prev != 1.f)) rescale(o, alpha_prev);
-      if constexpr (kQ8) pv_tile_vt(o, tile_buf(nt - 1), pp, vb);
-      else pv_tile(o, tile_buf(nt - 1), pp, vb);
-    } else {
-      const float alpha = softmax_tile(S, x_keep, c, pp);  // the last tile's softmax
-      if (__any(alpha != 1.f)) rescale(o, alpha);
-      pv_tile(o, tile_buf(nt - 1), pp, vb);
-    }
+    const float alpha = softmax_tile(S, x, c, pp);  // the last tile's softmax
+    if (__any(alpha != 1.f)) rescale(o, alpha);
+    pv_tile(o, tile_buf(nt - 1), pp, vb);
   }
 
   // ---- epilogue: normalised partial O and its lse ----
@@ -1634,6 +1429,9 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
 // One token range of one request on the FP8 split path (paged FP8 cache): the same
 // schedule as run_range (scores of tile i, then the output product of tile i-1 with the
 // softmax of tile i between its MFMAs), on raw tiles only, loads four tiles ahead.
+// kQ8 (cache format 3): the query rounded to E4M3 instead of split, scores on nine FP8
+// MFMAs (qk_tile_f8); everything else is the same.
+template <bool kQ8>
 __device__ __forceinline__ void run_range_split(const DecodeParams& p, uint32_t smem, int b, int n, int rg, int lt0,
                                                 int lt1, int64_t slot) {
   using PP = Pipe<kFmtFp8>;
@@ -1645,7 +1443,7 @@ __device__ __forceinline__ void run_range_split(const DecodeParams& p, uint32_t 
   const int my_row = kWaveRows * wave + lr;
   const int rc = min(row0 + my_row, p.rows - 1);  // rows past the end repeat the last row
   const int nt = lt1 - lt0;
-  i32x8 qh[9], ql[9];  // the query row, split (q_split)
+  i32x8 qh[9], ql[kQ8 ? 1 : 9];  // the query row, split (q_split) or rounded (q_round_e4m3, in qh)
   float c = 0.f;       // its score scale (set with the split)
 
   const int vis = max(n - p.q_len + rc / p.H + 1, 0);
@@ -1677,7 +1475,7 @@ __device__ __forceinline__ void run_range_split(const DecodeParams& p, uint32_t 
   };
   auto entry = [&](int i) { return table_entry(src, (lt0 + min(i, nt - 1)) * kTileTokens); };
   auto issue = [&](int i, int e) {
-    load_fp8_raw<2>(src, (lt0 + i) * kTileTokens, page_start(src, e), raw_buf(i), wave, lane);
+    load_fp8_raw(src, (lt0 + i) * kTileTokens, page_start(src, e), raw_buf(i), wave, lane);
   };
   int e_next = 0;
 
@@ -1689,7 +1487,9 @@ __device__ __forceinline__ void run_range_split(const DecodeParams& p, uint32_t 
       e_next = entry(i + PP::kAhead + 1);
     }
     if (!first && __any(alpha_prev != 1.f)) rescale(o, alpha_prev);
-    const f32x16 s = qk_tile_split(qh, ql, raw_buf(i), fq);
+    f32x16 s;
+    if constexpr (kQ8) s = qk_tile_f8(qh, raw_buf(i), fq);
+    else s = qk_tile_split(qh, ql, raw_buf(i), fq);
 #pragma unroll
     for (int v = 0; v < 16; ++v) x[v] = s[v];
     const int tbase = (lt0 + i) * kTileTokens;
@@ -1728,11 +1528,17 @@ __device__ __forceinline__ void run_range_split(const DecodeParams& p, uint32_t 
     for (int k = 0; k < pro; ++k) issue(k, entry(k));
     e_next = entry(PP::kAhead);
   }
-  const int sh = q_split(p.q + ((int64_t)b * p.rows + rc) * kLatent, p.qpe + ((int64_t)b * p.rows + rc) * kRope, lh,
-                         qh, ql);
-  // score scale of this row in log2 units, with the query's 2^sh taken out; kept positive
-  // (sm_scale = 0 gives the plain mean)
-  c = fmaxf(p.score_scale * __uint_as_float((unsigned)(127 - sh) << 23), 1e-37f);
+  const uint16_t* qrow = p.q + ((int64_t)b * p.rows + rc) * kLatent;
+  const uint16_t* prow = p.qpe + ((int64_t)b * p.rows + rc) * kRope;
+  if constexpr (kQ8) {
+    q_round_e4m3(qrow, prow, lh, qh);
+    c = fmaxf(p.score_scale, 1e-30f);  // sm_scale = 0 gives the plain mean
+  } else {
+    const int sh = q_split(qrow, prow, lh, qh, ql);
+    // score scale of this row in log2 units, with the query's 2^sh taken out; kept positive
+    // (sm_scale = 0 gives the plain mean)
+    c = fmaxf(p.score_scale * __uint_as_float((unsigned)(127 - sh) << 23), 1e-37f);
+  }
 
   if (nt > 0) {
     wait_vmcnt((pro - 1) * nloads);  // tile 0
@@ -1899,9 +1705,9 @@ void decode_paged_kernel(const DecodeParams p) {
     // these are the same in every lane (read from LDS words and tables that all lanes
     // share); saying so keeps the page addresses in scalar registers
     auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
-    if constexpr (FMT == kFmtFp8)
-      run_range_split(p, lds_addr((lds_ptr)smem), uni(b), uni(n), rg, uni(t - base + tf), uni(seg_end - base + tf),
-                      (int64_t)w + uni(b));
+    if constexpr (FMT == kFmtFp8 || FMT == kFmtFp8Q)
+      run_range_split<FMT == kFmtFp8Q>(p, lds_addr((lds_ptr)smem), uni(b), uni(n), rg, uni(t - base + tf),
+                                        uni(seg_end - base + tf), (int64_t)w + uni(b));
     else
       run_range<FMT, true>(p, lds_addr((lds_ptr)smem), uni(b), uni(n), rg, uni(t - base + tf),
                            uni(seg_end - base + tf), (int64_t)w + uni(b));
