@@ -134,7 +134,8 @@ int mla_decode_splitkv(const uint16_t* q, const uint16_t* qpe, const uint16_t* k
  *   o_part [rows, num_splits, 512] fp32, lse_part [rows, num_splits] fp32 (in)
  *   o      [rows, 512] bf16 (out, round-to-nearest-even)
  *   lse    [rows] fp32 (out; may be NULL)
- * Splits with lse_j = -inf are skipped (their o_part is not read).  rows >= 1,
+ * Splits with lse_j = -inf contribute nothing, whatever their o_part holds (NaN
+ * included; the buffer is still read, so it must span all rows x num_splits).  rows >= 1,
  * 1 <= num_splits <= 65536. */
 int mla_splitkv_combine(const float* o_part, const float* lse_part, int rows, int num_splits,
                         uint16_t* o, float* lse, void* stream);

@@ -1725,35 +1725,55 @@ void decode_paged_kernel(const DecodeParams p) {
 // combine kernels (one wavefront per output row)
 // ------------------------------------------------------------------------------------
 
-struct PartRef {
-  float lse;
-  const float* o;
-};
-
-// Merge ns partials of one row; part(j) returns (lse_j, pointer to O_j).
-// sink: an extra logit of the row that joins the denominator and carries no value
-// (-inf: none).
-template <class Part>
-__device__ __forceinline__ void combine_row(int ns, Part part, uint16_t* orow, float* lse_out, int lane,
+// Merge ns partials of one row; lse(j) returns lse_j (-inf for an empty or dead split)
+// and opart(j) the address of O_j.  sink: an extra logit of the row that joins the
+// denominator and carries no value (-inf: none).  Lane j % 64 holds lse_j, so the row's
+// maximum, LSE and weights take wavefront reductions; the O_j loads of a chunk of splits
+// are then issued back to back (their addresses do not depend on the weights), so a row
+// costs about two memory latencies whatever its split count.  An O_j of weight 0 (lse_j
+// = -inf, or too far below the row's LSE) is loaded but adds nothing, NaN included.
+template <class Lse, class OPart>
+__device__ __forceinline__ void combine_row(int ns, Lse lse, OPart opart, uint16_t* orow, float* lse_out, int lane,
                                             float sink = -INFINITY) {
-  float M = -INFINITY;
-  for (int j = lane; j < ns; j += 64) M = fmaxf(M, part(j).lse);
+  const float l0 = lane < ns ? lse(lane) : -INFINITY;  // the first 64 splits' lse, read once
+  float M = l0;
+  for (int j = lane + 64; j < ns; j += 64) M = fmaxf(M, lse(j));
   M = fmaxf(wave_max(M), sink);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float LSE = -INFINITY;
   if (M != -INFINITY) {
-    float den = 0.f;
-    for (int j = lane; j < ns; j += 64) den += expf(part(j).lse - M);
+    float den = expf(l0 - M);
+    for (int j = lane + 64; j < ns; j += 64) den += expf(lse(j) - M);
     den = wave_sum(den) + (sink != -INFINITY ? expf(sink - M) : 0.f);
     LSE = M + logf(den);
-    for (int j = 0; j < ns; ++j) {
-      const PartRef pj = part(j);
-      if (pj.lse == -INFINITY) continue;
-      const float wgt = expf(pj.lse - LSE);
-      const f32x4* src = reinterpret_cast<const f32x4*>(pj.o + 8 * lane);
-      const f32x4 a = src[0], b = src[1];
-      acc[0] += wgt * a[0]; acc[1] += wgt * a[1]; acc[2] += wgt * a[2]; acc[3] += wgt * a[3];
-      acc[4] += wgt * b[0]; acc[5] += wgt * b[1]; acc[6] += wgt * b[2]; acc[7] += wgt * b[3];
+    for (int j0 = 0; j0 < ns; j0 += 64) {
+      const int nc = min(ns - j0, 64);
+      const float lj = j0 == 0 ? l0 : (lane < nc ? lse(j0 + lane) : -INFINITY);
+      const float wl = expf(lj - LSE);  // weight of split j0 + lane
+      constexpr int kBatch = 4;
+      for (int jb = 0; jb < nc; jb += kBatch) {
+        f32x4 a[kBatch], b[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if (jb + u < nc) {
+            const f32x4* src = reinterpret_cast<const f32x4*>(opart(j0 + jb + u) + 8 * lane);
+            a[u] = src[0];
+            b[u] = src[1];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if (jb + u < nc) {
+            const float wgt = __shfl(wl, jb + u);
+            const bool on = wgt != 0.f;  // a weight-0 split adds nothing, whatever its O_j holds
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[e] += on ? wgt * a[u][e] : 0.f;
+              acc[4 + e] += on ? wgt * b[u][e] : 0.f;
+            }
+          }
+        }
+      }
     }
   }
   u32x4 packed;
@@ -1771,8 +1791,9 @@ __global__ __launch_bounds__(256) void combine_generic_kernel(const CombineParam
   if (row >= p.rows) return;
   const float* lses = p.lse_part + row * p.num_splits;
   const float* base = p.o_part + row * p.num_splits * kLatent;
-  auto part = [&](int j) { return PartRef{lses[j], base + (int64_t)j * kLatent}; };
-  combine_row(p.num_splits, part, p.o + row * kLatent, p.lse ? p.lse + row : nullptr, lane);
+  auto lse = [&](int j) { return lses[j]; };
+  auto opart = [&](int j) { return base + (int64_t)j * kLatent; };
+  combine_row(p.num_splits, lse, opart, p.o + row * kLatent, p.lse ? p.lse + row : nullptr, lane);
 }
 
 // paged: row (b, r) merges slots w + b for the non-empty ranges w in
@@ -1790,14 +1811,16 @@ __global__ __launch_bounds__(256) void combine_paged_kernel(const CombineParams 
     w0 = min(max(p.seg_first[b], 0), G - 1);
     w1 = min(max(p.seg_last[b], w0), G - 1);
   }
-  auto part = [&](int j) {
+  // a dead range (no tiles) wrote nothing: its lse counts as -inf (its slot is still
+  // inside the workspace, so the unused load of its O_j stays in bounds)
+  auto live = [&](int wj) { return ((int64_t)wj * W) / G < ((int64_t)(wj + 1) * W) / G; };  // range wj holds tiles
+  auto lse = [&](int j) {
     const int wj = w0 + j;
-    const bool live = ((int64_t)wj * W) / G < ((int64_t)(wj + 1) * W) / G;  // range wj holds tiles
-    const int64_t slot = (int64_t)wj + b;
-    return PartRef{live ? p.lse_part[slot * p.rows + r] : -INFINITY, p.o_part + (slot * p.rows + r) * kLatent};
+    return live(wj) ? p.lse_part[((int64_t)wj + b) * p.rows + r] : -INFINITY;
   };
+  auto opart = [&](int j) { return p.o_part + (((int64_t)w0 + j + b) * p.rows + r) * kLatent; };
   const float sink = p.sinks ? p.sinks[r % p.H] : -INFINITY;
-  combine_row(w1 - w0 + 1, part, p.o + grow * kLatent, p.lse ? p.lse + grow : nullptr, lane, sink);
+  combine_row(w1 - w0 + 1, lse, opart, p.o + grow * kLatent, p.lse ? p.lse + grow : nullptr, lane, sink);
 }
 
 // ------------------------------------------------------------------------------------
