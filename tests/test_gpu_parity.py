@@ -96,17 +96,20 @@ def test_contig_run_to_run_bitwise_stable():
         assert np.array_equal(x, y)
 
 
-def test_combine_matches_oracle_with_empty_splits():
-    say("combine generic")
-    rng = np.random.default_rng(4)
-    R, NS = 37, 9
+@pytest.mark.parametrize("R,NS", [(37, 9), (11, 150)])
+def test_combine_matches_oracle_with_empty_splits(R, NS):
+    """NS = 150 takes three rounds of 64 splits per row, the last one ragged."""
+    say(f"combine generic R={R} NS={NS}")
+    rng = np.random.default_rng(4 + NS)
     op = rng.standard_normal((R, NS, 512)).astype(np.float32)
     lp = (rng.standard_normal((R, NS)) * 3).astype(np.float32)
     lp[3, 2] = -np.inf
     lp[5, :] = -np.inf
     lp[7, :8] = -np.inf
-    op[3, 2] = np.nan   # a skipped split must not be read
+    lp[9, NS - 1] = -np.inf
+    op[3, 2] = np.nan   # a split with lse = -inf adds nothing, whatever its O holds
     op[5, :] = np.nan
+    op[9, NS - 1] = np.nan
     top = torch.from_numpy(op).to(DEV)
     tlp = torch.from_numpy(lp).to(DEV)
     o, lse = mla.splitkv_combine(top, tlp)
@@ -160,6 +163,19 @@ def test_paged_head_and_query_counts(H, q_len):
                        max_blocks=4)
     ro, rl = _paged_ref(w)
     o, lse = _paged_run(w)
+    assert max_err(o, ro) <= TOL_O_QUANT
+    assert max_err(lse, rl) <= TOL_LSE
+
+
+@pytest.mark.parametrize("ns", [None, 200])
+def test_paged_one_long_request_spans_every_range(ns):
+    """One 16000-token request beside a short one: the long request's rows merge one partial
+    per range (up to 256, several rounds of 64 in the combine)."""
+    say(f"paged one long request ns={ns}")
+    w = gen.make_paged(B=2, H=16, q_len=1, lo=1, hi=1, page_size=64, fmt=gen.FMT_FP8, seed=63,
+                       seq_lens=[16000, 40], max_blocks=250)
+    ro, rl = _paged_ref(w)
+    o, lse = _paged_run(w, ns)
     assert max_err(o, ro) <= TOL_O_QUANT
     assert max_err(lse, rl) <= TOL_LSE
 
