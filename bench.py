@@ -63,11 +63,11 @@ def algorithmic_counts(w):
     return flops, kv + qbytes + obytes + tbytes, kv
 
 
-def traffic_from_profiles(workload: str, src_hash: str):
+def traffic_from_profiles(workload: str, src_hash: str, kernel: str = "decode_paged"):
     """HBM bytes per decode launch (FETCH_SIZE and WRITE_SIZE, each scaled by what the
     counter reads for a copy kernel of known size) from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"decode_paged.{workload}.counters.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -179,14 +179,15 @@ def run_contig(args, w, mla, torch, np, gen):
     ms_step = (time.perf_counter() - t0) / args.steps * 1e3
     dec = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    traffic = traffic_from_profiles(args.workload, kernel_source_hash(), "decode_contig")
     if flops / nbytes >= ridge:
         a = flops / (dec * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(a, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+                "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic}
     else:
         a = nbytes / (dec * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(a / HBM_PEAK_GBPS, 4), "traffic": None}
+                "frac": round(a / HBM_PEAK_GBPS, 4), "traffic": traffic}
     out = {
         "metric": METRIC, "value": round(flops / (ms_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,

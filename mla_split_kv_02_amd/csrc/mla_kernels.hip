@@ -1728,10 +1728,10 @@ void decode_paged_kernel(const DecodeParams p) {
 // Merge ns partials of one row; lse(j) returns lse_j (-inf for an empty or dead split)
 // and opart(j) the address of O_j.  sink: an extra logit of the row that joins the
 // denominator and carries no value (-inf: none).  Lane j % 64 holds lse_j, so the row's
-// maximum, LSE and weights take wavefront reductions; the O_j loads of a chunk of splits
-// are then issued back to back (their addresses do not depend on the weights), so a row
-// costs about two memory latencies whatever its split count.  An O_j of weight 0 (lse_j
-// = -inf, or too far below the row's LSE) is loaded but adds nothing, NaN included.
+// maximum, LSE and weights take wavefront reductions instead of a serial walk; the O_j
+// loads then go out four splits at a time, back to back (their addresses do not depend
+// on the weights).  An O_j of weight 0 (lse_j = -inf, or too far below the row's LSE) is
+// loaded but adds nothing, NaN included.
 template <class Lse, class OPart>
 __device__ __forceinline__ void combine_row(int ns, Lse lse, OPart opart, uint16_t* orow, float* lse_out, int lane,
                                             float sink = -INFINITY) {
