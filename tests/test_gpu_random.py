@@ -3,6 +3,8 @@ size and stride, batch, lengths (including empty requests), sliding window, sink
 split count, each compared with the oracle on every output.  Each case prints its
 parameters before it runs."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -34,7 +36,8 @@ def _case(seed):
                 sinks=with_sinks, num_splits=ns, pad=pad, seed=seed)
 
 
-@pytest.mark.parametrize("seed", range(24))
+# MLA_RANDOM_CASES widens the sweep (default 24 cases)
+@pytest.mark.parametrize("seed", range(int(os.environ.get("MLA_RANDOM_CASES", "24"))))
 def test_random_paged_case_matches_oracle(seed):
     c = _case(seed)
     say(f"random case {c}")
