@@ -20,8 +20,8 @@
 // Per tile i (bf16, NVFP4): the global->LDS loads of a later tile are issued first; then
 // the scores of tile i, with the softmax of tile i-1 (whose scores stayed in registers)
 // spread between the score MFMAs, so the vector work issues while the matrix core is
-// busy; then the output product of tile i-1 (NVFP4 dequantises tile i+1 just before);
-// then one barrier.  The first tile's softmax and the last tile's output product come
+// busy; then the output product of tile i-1, with NVFP4's dequantisation of tile i+1
+// spread between its MFMAs in nine steps; then one barrier.  The first tile's softmax and the last tile's output product come
 // after the loop.
 //
 // FP8 cache (run_range_split): no tile is converted to bf16.  The bf16 query of each row
@@ -332,24 +332,41 @@ __device__ __forceinline__ void load_nvfp4_raw(const Src& S, int tb, const uint8
 // (t % 8) / 2 + 4m of the row: byte (t % 8) / 2 of scale dword m).  The hardware
 // converts the codes exactly to f32 (unit scale); the products have at most 6
 // significant bits, so their high halves are the exact bf16 values.
-__device__ __forceinline__ void dequant_nvfp4(uint32_t st, uint32_t tile, int tid) {
-  const int r = tid >> 3, t7 = tid & 7;
-  const uint32_t rd = st + 32 * r + 4 * t7;                                   // + 1024 m
-  const uint32_t sd = st + kNvRawData + 8 * r + (t7 >> 1);                    // + 256 (m/2) + 4 (m%2)
-  const uint32_t wr = tile + 128 * r + ((t7 ^ swz(r)) << 4);                  // + 4096 m
-#pragma unroll
-  for (int m = 0; m < 9; ++m) {
-    const unsigned w = *at<unsigned>(rd + 1024 * m);
-    const unsigned char sc = *at<unsigned char>(sd + 256 * (m >> 1) + 4 * (m & 1));
-    const float scale = __builtin_amdgcn_cvt_pk_f32_fp8((int)sc, false)[0];
-    const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-    const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-    const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-    const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+// The work is cut into nine steps, one per 4 KiB group m of the bf16 tile, so that the
+// output phase can spread them between its MFMAs: read(m) fetches the step's code dword
+// and scale byte, put(m) converts and writes them.
+struct NvDequant {
+  uint32_t rd, sd, wr;
+  unsigned w[9];
+  unsigned char sc[9];
+  __device__ __forceinline__ NvDequant(uint32_t st, uint32_t tile, int tid) {
+    const int r = tid >> 3, t7 = tid & 7;
+    rd = st + 32 * r + 4 * t7;                   // + 1024 m
+    sd = st + kNvRawData + 8 * r + (t7 >> 1);    // + 256 (m/2) + 4 (m%2)
+    wr = tile + 128 * r + ((t7 ^ swz(r)) << 4);  // + 4096 m
+  }
+  __device__ __forceinline__ void read(int m) {
+    w[m] = *at<unsigned>(rd + 1024 * m);
+    sc[m] = *at<unsigned char>(sd + 256 * (m >> 1) + 4 * (m & 1));
+  }
+  __device__ __forceinline__ void put(int m) {
+    const float scale = __builtin_amdgcn_cvt_pk_f32_fp8((int)sc[m], false)[0];
+    const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[m], 1.0f, 0);
+    const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[m], 1.0f, 1);
+    const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[m], 1.0f, 2);
+    const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[m], 1.0f, 3);
     *at<u32x4>(wr + kGroupBytes * m) =
         u32x4{pack_hi16(f0[0] * scale, f0[1] * scale), pack_hi16(f1[0] * scale, f1[1] * scale),
               pack_hi16(f2[0] * scale, f2[1] * scale), pack_hi16(f3[0] * scale, f3[1] * scale)};
   }
+};
+
+__device__ __forceinline__ void dequant_nvfp4(uint32_t st, uint32_t tile, int tid) {
+  NvDequant d(st, tile, tid);
+#pragma unroll
+  for (int m = 0; m < 9; ++m) d.read(m);
+#pragma unroll
+  for (int m = 0; m < 9; ++m) d.put(m);
 }
 
 // ------------------------------------------------------------------------------------
@@ -899,7 +916,10 @@ __device__ __forceinline__ f32x16 qk_softmax_tile(const bf16x8* q, uint32_t tile
 
 // Output product of tile i-1 (vtile, P^T in pp): 32 MFMAs, V^T from the transpose reads
 // four MFMAs ahead (bf16 and NVFP4 caches; the softmax ran in the score block).
-__device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const unsigned* pp, const int* vb) {
+// nv: the NVFP4 dequantisation of the next tile, spread over the MFMAs (step m after
+// MFMA 3m + 2, its reads two steps earlier); null for the other formats.
+__device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const unsigned* pp, const int* vb,
+                                             NvDequant* nv = nullptr) {
   constexpr int kAhead = 4;
   uint32_t base[4];
 #pragma unroll
@@ -916,11 +936,19 @@ __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const un
   bf16x8 va[2 * kDimBlocks];
 #pragma unroll
   for (int k = 0; k < kAhead; ++k) va[k] = tr(k);
+  if (nv) {
+    nv->read(0);
+    nv->read(1);
+  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int k = 0; k < 2 * kDimBlocks; ++k) {
     o[k & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k], (k < kDimBlocks) ? pb0 : pb1, o[k & 15], 0, 0, 0);
     if (k + kAhead < 2 * kDimBlocks) va[k + kAhead] = tr(k + kAhead);
+    if (nv && k % 3 == 2 && k / 3 < 9) {
+      nv->put(k / 3);
+      if (k / 3 + 2 < 9) nv->read(k / 3 + 2);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -1371,9 +1399,16 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
         x[v] = (t < lim && t >= flo) ? x[v] : -INFINITY;
       }
     }
-    // past the last tile the dequantisation only rewrites an unused buffer
-    if (FMT == kFmtNvfp4) dequant(i + 1);
-    if (!first) output_phase(o, tile_buf(i - 1), pp, vb);
+    // past the last tile the dequantisation only rewrites an unused buffer; after the
+    // first tile it runs spread over the output phase
+    if (first) {
+      if (FMT == kFmtNvfp4) dequant(i + 1);
+    } else if constexpr (FMT == kFmtNvfp4) {
+      NvDequant nv(raw_buf(i + 1), tile_buf(i + 1), tid);
+      output_phase(o, tile_buf(i - 1), pp, vb, &nv);
+    } else {
+      output_phase(o, tile_buf(i - 1), pp, vb);
+    }
     // the loads the next tile depends on: bf16 tile i+1 (issued one tile ago), raw NVFP4
     // tile i+2 (one tile ago)
     wait_vmcnt(more ? nloads : 0);
