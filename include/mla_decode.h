@@ -81,8 +81,10 @@ typedef enum {
   /* Same page bytes and kv_scale as MLA_KV_FP8_E4M3, with the query rounded to E4M3
    * (nearest, ties to even, saturating at 448) and the score product on FP8 matrix cores,
    * as the TokenSpeed page's FP8 decode does (forward_decode: the query is cast to the
-   * cache's FP8 type and k_scale is folded into the softmax scale).  The output product
-   * still runs in bf16 on the exactly dequantised latent. */
+   * cache's FP8 type and k_scale is folded into the softmax scale).  The output product is
+   * that of MLA_KV_FP8_E4M3: the softmax weights, scaled per row and 32-token tile by a
+   * power of two, as two E4M3 terms (about 8 significant bits) against the raw cache codes
+   * on FP8 matrix cores, with fp32 accumulation. */
   MLA_KV_FP8_E4M3_QFP8 = 3
 } mla_kv_format;
 

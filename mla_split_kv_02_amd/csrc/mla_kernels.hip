@@ -27,12 +27,13 @@
 // FP8 cache (run_range_split): no tile is converted to bf16.  The bf16 query of each row
 // is split exactly into two E4M3 operands (hi + lo, after a power-of-two row scale), so
 // the scores run on FP8 MFMA 32x32x64 straight from the raw tile, each K operand read
-// once for both halves (18 MFMAs per tile).  The softmax weights are split the same way
-// (about 8 significant bits, like bf16), and the output product takes the raw tile's V^T
-// through the 8-bit LDS transpose read: one MFMA 32x32x64 per 32 dims whose K = 64 holds
-// the tile's 32 tokens twice, with P_hi in the low lane half and P_lo in the high half
-// (16 MFMAs per tile).  The matrix-core time per token is that of the bf16 path; the LDS
-// traffic per tile drops from about 290 to 200 KiB and the dequantisation pass is gone.
+// once for both halves (18 MFMAs per tile).  The softmax weights of each row and tile are
+// scaled by a power of two 2^e that puts the tile's largest at 2^7..2^8 and split the
+// same way (about 8 significant bits, like bf16), and the output product takes the raw
+// tile's V^T through the 8-bit LDS transpose read: one scaled MFMA 32x32x64 per 32 dims
+// whose first 32-element scale block holds the tile's tokens with P_hi and whose second
+// holds them with P_lo, both with the row's E8M0 scale 2^-e (16 MFMAs per tile).  The
+// matrix-core time per token is that of the bf16 path, and no tile is converted to bf16.
 //
 // Paged ranges are balanced by cost: a request costs its tiles plus a fixed overhead for
 // its segment's query load, pipeline fill and partial store (decode_paged_kernel).
@@ -599,9 +600,14 @@ __device__ __forceinline__ void pv_tile(f32x16* o, uint32_t tile, const unsigned
   }
 }
 
+// Wait states before the accumulators may be read after an MFMA issued as an assembly
+// statement (the FP8 split path's output product), which the compiler cannot see.
+__device__ __forceinline__ void mfma_drain_any() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
 // o *= alpha in place in the accumulation registers, one value at a time through one
 // vector register.
 __device__ __forceinline__ void rescale(f32x16* o, float alpha) {
+  mfma_drain_any();
 #pragma unroll
   for (int db = 0; db < kDimBlocks; ++db)
 #pragma unroll
@@ -966,12 +972,15 @@ __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const un
 // most 2^-10 after scaling, under 2^-17 of the row's largest.
 //   scores  S^T = K . (Q_hi + Q_lo)^T: 9 K-steps of 64 dims, each raw K operand read from
 //           LDS once and used by two MFMA 32x32x64 (hi, then lo)
-//   output  O^T += V^T . (P_hi + P_lo)^T over a 32-token tile: one MFMA 32x32x64 per 32
-//           dims, whose K = 64 is the tile's 32 tokens twice: the low lane half carries
-//           V^T with P_hi, the high half the same V^T with P_lo.  V^T is read from the raw
-//           tile with the 8-bit LDS transpose read, so no tile is ever converted to bf16.
-// The softmax weights are split the same way (P = hi + lo to about 8 significant bits,
-// like bf16); they are kept at most 2^8 (lazy rescale), within E4M3's range.
+//   output  O^T += V^T . (P_hi + P_lo)^T 2^-e over a 32-token tile: one scaled MFMA
+//           32x32x64 per 32 dims, whose K = 64 is the tile's 32 tokens twice: its first
+//           scale block pairs V^T with P_hi, its second the same V^T with P_lo (see
+//           split_vt_offsets for the operand layout).  V^T is read from the raw tile with
+//           the 8-bit LDS transpose read, so no tile is ever converted to bf16.
+// The softmax weights are split the same way after a per-row, per-tile power-of-two
+// scale 2^e that puts the tile's largest weight in [2^7, 2^8) (split_piece): P' = hi + lo
+// to about 8 significant bits, like bf16, within E4M3's range, and the output MFMA's E8M0
+// operand scale takes 2^e out again.
 // ------------------------------------------------------------------------------------
 
 // two floats -> two E4M3 codes (nearest, ties to even) in half-word `hw` of w
@@ -1138,50 +1147,95 @@ __device__ __forceinline__ f32x16 qk_tile_split(const i32x8* qh, const i32x8* ql
   return s;
 }
 
-// V^T operand of output MFMA db from the raw tile: dims 32 db + l % 32, tokens 0..31 as
-// bytes 0..31, in both lane halves.  Four 8-bit transpose reads, read t covering tokens
-// 8t .. 8t+7: in each 16-lane group g, lane s addresses token 8t + s / 2 and dims
-// 32 db + 16 (g % 2) + 8 (s % 2) .. + 8 (raw chunk 2 db + g % 2, whose position in the
-// row is swizzled with sswz), and lane j receives dim 32 db + 16 (g % 2) + j of the 8
-// tokens.  vs[2t + (db & 1)] is the lane's offset inside chunk group db / 2 (odd blocks
-// flip position bit 1, byte-offset bit 5).
+// Operand layout of MFMA 32x32x64 with 8-bit operands (probed on the box with one-hot
+// operands and distinct E8M0 scales): byte t of lane half h is element
+// k = 32 (t / 16) + 16 h + t % 16, so bytes 0..15 of both halves form the first 32-element
+// scale block and bytes 16..31 the second; the scale of block b for row (A) or column
+// (B) j comes from lane 32 b + j.
+//
+// Output product of the split path: per 32 dims, one MFMA whose first scale block holds
+// the tile's 32 tokens with P_hi and whose second block holds the same tokens with P_lo,
+// so A = V^T carries each token twice (bytes t and t + 16) and B = [hi codes | lo codes].
+// The tokens of lane half h are the 16 whose scores that half already holds (tokens
+// 4h + 8g + r, g, r = 0..3, in the scores' register order), so P needs no lane exchange.
+// V^T of output MFMA db (dims 32 db + l % 32) takes two 8-bit transpose reads per lane:
+// read t covers tokens 4h + 16t + {0..3, 8..11}; in each 16-lane group g, lane s addresses
+// token 4h + 16t + u % 4 + 8 (u / 4), u = s / 2, and dims 32 db + 16 (g % 2) + 8 (s % 2)
+// .. + 8 (raw chunk 2 db + g % 2, whose position in the row is swizzled with sswz), and
+// lane j receives dim 32 db + 16 (g % 2) + j of the 8 tokens.  vs[2t + (db & 1)] is the
+// lane's offset inside chunk group db / 2 (odd blocks flip position bit 1, byte-offset
+// bit 5).
 __device__ __forceinline__ void split_vt_offsets(int lane, int* vs) {
-  const int g = lane >> 4, s = lane & 15;
+  const int g = lane >> 4, s = lane & 15, h = lane >> 5, u = s >> 1;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int tok = 8 * t + (s >> 1);
+  for (int t = 0; t < 2; ++t) {
+    const int tok = 4 * h + 16 * t + (u & 3) + 8 * (u >> 2);
     const int off = 64 * tok + 16 * ((g & 1) ^ sswz(tok)) + 8 * (s & 1);
     vs[2 * t] = off;
     vs[2 * t + 1] = off ^ 32;
   }
 }
-__device__ __forceinline__ i32x8 split_vt_read(const uint32_t* base, int db) {
+// base[0..3]: the four offsets above plus the tile; dup[0..3]: the same addresses in
+// other registers (opaque to the compiler), so that the second copy of each operand half
+// is a load of its own straight into its registers rather than a register copy.
+__device__ __forceinline__ i32x8 split_vt_read(const uint32_t* base, const uint32_t* dup, int db) {
   i32x2 r[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < 2; ++t) {
     r[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(at<i32x2>(base[2 * t + (db & 1)] + 2048 * (db >> 1)));
+    r[2 + t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(at<i32x2>(dup[2 * t + (db & 1)] + 2048 * (db >> 1)));
+  }
   return i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
 }
-
-__device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
 }
+
+// Output MFMA of the split path, c += V^T . P'^T: A = V^T codes at unit scale (E8M0
+// 127 in ua), B = P'^T codes with this lane's E8M0 scale sb.  Written as an assembly
+// statement, which stays where the schedule puts it (the compiler sinks the builtin
+// form past the softmax work it is meant to interleave with).  Hazards the compiler
+// cannot see: a vector instruction writing an operand needs two wait states before the
+// MFMA reads it (NOP: the first MFMA of a phase, whose P operand may just have been
+// assembled), and a read of the accumulators after the last MFMA waits for it
+// (mfma_drain).
+template <bool NOP = false>
+__device__ __forceinline__ void mfma_f8s(f32x16& c, const i32x8& a, const i32x8& b, int ua, int sb) {
+  if (NOP)
+    asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+                 : "+a"(c) : "v"(a), "v"(b), "v"(ua), "v"(sb));
+  else
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+                 : "+a"(c) : "v"(a), "v"(b), "v"(ua), "v"(sb));
+}
+// wait states (more than the 16-pass MFMA's 19) before an accumulator may be read
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 // Online softmax of one tile for the split path, in 16 pieces (one per output MFMA).  x:
 // raw scores of this lane (row l % 32, tokens 8 (v / 4) + 4 (l / 32) + v % 4), masked ones
 // -inf; c > 0 the row's score scale in log2 units.  Weights are p = 2^(x c - m) with the
 // reference m moved only when the tile's max exceeds it by more than 8, and then to
 // that max - 1, so p <= 2^8 and the row's max may grow by 7 before the accumulators
-// need rescaling (any row of the wavefront then rescales all 256 accumulators).  Output: alpha (factor for the accumulators before this tile's
-// product) and P^T in pn: dwords 2j, 2j+1 hold tokens 8j .. 8j+3, 8j+4 .. 8j+7, as the
-// codes of P_hi in the low lane half and of P_lo in the high half.
+// need rescaling (any row of the wavefront then rescales all 256 accumulators).
+// Each row's weights of the tile are carried as p' = p 2^e, with the integer e chosen so
+// that the tile's largest p' lies in [2^7, 2^8): p' = hi + lo, hi and lo E4M3, so every
+// weight within 2^-8 of the tile's largest keeps 8 significant bits and smaller ones an
+// absolute error of at most 2^-10, i.e. 2^-17 of the tile's largest, however far the tile
+// lies below the row's reference.  The output MFMA undoes 2^e with the B operand's E8M0
+// scale.
+// Output: alpha (factor for the accumulators before this tile's product), P'^T in pn
+// (dwords 0..3: the hi codes of the lane's 16 values in register order, dwords 4..7 their
+// lo codes: the output MFMA's two scale blocks) and sb, the E8M0 code of 2^-e (the low
+// lane half gives the hi block's scale, the high half the lo block's: the same).
 struct SplitPieces {
-  float mt, m_new, ex, nm, acc;
+  float mt, m_new, ex, nm, acc, esc;
   bool need;
   unsigned h[4], l[4];  // dword j: codes of values 4j .. 4j+3
 };
 __device__ __forceinline__ void split_piece(int k, Softmax& S, float* x, float c, SplitPieces& w, unsigned* pn,
-                                            float& alpha) {
+                                            float& alpha, int& sb) {
   auto split4 = [&](int j) {  // values 4j .. 4j+3 -> dword j of the hi and lo codes
     unsigned hc = 0, lc = 0;
     e4m3_split_pair<false>(hc, lc, x[4 * j], x[4 * j + 1]);
@@ -1204,7 +1258,13 @@ __device__ __forceinline__ void split_piece(int k, Softmax& S, float* x, float c
     alpha = (w.need && S.m_used != -INFINITY) ? w.ex : 1.0f;
     S.l_sum *= alpha;
     S.m_used = w.m_new;
-    w.nm = (w.m_new == -INFINITY) ? 0.f : -w.m_new;
+    // e = 7 - floor(tile max - reference), within [-1, 100]; a row with no visible token
+    // in this tile (mt = -inf, NaN difference) takes the bound, its weights are all 0
+    const float d = fmaxf(w.mt - w.m_new, -100.0f);
+    const int e = min(7 - (int)floorf(d), 100);
+    w.esc = __uint_as_float((unsigned)(127 - e) << 23);  // 2^-e
+    w.nm = (w.m_new == -INFINITY) ? 0.f : (float)e - w.m_new;
+    sb = 127 - e;
     w.acc = 0.f;
   } else if (k >= 5 && k < 13) {
     const int v = 2 * (k - 5);
@@ -1217,58 +1277,73 @@ __device__ __forceinline__ void split_piece(int k, Softmax& S, float* x, float c
     if (k == 12) split4(2);
   } else if (k == 13) {
     split4(3);
-    S.l_sum += w.acc;
-  } else if (k == 14 || k == 15) {
+    S.l_sum = fmaf(w.acc, w.esc, S.l_sum);  // sum of p = 2^-e sum of p'
+  } else if (k == 14) {
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int j = 2 * (k - 14) + jj;
-      const auto r = __builtin_amdgcn_permlane32_swap(w.h[j], w.l[j], false, false);
-      pn[2 * j] = r[0];
-      pn[2 * j + 1] = r[1];
+    for (int j = 0; j < 4; ++j) {
+      pn[j] = w.h[j];
+      pn[4 + j] = w.l[j];
     }
   }
 }
 
-// Output product of tile i-1 (raw tile `raw`, P^T in pp) for the split path, with the
-// softmax of tile i in pieces between its 16 MFMAs; V^T reads run kAhead MFMAs ahead.
+// Output product of tile i-1 (raw tile `raw`, P'^T in pp with B scales sbp) for the split
+// path, with the softmax of tile i in pieces between its 16 MFMAs; V^T reads run kAhead
+// MFMAs ahead.
 template <int kAhead>
-__device__ __forceinline__ void output_phase_split(f32x16* o, uint32_t raw, const unsigned* pp, const int* vs,
-                                                   float* x, Softmax& S, float c, unsigned* pn, float& alpha) {
-  uint32_t base[8];
+__device__ __forceinline__ void output_phase_split(f32x16* o, uint32_t raw, const unsigned* pp, int sbp,
+                                                   const int* vs, float* x, Softmax& S, float c, unsigned* pn,
+                                                   float& alpha, int& sb) {
+  uint32_t base[4], dup[4];
 #pragma unroll
-  for (int v = 0; v < 8; ++v) base[v] = raw + vs[v];
+  for (int v = 0; v < 4; ++v) {
+    base[v] = raw + vs[v];
+    dup[v] = opaque(base[v]);
+  }
   const i32x8 pb = {(int)pp[0], (int)pp[1], (int)pp[2], (int)pp[3], (int)pp[4], (int)pp[5], (int)pp[6], (int)pp[7]};
+  const int ua = 127;
   SplitPieces w;
   i32x8 va[kDimBlocks];
 #pragma unroll
-  for (int k = 0; k < kAhead; ++k) va[k] = split_vt_read(base, k);
+  for (int k = 0; k < kAhead; ++k) va[k] = split_vt_read(base, dup, k);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int k = 0; k < kDimBlocks; ++k) {
-    o[k] = mfma_f8(va[k], pb, o[k]);
-    if (k + kAhead < kDimBlocks) va[k + kAhead] = split_vt_read(base, k + kAhead);
-    split_piece(k, S, x, c, w, pn, alpha);
+    if (k == 0) mfma_f8s<true>(o[k], va[k], pb, ua, sbp);
+    else mfma_f8s(o[k], va[k], pb, ua, sbp);
+    if (k + kAhead < kDimBlocks) va[k + kAhead] = split_vt_read(base, dup, k + kAhead);
+    split_piece(k, S, x, c, w, pn, alpha, sb);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // The softmax of one tile on its own (the first tile of a range).
-__device__ __forceinline__ float softmax_split(Softmax& S, float* x, float c, unsigned* pn) {
+__device__ __forceinline__ float softmax_split(Softmax& S, float* x, float c, unsigned* pn, int& sb) {
   SplitPieces w;
   float alpha = 1.f;
 #pragma unroll
-  for (int k = 0; k < kDimBlocks; ++k) split_piece(k, S, x, c, w, pn, alpha);
+  for (int k = 0; k < kDimBlocks; ++k) split_piece(k, S, x, c, w, pn, alpha, sb);
   return alpha;
 }
 
-// The output product of one tile on its own (the last tile of a range).
-__device__ __forceinline__ void pv_split(f32x16* o, uint32_t raw, const unsigned* pp, const int* vs) {
-  uint32_t base[8];
+// The output product of one tile on its own (the last tile of a range); the accumulators
+// may be read right after it.
+__device__ __forceinline__ void pv_split(f32x16* o, uint32_t raw, const unsigned* pp, int sbp, const int* vs) {
+  uint32_t base[4], dup[4];
 #pragma unroll
-  for (int v = 0; v < 8; ++v) base[v] = raw + vs[v];
+  for (int v = 0; v < 4; ++v) {
+    base[v] = raw + vs[v];
+    dup[v] = opaque(base[v]);
+  }
   const i32x8 pb = {(int)pp[0], (int)pp[1], (int)pp[2], (int)pp[3], (int)pp[4], (int)pp[5], (int)pp[6], (int)pp[7]};
+  const int ua = 127;
 #pragma unroll
-  for (int db = 0; db < kDimBlocks; ++db) o[db] = mfma_f8(split_vt_read(base, db), pb, o[db]);
+  for (int db = 0; db < kDimBlocks; ++db) {
+    const i32x8 va = split_vt_read(base, dup, db);
+    if (db == 0) mfma_f8s<true>(o[db], va, pb, ua, sbp);
+    else mfma_f8s(o[db], va, pb, ua, sbp);
+  }
+  mfma_drain();
 }
 
 // ------------------------------------------------------------------------------------
@@ -1493,7 +1568,7 @@ __device__ __forceinline__ void run_range_split(const DecodeParams& p, uint32_t 
   uint32_t fq[2];  // score reads: chunks 2h, 2h+1 of token row l % 32 (as in qk_tile_f8, swizzled with sswz)
 #pragma unroll
   for (int e = 0; e < 2; ++e) fq[e] = 64 * lr + 16 * ((2 * lh + e) ^ sswz(lr));
-  int vs[8];
+  int vs[4];
   split_vt_offsets(lane, vs);
 
   f32x16 o[kDimBlocks];
@@ -1501,6 +1576,7 @@ __device__ __forceinline__ void run_range_split(const DecodeParams& p, uint32_t 
   for (int db = 0; db < kDimBlocks; ++db) o[db] = f32x16{};
   Softmax S{-INFINITY, 0.f, 0.f};
   unsigned pp[8];
+  int sb_prev = 127;  // B operand scales of pp
   float alpha_prev = 1.f;
 
   const Src src{&p, b, n};
@@ -1539,10 +1615,12 @@ __device__ __forceinline__ void run_range_split(const DecodeParams& p, uint32_t 
     }
     unsigned pn[8];
     float alpha = 1.f;
-    if (first) alpha = softmax_split(S, x, c, pn);
-    else output_phase_split<2>(o, raw_buf(i - 1), pp, vs, x, S, c, pn, alpha);
+    int sbn = 127;
+    if (first) alpha = softmax_split(S, x, c, pn, sbn);
+    else output_phase_split<2>(o, raw_buf(i - 1), pp, sb_prev, vs, x, S, c, pn, alpha, sbn);
 #pragma unroll
     for (int k = 0; k < 8; ++k) pp[k] = pn[k];
+    sb_prev = sbn;
     alpha_prev = alpha;
     // tile i+1 must have landed (its loads were issued kAhead - 1 tiles ago); the loads of
     // the tiles after it may stay in flight (near the end of the range: wait for all)
@@ -1581,7 +1659,7 @@ __device__ __forceinline__ void run_range_split(const DecodeParams& p, uint32_t 
     body(0, std::true_type{});
     for (int i = 1; i < nt; ++i) body(i, std::false_type{});
     if (__any(alpha_prev != 1.f)) rescale(o, alpha_prev);
-    pv_split(o, raw_buf(nt - 1), pp, vs);
+    pv_split(o, raw_buf(nt - 1), pp, sb_prev, vs);
   }
 
   // ---- epilogue: normalised partial O and its lse (normalised by the unrounded sum) ----

@@ -69,6 +69,14 @@ def max_err(got: np.ndarray, want: np.ndarray) -> float:
     return Err(float(d[i]), f"at {tuple(int(x) for x in i)} got {got[i]:.6g} want {want[i]:.6g}")
 
 
+def check(what: str, got: np.ndarray, want: np.ndarray, tol: float):
+    """Assert max |got - want| <= tol, and print the margin (it shows in the test log)."""
+    e = max_err(got, want)
+    say(f"  {what}: max|d|={float(e):.3e} tol={tol:.0e} ({float(e) / tol:.2f} of tol)")
+    assert e <= tol, (what, e)
+    return e
+
+
 def paged_device_inputs(w, dev="cuda:0"):
     return dict(q=bf16_dev(w.q, dev), qpe=bf16_dev(w.qpe, dev), cache=u8_dev(w.cache, dev),
                 bt=i32_dev(w.block_tables, dev), sl=i32_dev(w.seq_lens, dev))

@@ -12,7 +12,7 @@ import torch
 import oracle
 import mla_split_kv_02_amd as mla
 from workloads import gen
-from gpu_util import (TOL_LSE, TOL_O_BF16, TOL_O_QUANT, bf16_dev, host, i32_dev, max_err,
+from gpu_util import (TOL_LSE, TOL_O_BF16, TOL_O_QUANT, bf16_dev, check, host, i32_dev, max_err,
                       paged_device_inputs, say, u8_dev)
 
 pytestmark = pytest.mark.gpu
@@ -313,6 +313,46 @@ def test_paged_fp8_rising_scores(q_len, page_size):
         o, lse = _paged_run(w, ns)
         assert max_err(o, ro) <= TOL_O_QUANT, ns
         assert max_err(lse, rl) <= TOL_LSE, ns
+
+
+@pytest.mark.parametrize("fmt", [gen.FMT_FP8, oracle.FMT_FP8_QFP8])
+@pytest.mark.parametrize("where", ["first", "middle"])
+def test_paged_fp8_dominant_token_over_long_tail(fmt, where):
+    """One token scores 6-15 (natural units, by head) above a flat bulk of 32768 and 20000
+    latent rows of mean 1, so that each bulk weight is 2^-9 .. 2^-21 of the dominant
+    one while the bulk's total weight still rivals it.  The FP8 paths carry each
+    tile's weights with their own power-of-two scale, so the bulk keeps its weight in
+    both the numerator and the denominator; losing it in either shifts O by up to 1."""
+    say(f"paged fp8 dominant token ({where}) over a long tail, fmt={fmt}")
+    w = gen.make_paged(B=2, H=128, q_len=1, lo=1, hi=1, page_size=64, fmt=gen.FMT_FP8, seed=67,
+                       seq_lens=[32768, 20000])
+    rng = np.random.default_rng(11)
+    pages = w.cache.reshape(w.num_pages, w.page_stride)
+    rows, star = {}, {}
+    for b in range(w.B):
+        n = int(w.seq_lens[b])
+        u = rng.choice(np.array([-1.0, 1.0], dtype=np.float32), size=576)
+        r = rng.standard_normal((gen.cdiv(n, 64) * 64, 576), dtype=np.float32) + np.float32(1.0)
+        t = 0 if where == "first" else n // 2 + 17
+        r[t] = u
+        rows[b], star[b] = r, u
+    w.kv_scale = float(np.float32(max(float(np.abs(r).max()) for r in rows.values())) / np.float32(448.0))
+    for b in range(w.B):
+        npg = rows[b].shape[0] // 64
+        pages[w.block_tables[b, :npg]] = gen.encode_pages(rows[b], gen.FMT_FP8, 64, w.page_stride, w.kv_scale)
+    alpha = np.linspace(0.14, 0.35, w.H, dtype=np.float32)  # per head
+    q = np.empty((w.B, 1, w.H, 576), dtype=np.float32)
+    for b in range(w.B):
+        q[b, 0] = alpha[:, None] * star[b][None, :]
+    w.q = gen.to_bf16_bits(q[..., :512])
+    w.qpe = gen.to_bf16_bits(q[..., 512:])
+    w.fmt = fmt
+    ro, rl = _paged_ref(w)
+    # the bulk carries a large share of the weight in most heads
+    for ns in (None, 1):
+        o, lse = _paged_run(w, ns)
+        check(f"O ns={ns}", o, ro, TOL_O_QUANT)
+        check(f"LSE ns={ns}", lse, rl, TOL_LSE)
 
 
 # ----------------------------------------------------------------------------------
