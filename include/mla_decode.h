@@ -52,13 +52,17 @@ extern "C" {
 #define MLA_MAX_Q_LEN 8        /* query tokens per request (TokenSpeed page: q_len capacity 8) */
 #define MLA_MAX_BATCH 4096     /* requests per paged call */
 #define MLA_MAX_SPLITS 65536   /* num_splits of a paged call */
+/* Size of the built-in workspace of mla_paged_decode_noalloc (128 MiB per GPU). */
+#define MLA_NOALLOC_SCRATCH_BYTES (128u << 20)
 
 typedef enum {
   MLA_OK = 0,
   MLA_ERR_INVALID_ARG = -1,         /* null pointer, bad size, misalignment, bad split */
   MLA_ERR_UNSUPPORTED = -2,         /* format, page size, head count or q_len not built */
   MLA_ERR_WORKSPACE_TOO_SMALL = -3, /* workspace_bytes below mla_paged_workspace_bytes */
-  MLA_ERR_HIP = -4                  /* a kernel launch failed */
+  MLA_ERR_HIP = -4,                 /* a kernel launch failed */
+  MLA_ERR_SCRATCH_LIMIT = -5        /* mla_paged_decode_noalloc: the problem needs more
+                                       workspace than MLA_NOALLOC_SCRATCH_BYTES */
 } mla_status;
 
 /* Cache formats of the paged op.
@@ -211,6 +215,25 @@ int mla_paged_decode_ext(const uint16_t* q, const uint16_t* qpe, const void* kv_
                          const int32_t* seq_lens, int B, int q_len, int H, float sm_scale,
                          int sliding_window, const float* sinks, int num_splits, void* workspace,
                          size_t workspace_bytes, uint16_t* o, float* lse, void* stream);
+
+/* mla_paged_decode for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments,
+ * checks and results, without workspace arguments.  The workspace is a 256-byte aligned
+ * array of MLA_NOALLOC_SCRATCH_BYTES in the library's own device memory, one per GPU,
+ * held from the first call on that GPU until the process ends; its device address is
+ * looked up once per GPU (the GPU of `stream`, or the current one for a null stream).
+ * The call allocates nothing.  The problem's workspace, mla_paged_workspace_bytes(B,
+ * q_len, H, num_splits), must fit: otherwise it returns MLA_ERR_SCRATCH_LIMIT (for
+ * B = 64, q_len = 1, H = 128 and 256 splits it is 84 MB; for B = 128, q_len = 2, H = 128
+ * and 128 splits, 134 MB).  Every call on one GPU shares that GPU's array, and the array
+ * keeps the last call's contents, which the next call does not need: calls that overlap
+ * on one GPU (on different streams, or from different threads) race and must not be
+ * issued. */
+int mla_paged_decode_noalloc(const uint16_t* q, const uint16_t* qpe, const void* kv_cache, int fmt,
+                             float kv_scale, int num_pages, int page_size, int64_t page_stride_bytes,
+                             const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* seq_lens, int B, int q_len, int H, float sm_scale,
+                             int num_splits, uint16_t* o, float* lse, void* stream);
 
 /* KV-cache append: store T new tokens into the paged pool before decoding them
  * (TokenSpeed page, forward_decode: each new token's latent and rope key are written into

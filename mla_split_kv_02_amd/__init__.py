@@ -10,12 +10,14 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     MLA_ERR_HIP,
     MLA_ERR_INVALID_ARG,
+    MLA_ERR_SCRATCH_LIMIT,
     MLA_ERR_UNSUPPORTED,
     MLA_ERR_WORKSPACE_TOO_SMALL,
     MLA_KV_BF16,
     MLA_KV_FP8_E4M3,
     MLA_KV_FP8_E4M3_QFP8,
     MLA_KV_NVFP4,
+    MLA_NOALLOC_SCRATCH_BYTES,
     MLA_OK,
     EXPORTED_SYMBOLS,
     MlaError,
@@ -25,6 +27,7 @@ from ._lib import (  # noqa: F401
     kv_append,
     lib,
     paged_decode,
+    paged_decode_noalloc,
     paged_workspace,
     paged_workspace_bytes,
     plan_contig,

@@ -21,6 +21,8 @@ MLA_ERR_INVALID_ARG = -1
 MLA_ERR_UNSUPPORTED = -2
 MLA_ERR_WORKSPACE_TOO_SMALL = -3
 MLA_ERR_HIP = -4
+MLA_ERR_SCRATCH_LIMIT = -5
+MLA_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3 = 1
@@ -42,6 +44,7 @@ EXPORTED_SYMBOLS = (
     "mla_paged_combine",
     "mla_paged_decode",
     "mla_paged_decode_ext",
+    "mla_paged_decode_noalloc",
     "mla_kv_append",
 )
 
@@ -90,6 +93,9 @@ def lib() -> ctypes.CDLL:
     L.mla_paged_decode_ext.restype = c_int
     L.mla_paged_decode_ext.argtypes = [vp, vp, vp, c_int, c_float, c_int, c_int, c_i64, vp, c_int, vp, c_int, c_int,
                                        c_int, c_float, c_int, vp, c_int, vp, c_size, vp, vp, vp]
+    L.mla_paged_decode_noalloc.restype = c_int
+    L.mla_paged_decode_noalloc.argtypes = [vp, vp, vp, c_int, c_float, c_int, c_int, c_i64, vp, c_int, vp, c_int,
+                                           c_int, c_int, c_float, c_int, vp, vp, vp]
     L.mla_kv_append.restype = c_int
     L.mla_kv_append.argtypes = [vp, vp, vp, c_int, vp, c_int, c_float, c_int, c_int, c_i64, vp]
     _lib = L
@@ -300,6 +306,45 @@ def paged_decode(q, qpe, kv_cache, fmt, block_tables, seq_lens, page_size, page_
     (device).  Returns (o [B,q_len,H,512] bf16, lse [B,q_len,H] f32 or None)."""
     return PagedCall(q, qpe, kv_cache, fmt, block_tables, seq_lens, page_size, page_stride, kv_scale, sm_scale,
                      num_splits, workspace, o, lse, want_lse, num_cus, window, sinks).run()
+
+
+def paged_decode_noalloc(q, qpe, kv_cache, fmt, block_tables, seq_lens, page_size, page_stride=None, kv_scale=1.0,
+                         sm_scale=None, num_splits=None, o=None, lse=None, want_lse=True, num_cus=None):
+    """paged_decode through mla_paged_decode_noalloc: the workspace is the library's own
+    per-GPU scratch array (no workspace tensor).  Outputs are allocated here when not
+    given; the C call itself allocates nothing."""
+    B, q_len, H, _ = q.shape
+    dev = q.device
+    _need(q, "q", torch.bfloat16, (B, q_len, H, LATENT))
+    _need(qpe, "qpe", torch.bfloat16, (B, q_len, H, ROPE), dev)
+    _need(kv_cache, "kv_cache", torch.uint8, None, dev)
+    _need(block_tables, "block_tables", torch.int32, None, dev)
+    _need(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks]")
+    rb = {MLA_KV_BF16: 2 * ROW, MLA_KV_FP8_E4M3: ROW, MLA_KV_NVFP4: ROW // 2 + ROW // 16,
+          MLA_KV_FP8_E4M3_QFP8: ROW}.get(fmt)
+    if rb is None:
+        raise MlaError(MLA_ERR_UNSUPPORTED, "cache format")
+    if page_stride is None:
+        page_stride = page_size * rb
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(LATENT + ROPE)
+    if num_splits is None:
+        num_splits = plan_paged(num_cus or device_num_cus(dev.index or 0), B, q_len, H)
+    if o is None:
+        o = torch.empty((B, q_len, H, LATENT), dtype=torch.bfloat16, device=dev)
+    _need(o, "o", torch.bfloat16, (B, q_len, H, LATENT), dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, q_len, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, q_len, H), dev)
+    _check(lib().mla_paged_decode_noalloc(_ptr(q), _ptr(qpe), _ptr(kv_cache), int(fmt), float(kv_scale),
+                                          int(kv_cache.numel() // page_stride), int(page_size), int(page_stride),
+                                          _ptr(block_tables), int(block_tables.shape[1]), _ptr(seq_lens), B, q_len,
+                                          H, float(sm_scale), int(num_splits), _ptr(o), _ptr(lse), _stream(dev)),
+           "mla_paged_decode_noalloc")
+    return o, lse
 
 
 def kv_append(latent, rope, slots, kv_cache, fmt, page_size, page_stride=None, kv_scale=1.0):

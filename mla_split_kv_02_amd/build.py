@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla_decode.so")
 SOURCES = [os.path.join(CSRC, "mla_kernels.hip"), os.path.join(CSRC, "mla_append.hip"),
-           os.path.join(CSRC, "mla_api.cpp")]
+           os.path.join(CSRC, "mla_noalloc.hip"), os.path.join(CSRC, "mla_api.cpp")]
 
 ARCH = "gfx950"
 # packed-FP32 VALU forms are disabled for all device code (hipcc writes them on its

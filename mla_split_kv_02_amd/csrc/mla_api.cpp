@@ -69,6 +69,8 @@ const char* mla_status_string(int status) {
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: configuration not supported";
     case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL: workspace below mla_paged_workspace_bytes";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: kernel launch failed";
+    case MLA_ERR_SCRATCH_LIMIT:
+      return "MLA_ERR_SCRATCH_LIMIT: the problem's workspace exceeds the built-in scratch (MLA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown mla_status";
   }
 }
