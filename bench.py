@@ -1,4 +1,4 @@
-"""Benchmark of the absorbed-MLA paged decode on one MI355X.
+"""Benchmark of the absorbed-MLA split-KV decode on one MI355X.
 
 One step = the whole hot path on one batch: the split-KV decode launch (partials) and
 the LSE combine launch, through the C ABI, on inputs already resident in HBM.  The
@@ -10,6 +10,21 @@ default workload is the paged FP8 batch B=64, H=128, q_len=1, seq_len uniform in
 Algorithmic counts (per step): flops = 2 * (576 + 512) * H * sum over requests and
 queries of the tokens each query sees; bytes = visible cache rows (576 FP8 bytes per
 token) + Q + QPE + O (bf16) + LSE (fp32) + one int32 block-table entry per page read.
+
+Roofline.  The binding roof of the decode kernel is max(bytes / HBM peak, flops / MFMA
+peak of the contraction's own operand type): FP8 MFMA (5.0 PFLOP/s) for the FP8 cache,
+whose products run on FP8 matrix cores, bf16 MFMA (2.5 PFLOP/s) for the bf16 and NVFP4
+caches.  The fraction is quoted against the published peaks and, beside them, against
+ceilings measured in the same run (a stream-read kernel and MFMA loops,
+libmla_ceiling.so).
+
+Timing.  Before the warm-up, steps run for --settle-ms of wall time so that the clocks
+have settled (the first launches on a fresh GPU run ~20% slower); the settle steps are
+reported apart from the warm-up.  The decode and combine launches are bracketed with
+HIP events on the launch stream; per-launch decode times go to stderr.  Workloads whose
+streamed bytes would fit twice in the 256 MB MALL are flushed between steps (a 1 GiB
+write); their value and times then come from the events (the wall clock includes the
+flush), and their warm time is reported too.
 """
 
 from __future__ import annotations
@@ -24,15 +39,18 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBPS = 8000.0                          # MI355X HBM3E, published
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA, published
+MALL_BYTES = 256 << 20
 METRIC = "MLA decode KV GB/s + TFLOP/s (% roofline), B=64 H=128 paged fp8"
-# what each paged cache format computes in
+# operand type of each paged cache format's matrix-core products
+CONTRACTION = {0: "bf16", 1: "fp8", 2: "bf16", 3: "fp8"}
 ARITHMETIC = {
     0: "bf16 MFMA (bf16 query, bf16 weights), fp32 accumulation",
-    1: "bf16 query and softmax weights as exact two-term E4M3 splits on FP8 MFMA with the raw FP8 cache, "
-       "fp32 accumulation",
+    1: "FP8 MFMA on the raw FP8 cache: the bf16 query as an exact two-term E4M3 split, the softmax weights "
+       "(per-row, per-tile power-of-two scale) as two E4M3 terms (~8 significant bits), fp32 accumulation",
     2: "bf16 MFMA on the NVFP4 cache dequantised exactly to bf16, fp32 accumulation",
+    3: "FP8 MFMA: query rounded to E4M3, weights as two E4M3 terms, fp32 accumulation",
 }
 KERNEL_SOURCES = ("mla_split_kv_02_amd/csrc/mla_kernels.hip", "mla_split_kv_02_amd/csrc/mla_internal.h")
 
@@ -77,10 +95,20 @@ def traffic_from_profiles(workload: str, src_hash: str, kernel: str = "decode_pa
     return d.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_s: float):
     """The float64 oracle, as it stands, on requests of the same batch taken in order
     until about budget_s seconds of CPU work."""
-    import numpy as np
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -99,7 +127,8 @@ def cpu_baseline(w, budget_s: float):
         used += 1
     dt = time.perf_counter() - t0
     return {"value": round(done_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"requests 0..{used - 1} of the same batch ({used} of {w.B}), float64 numpy, {dt:.1f} s"}
+            "sample": f"requests 0..{used - 1} of the same batch ({used} of {w.B}), float64 numpy, {dt:.1f} s",
+            "cpu_model": cpu_model()}
 
 
 def copy_calibration(torch, dev, nbytes: int, steps: int):
@@ -114,102 +143,233 @@ def copy_calibration(torch, dev, nbytes: int, steps: int):
     print(json.dumps({"copy_calibration_bytes": nbytes, "steps": steps}), flush=True)
 
 
-# Score flops run at the FP8 rate and output flops at the bf16 rate in the FP8-query
-# variant (its output product is two FP8 terms, the bf16 rate's time): per (row, token)
-# pair 1152 flops at 5.0 PFLOP/s and 1024 at 2.5 PFLOP/s.
-MFMA_FP8_PEAK_TFLOPS = 5000.0
-MIXED_PEAK_TFLOPS = 2176.0 / (1152.0 / MFMA_FP8_PEAK_TFLOPS + 1024.0 / MFMA_BF16_PEAK_TFLOPS)
+def measure_ceilings(torch, dev):
+    """On-box ceilings: a 2 GiB stream read (GB/s) and MFMA loops, bf16 and FP8
+    (TFLOP/s), each the median of several launches timed with events."""
+    import numpy as np
+    from mla_split_kv_02_amd import ceiling
+
+    def timed(fn, reps):
+        st = torch.cuda.current_stream(dev)
+        fn()  # warm
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            fn()
+            b.record(st)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return float(np.median(ts))
+
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(3)
+    blocks = 256 * 8
+    out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    t_read = timed(lambda: ceiling.stream_read(buf, out, blocks), 7)
+    del buf
+    res = {"hbm_stream_read_GBps": round(nbytes / t_read / 1e9, 1)}
+    mb = 1024  # 4 wavefronts per SIMD
+    mout = torch.empty(mb * 4, dtype=torch.float32, device=dev)
+    for name, kind, iters in (("bf16", ceiling.MFMA_BF16, 2000), ("fp8", ceiling.MFMA_FP8, 1000)):
+        flops = mb * 4 * iters * 4 * ceiling.lib().mla_ceiling_mfma_flops(kind)
+        t = timed(lambda: ceiling.mfma(kind, iters, mout, mb), 5)
+        res[f"mfma_{name}_TFLOPs"] = round(flops / t / 1e12, 1)
+    # the clock the MFMA loop implies (published peaks assume 2.4 GHz)
+    res["mfma_clock_GHz"] = round(res["mfma_bf16_TFLOPs"] / PEAK_TFLOPS["bf16"] * 2.4, 3)
+    torch.cuda.synchronize()
+    return res
 
 
-def time_fp8_query_variant(mla, torch, w, q, qpe, cache, bt, sl, G, args, flops):
-    """The same pages decoded as format 3 (query rounded to E4M3, FP8-MFMA scores): same
-    steps, same timing, reported beside the headline (which is the bf16-query path)."""
-    call = mla.PagedCall(q, qpe, cache, mla.MLA_KV_FP8_E4M3_QFP8, bt, sl, w.page_size, w.page_stride, w.kv_scale,
-                         w.sm_scale, num_splits=G)
-    for _ in range(args.warmup):
-        call.partials()
-        call.combine()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+def roofline(flops, nbytes, t_ms, contraction, ceilings, traffic):
+    """Fraction of the binding roof for a kernel of `flops` / `nbytes` taking t_ms."""
+    peak = PEAK_TFLOPS[contraction]
+    t_hbm = nbytes / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = flops / (peak * 1e12)
+    if t_hbm >= t_mfma:
+        a = nbytes / (t_ms * 1e-3) / 1e9
+        r = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+             "frac": round(a / HBM_PEAK_GBPS, 4), "traffic": traffic, "contraction": contraction}
+        m = ceilings.get("hbm_stream_read_GBps") if ceilings else None
+    else:
+        a = flops / (t_ms * 1e-3) / 1e12
+        r = {"bound": "mfma", "achieved": round(a, 3), "peak": peak, "unit": "TFLOP/s",
+             "frac": round(a / peak, 4), "traffic": traffic, "contraction": contraction}
+        m = ceilings.get(f"mfma_{contraction}_TFLOPs") if ceilings else None
+    r["roof_us"] = round(max(t_hbm, t_mfma) * 1e6, 2)
+    if m:
+        r["measured_peak"] = m
+        r["frac_of_measured"] = round(a / m, 4)
+    return r
+
+
+def settle(step, torch, ms: float):
+    """Run steps for about `ms` of wall time (clocks settle); returns (steps, ms)."""
+    t0, n = time.perf_counter(), 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(10):
+            step()
+            n += 1
+        torch.cuda.synchronize()
+    return n, round((time.perf_counter() - t0) * 1e3, 1)
+
+
+def timed_steps(torch, steps, decode, combine, flush_buf=None):
+    """K steps with events around each launch; returns (wall_s, decode_ms[], combine_ms[])."""
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
+    for k in range(steps):
+        if flush_buf is not None:
+            flush_buf.fill_(k & 0x7F)
         ev[k][0].record()
-        call.partials()
+        decode()
         ev[k][1].record()
-        call.combine()
+        combine()
+        ev[k][2].record()
     torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
-    dec = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    dec_tflops = flops / (dec * 1e-3) / 1e12
-    log(f"[bench] fp8-query variant: {ms_step:.4f} ms/step, decode {dec:.4f} ms")
-    return {"kv_format": "fp8_e4m3, query rounded to e4m3 (FP8-MFMA scores; output product as on the FP8 path: "
-                         "weights split into two E4M3 terms on FP8 MFMA)",
-            "ms_per_step": round(ms_step, 5), "value": round(flops / (ms_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
-            "decode_ms": round(dec, 5),
-            "roofline": {"bound": "mfma", "achieved": round(dec_tflops, 3), "peak": round(MIXED_PEAK_TFLOPS, 1),
-                         "unit": "TFLOP/s", "frac": round(dec_tflops / MIXED_PEAK_TFLOPS, 4),
-                         "peak_note": "score flops at the fp8 peak, output flops at the bf16 peak (two FP8 terms)"}}
+    wall = time.perf_counter() - t0
+    return wall, [e[0].elapsed_time(e[1]) for e in ev], [e[1].elapsed_time(e[2]) for e in ev]
 
 
-def run_contig(args, w, mla, torch, np, gen):
-    """Contiguous split-KV decode (bf16 cache, q_len 1): one step is mla_decode_splitkv
-    followed by mla_splitkv_combine, with the planner's split (fixed at 128 tokens for the
-    tiny workload, as its definition states)."""
+def log_launches(name, ts):
+    import numpy as np
+    t = np.array(ts)
+    log(f"[bench] {name} per launch (ms): min {t.min():.4f} p10 {np.percentile(t, 10):.4f} median "
+        f"{np.median(t):.4f} p90 {np.percentile(t, 90):.4f} max {t.max():.4f}; first "
+        f"{', '.join(f'{x:.4f}' for x in t[:5])}; last {', '.join(f'{x:.4f}' for x in t[-3:])}")
+
+
+def run(args, w, mla, torch, np, gen):
     dev = torch.device("cuda:0")
     t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-    q, qpe, kv, kpe = (t16(a) for a in (w.q, w.qpe, w.kv, w.kpe))
-    L = gen.WORKLOADS[args.workload].get("kv_len_per_split")
-    op, lp, L = mla.decode_splitkv(q, qpe, kv, kpe, w.sm_scale, L)
-    o, lse = mla.splitkv_combine(op, lp)
-    flops = 2.0 * (576 + 512) * w.H * w.B * w.S
-    kvb = 2.0 * 576 * w.B * w.S
-    nbytes = kvb + w.B * w.H * (576 * 2 + 512 * 2 + 4)
-    for _ in range(args.warmup):
-        mla.decode_splitkv(q, qpe, kv, kpe, w.sm_scale, L, o_part=op, lse_part=lp)
-        mla.splitkv_combine(op, lp, o=o, lse=lse)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        ev[k][0].record()
-        mla.decode_splitkv(q, qpe, kv, kpe, w.sm_scale, L, o_part=op, lse_part=lp)
-        ev[k][1].record()
-        mla.splitkv_combine(op, lp, o=o, lse=lse)
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
-    dec = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
-    traffic = traffic_from_profiles(args.workload, kernel_source_hash(), "decode_contig")
-    if flops / nbytes >= ridge:
-        a = flops / (dec * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(a, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic}
+    paged = w.__class__.__name__ == "PagedInputs"
+    if paged:
+        q, qpe = t16(w.q), t16(w.qpe)
+        cache = torch.from_numpy(w.cache).to(dev)
+        bt = torch.from_numpy(w.block_tables).to(dev)
+        sl = torch.from_numpy(w.seq_lens).to(dev)
+        G = args.num_splits or mla.plan_paged(mla.device_num_cus(0), w.B, w.q_len, w.H)
+        call = mla.PagedCall(q, qpe, cache, w.fmt, bt, sl, w.page_size, w.page_stride, w.kv_scale, w.sm_scale,
+                             num_splits=G)
+        decode, combine = call.partials, call.combine
+        flops, nbytes, kvbytes = algorithmic_counts(w)
+        fmt = w.fmt
+        cfg = {"workload": args.workload, "B": w.B, "H": w.H, "q_len": w.q_len, "page_size": w.page_size,
+               "kv_format": gen.FMT_NAMES[w.fmt], "tokens": int(w.seq_lens.sum()), "num_splits": G}
+        log(f"[bench] B={w.B} H={w.H} q_len={w.q_len} tokens={int(w.seq_lens.sum())} num_splits={G} "
+            f"flops={flops:.3e} bytes={nbytes:.3e}")
     else:
-        a = nbytes / (dec * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(a / HBM_PEAK_GBPS, 4), "traffic": traffic}
+        q, qpe, kv, kpe = (t16(a) for a in (w.q, w.qpe, w.kv, w.kpe))
+        L = gen.WORKLOADS[args.workload].get("kv_len_per_split")
+        op, lp, L = mla.decode_splitkv(q, qpe, kv, kpe, w.sm_scale, L)
+        o, lse = mla.splitkv_combine(op, lp)
+        decode = lambda: mla.decode_splitkv(q, qpe, kv, kpe, w.sm_scale, L, o_part=op, lse_part=lp)
+        combine = lambda: mla.splitkv_combine(op, lp, o=o, lse=lse)
+        flops = 2.0 * (576 + 512) * w.H * w.B * w.S
+        kvbytes = 2.0 * 576 * w.B * w.S
+        nbytes = kvbytes + w.B * w.H * (576 * 2 + 512 * 2 + 4)
+        fmt = 0
+        cfg = {"workload": args.workload, "B": w.B, "H": w.H, "S_kv": w.S, "q_len": 1, "kv_format": "bf16",
+               "kv_len_per_split": L, "num_splits": int(op.shape[2])}
+    step = lambda: (decode(), combine())
+    flush = {"on": True, "off": False}.get(args.flush, kvbytes < 2 * MALL_BYTES)
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if flush else None
+
+    n_settle, settle_ms = settle(step, torch, args.settle_ms)
+    log(f"[bench] settle: {n_settle} steps in {settle_ms} ms")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    wall, dec_ms, comb_ms = timed_steps(torch, args.steps, decode, combine, flush_buf)
+    dec = float(np.mean(dec_ms))
+    comb = float(np.mean(comb_ms))
+    log_launches("decode", dec_ms)
+    log(f"[bench] timed {args.steps} steps: {wall / args.steps * 1e3:.4f} ms/step wall"
+        f"{' (incl. flush)' if flush else ''}, decode {dec:.4f} ms, combine {comb:.4f} ms")
+    if flush:
+        # value from the launches themselves: the wall clock includes the flush writes
+        ms_step = dec + comb
+        _, wdec, wcomb = timed_steps(torch, args.steps, decode, combine, None)
+        cfg["warm_decode_ms"] = round(float(np.mean(wdec)), 5)
+        cfg["warm_combine_ms"] = round(float(np.mean(wcomb)), 5)
+        cfg["value_from"] = "hip events (decode + combine), L2/MALL flushed before each step"
+    else:
+        ms_step = wall / args.steps * 1e3
+        cfg["value_from"] = "wall clock over the timed steps"
+
+    ceilings = {}
+    if not args.no_ceilings:
+        ceilings = measure_ceilings(torch, dev)
+        log(f"[bench] ceilings: {ceilings}")
+    contraction = CONTRACTION[fmt]
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profiles(args.workload, src_hash, "decode_paged" if paged else "decode_contig")
+    roof = roofline(flops, nbytes, dec, contraction, ceilings, traffic)
+
+    value = flops / (ms_step * 1e-3) / 1e12
+    cfg.update({"arithmetic": ARITHMETIC[fmt], "decode_ms": round(dec, 5), "combine_ms": round(comb, 5),
+                "decode_ms_median": round(float(np.median(dec_ms)), 5),
+                "kv_GBps": round(nbytes / (ms_step * 1e-3) / 1e9, 1),
+                "settle": {"steps": n_settle, "ms": settle_ms}, "flush_between_steps": flush,
+                "kernel_source_sha": src_hash})
+    if fmt == 1:
+        # the split path runs each product as two FP8 MFMA terms: twice the algorithmic
+        # flops on FP8 matrix cores, i.e. the matrix-core time of a bf16 contraction
+        a = flops / (dec * 1e-3) / 1e12
+        roof["bf16_rate_view"] = {"achieved_TFLOPs": round(a, 3), "peak": PEAK_TFLOPS["bf16"],
+                                  "frac": round(a / PEAK_TFLOPS["bf16"], 4),
+                                  "note": "algorithmic flops against the bf16 MFMA peak: the rate the two-term "
+                                          "FP8 products execute at"}
     out = {
-        "metric": METRIC, "value": round(flops / (ms_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": args.workload, "B": w.B, "H": w.H, "S_kv": w.S, "q_len": 1, "kv_format": "bf16",
-                   "kv_len_per_split": L, "num_splits": int(op.shape[2]), "decode_ms": round(dec, 5),
-                   "kv_GBps": round(kvb / (ms_step * 1e-3) / 1e9, 1), "kernel_source_sha": kernel_source_hash()},
-        "roofline": roof,
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": contraction, "data": "synthetic", "config": cfg, "roofline": roof,
     }
+    if ceilings:
+        out["ceilings"] = ceilings
+    if paged and fmt == gen.FMT_FP8 and not args.no_variant:
+        out["fp8_query_variant"] = time_fp8_query_variant(mla, torch, np, w, q, qpe, cache, bt, sl, G, args, flops,
+                                                          nbytes, ceilings)
+    if paged and not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def time_fp8_query_variant(mla, torch, np, w, q, qpe, cache, bt, sl, G, args, flops, nbytes, ceilings):
+    """The same pages decoded as format 3 (query rounded to E4M3, FP8-MFMA scores): same
+    steps, same timing, reported beside the headline (which keeps the bf16 query)."""
+    call = mla.PagedCall(q, qpe, cache, mla.MLA_KV_FP8_E4M3_QFP8, bt, sl, w.page_size, w.page_stride, w.kv_scale,
+                         w.sm_scale, num_splits=G)
+    for _ in range(max(args.warmup, 20)):
+        call.partials()
+        call.combine()
+    wall, dec_ms, _ = timed_steps(torch, args.steps, call.partials, call.combine)
+    ms_step = wall / args.steps * 1e3
+    dec = float(np.mean(dec_ms))
+    log(f"[bench] fp8-query variant: {ms_step:.4f} ms/step, decode {dec:.4f} ms")
+    return {"kv_format": "fp8_e4m3, query rounded to e4m3", "arithmetic": ARITHMETIC[3],
+            "ms_per_step": round(ms_step, 5), "value": round(flops / (ms_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+            "decode_ms": round(dec, 5), "roofline": roofline(flops, nbytes, dec, "fp8", ceilings, None)}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # the clocks take a few tens of milliseconds of load to settle (the first ~20 launches
-    # run ~20% slower), so the default warm-up is ~0.2 s of steps; the whole run stays < 1 s
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="wall time of untimed steps before the warm-up, for the clocks to settle")
     ap.add_argument("--workload", default="paged_fp8_b64_h128_s1k_32k")
     ap.add_argument("--num-splits", type=int, default=None)
+    ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto",
+                    help="write 1 GiB between timed steps (auto: when the cache would fit twice in the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-variant", action="store_true",
                     help="skip the extra timing of the FP8-query variant on FP8 workloads")
@@ -234,84 +394,7 @@ def main():
         return
     log(f"[bench] generating {args.workload}")
     w = gen.make_workload(args.workload)
-    if w.__class__.__name__ != "PagedInputs":
-        return run_contig(args, w, mla, torch, np, gen)
-    t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-    q, qpe = t16(w.q), t16(w.qpe)
-    cache = torch.from_numpy(w.cache).to(dev)
-    bt = torch.from_numpy(w.block_tables).to(dev)
-    sl = torch.from_numpy(w.seq_lens).to(dev)
-    num_cus = mla.device_num_cus(0)
-    G = args.num_splits or mla.plan_paged(num_cus, w.B, w.q_len, w.H)
-    call = mla.PagedCall(q, qpe, cache, w.fmt, bt, sl, w.page_size, w.page_stride, w.kv_scale, w.sm_scale,
-                         num_splits=G)
-    flops, nbytes, kvbytes = algorithmic_counts(w)
-    log(f"[bench] B={w.B} H={w.H} q_len={w.q_len} tokens={int(w.seq_lens.sum())} num_splits={G} "
-        f"flops={flops:.3e} bytes={nbytes:.3e}")
-
-    for _ in range(args.warmup):
-        call.partials()
-        call.combine()
-    torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup} steps)")
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        ev[k][0].record()
-        call.partials()
-        ev[k][1].record()
-        call.combine()
-        ev[k][2].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    dec_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    comb_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    ms_step = wall / args.steps * 1e3
-    dec_avg = sum(dec_ms) / len(dec_ms)
-    log(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step wall, decode {dec_avg:.4f} ms "
-        f"(min {min(dec_ms):.4f}, max {max(dec_ms):.4f}), combine {sum(comb_ms) / len(comb_ms):.4f} ms")
-
-    value = flops / (ms_step * 1e-3) / 1e12
-    kv_gbps = nbytes / (ms_step * 1e-3) / 1e9
-    dec_tflops = flops / (dec_avg * 1e-3) / 1e12
-    intensity = flops / nbytes
-    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
-    src_hash = kernel_source_hash()
-    traffic = traffic_from_profiles(args.workload, src_hash)
-    if intensity >= ridge:
-        roof = {"bound": "mfma", "achieved": round(dec_tflops, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(dec_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic}
-        if w.fmt == gen.FMT_FP8:
-            # the FP8 cache path runs each product as two FP8 MFMA terms (exact E4M3 splits of
-            # the bf16 query and of the weights): twice the algorithmic flops at twice the rate
-            roof["peak_note"] = ("bf16 dense MFMA peak; the FP8 cache path executes 2x these flops on FP8 MFMA "
-                                 "(two-term E4M3 operand splits), the same fraction of the 5.0 PFLOP/s FP8 peak")
-    else:
-        dec_gbps = nbytes / (dec_avg * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
-
-    out = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": args.workload, "B": w.B, "H": w.H, "q_len": w.q_len, "page_size": w.page_size,
-                   "kv_format": gen.FMT_NAMES[w.fmt], "tokens": int(w.seq_lens.sum()), "num_splits": G,
-                   "arithmetic": ARITHMETIC[w.fmt],
-                   "decode_ms": round(dec_avg, 5), "combine_ms": round(sum(comb_ms) / len(comb_ms), 5),
-                   "kv_GBps": round(kv_gbps, 1), "kv_GBps_frac_of_hbm": round(kv_gbps / HBM_PEAK_GBPS, 4),
-                   "step_TFLOPs_frac_of_bf16_mfma": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
-                   "kernel_source_sha": src_hash},
-        "roofline": roof,
-    }
-    if w.fmt == gen.FMT_FP8 and not args.no_variant:
-        out["fp8_query_variant"] = time_fp8_query_variant(mla, torch, w, q, qpe, cache, bt, sl, G, args, flops)
-    if not args.no_cpu_baseline:
-        log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+    run(args, w, mla, torch, np, gen)
 
 
 if __name__ == "__main__":

@@ -16,6 +16,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla_decode.so")
+# measurement kernels for the benchmark's on-box ceilings (not part of the decode path)
+CEILING_LIB = os.path.join(PKG, "libmla_ceiling.so")
+CEILING_SOURCES = [os.path.join(CSRC, "mla_ceiling.hip")]
 SOURCES = [os.path.join(CSRC, "mla_kernels.hip"), os.path.join(CSRC, "mla_append.hip"),
            os.path.join(CSRC, "mla_noalloc.hip"), os.path.join(CSRC, "mla_api.cpp")]
 
@@ -30,11 +33,10 @@ def hipcc() -> str:
     return exe
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    """Compile every source into LIB; returns its path.  Raises on failure."""
-    tmp = LIB + ".tmp"
+def _compile(sources: list[str], out: str, verbose: bool, extra: list[str] | None) -> str:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS, *(extra or []), *SOURCES, "-o", tmp]
+           "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS, *(extra or []), *sources, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -42,8 +44,15 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
     if verbose and (res.stdout or res.stderr):
         print(res.stdout, res.stderr, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+    """Compile the decode library (LIB) and the measurement library (CEILING_LIB);
+    returns LIB's path.  Raises on failure."""
+    _compile(CEILING_SOURCES, CEILING_LIB, verbose, extra)
+    return _compile(SOURCES, LIB, verbose, extra)
 
 
 if __name__ == "__main__":

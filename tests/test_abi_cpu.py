@@ -34,8 +34,25 @@ def test_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
+def test_ceiling_library_exports_its_header():
+    from mla_split_kv_02_amd import ceiling
+    if not os.path.exists(ceiling.CEILING_LIB_PATH):
+        pytest.skip("measurement library not built")
+    text = open(os.path.join(ROOT, "include", "mla_ceiling.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    decl = sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+    assert decl == sorted(ceiling.EXPORTED_SYMBOLS)
+    L = ceiling.lib()
+    for name in decl:
+        assert hasattr(L, name), name
+    assert L.mla_ceiling_mfma_flops(0) == 32768.0 and L.mla_ceiling_mfma_flops(1) == 131072.0
+    # invalid arguments are refused before any launch
+    assert L.mla_ceiling_stream_read(None, 16, None, 1, None) == -1
+    assert L.mla_ceiling_mfma(7, 1, ctypes.c_void_p(F), 1, None) == -1
+
+
 def test_status_strings():
-    for s in (0, -1, -2, -3, -4):
+    for s in (0, -1, -2, -3, -4, -5):
         assert mla.status_string(s).startswith("MLA_")
     assert mla.status_string(7) == "unknown mla_status"
 
