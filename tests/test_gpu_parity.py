@@ -42,10 +42,10 @@ def test_contig_splitkv_matches_oracle(B, H, S, L):
     q, qpe, kv, kpe = c.f64()
     rop, rlp = oracle.contig_decode_splitkv(q, qpe, kv, kpe, c.sm_scale, L)
     ro, rl = oracle.contig_decode(q, qpe, kv, kpe, c.sm_scale)
-    assert max_err(op, rop) <= TOL_O_BF16
-    assert max_err(lp, rlp) <= TOL_LSE
-    assert max_err(o, ro) <= TOL_O_BF16
-    assert max_err(lse, rl) <= TOL_LSE
+    check("op", op, rop, TOL_O_BF16)
+    check("lp", lp, rlp, TOL_LSE)
+    check("o", o, ro, TOL_O_BF16)
+    check("lse", lse, rl, TOL_LSE)
 
 
 def test_contig_b4_h16_s4096_full_size():
@@ -56,25 +56,29 @@ def test_contig_b4_h16_s4096_full_size():
     op, lp, o, lse, _ = _contig_run(c, L)
     q, qpe, kv, kpe = c.f64()
     ro, rl = oracle.contig_decode(q, qpe, kv, kpe, c.sm_scale)
-    assert max_err(o, ro) <= TOL_O_BF16
-    assert max_err(lse, rl) <= TOL_LSE
+    check("o", o, ro, TOL_O_BF16)
+    check("lse", lse, rl, TOL_LSE)
     rop, rlp = oracle.contig_decode_splitkv(q[:1], qpe[:1], kv[:1], kpe[:1], c.sm_scale, L)
-    assert max_err(op[:1], rop) <= TOL_O_BF16 and max_err(lp[:1], rlp) <= TOL_LSE
+    check("op[:1]", op[:1], rop, TOL_O_BF16)
+    check("lp[:1]", lp[:1], rlp, TOL_LSE)
 
 
-def test_contig_b32_h128_s8192_full_size_sampled():
-    say("contig_b32_h128_s8192 full size, requests 0 and 31")
+def test_contig_b32_h128_s8192_full_size():
+    """Every request of the contiguous B=32 H=128 workload, final and per-split outputs."""
+    say("contig_b32_h128_s8192 full size, all 32 requests")
     c = gen.make_workload("contig_b32_h128_s8192")
     L, ns = mla.plan_contig(256, c.B, c.S)
     assert (L, ns) == (1024, 8)
     op, lp, o, lse, _ = _contig_run(c, L)
     q, qpe, kv, kpe = c.f64()
-    for b in (0, 31):
+    eo = el = epo = epl = 0.0
+    for b in range(c.B):
         ro, rl = oracle.contig_decode(q[b:b + 1], qpe[b:b + 1], kv[b:b + 1], kpe[b:b + 1], c.sm_scale)
-        assert max_err(o[b:b + 1], ro) <= TOL_O_BF16
-        assert max_err(lse[b:b + 1], rl) <= TOL_LSE
+        eo, el = max(eo, max_err(o[b:b + 1], ro)), max(el, max_err(lse[b:b + 1], rl))
         rop, rlp = oracle.contig_decode_splitkv(q[b:b + 1], qpe[b:b + 1], kv[b:b + 1], kpe[b:b + 1], c.sm_scale, L)
-        assert max_err(op[b:b + 1], rop) <= TOL_O_BF16 and max_err(lp[b:b + 1], rlp) <= TOL_LSE
+        epo, epl = max(epo, max_err(op[b:b + 1], rop)), max(epl, max_err(lp[b:b + 1], rlp))
+    say(f"  O max|d|={eo:.3e} LSE {el:.3e} O_j {epo:.3e} lse_j {epl:.3e} (tol {TOL_O_BF16:.0e} / {TOL_LSE:.0e})")
+    assert eo <= TOL_O_BF16 and el <= TOL_LSE and epo <= TOL_O_BF16 and epl <= TOL_LSE
 
 
 def test_contig_zero_query_is_mean_of_latent():
@@ -115,8 +119,13 @@ def test_combine_matches_oracle_with_empty_splits(R, NS):
     o, lse = mla.splitkv_combine(top, tlp)
     torch.cuda.synchronize()
     ro, rl = oracle.combine(np.nan_to_num(op.astype(np.float64)), lp.astype(np.float64))
-    assert max_err(host(lse), rl) <= 1e-5
-    assert max_err(host(o), ro) <= 8e-3  # bf16 rounding of |O| < 4
+    check("host(lse)", host(lse), rl, 1e-5)
+    # O is rounded to bf16 (round to nearest even): at most half a unit in the last place,
+    # 2^-8 of |O| relative, plus the fp32 accumulation over <= 150 splits
+    err = np.abs(host(o) - ro)
+    bound = 2.0 ** -8 * np.abs(ro) + 1e-5
+    say(f"  O: max |d| / bound = {float((err / bound).max()):.3f}")
+    assert (err <= bound).all()
     assert (host(o)[5] == 0).all() and np.isneginf(host(lse)[5])
 
 
@@ -152,8 +161,8 @@ def test_paged_matches_oracle(fmt, q_len, page_size):
     ro, rl = _paged_ref(w)
     for ns in (None, 1, 5):
         o, lse = _paged_run(w, ns)
-        assert max_err(o, ro) <= _tol_o(fmt), ns
-        assert max_err(lse, rl) <= TOL_LSE, ns
+        check(f"o {ns}", o, ro, _tol_o(fmt))
+        check(f"lse {ns}", lse, rl, TOL_LSE)
 
 
 @pytest.mark.parametrize("H,q_len", [(16, 1), (16, 2), (48, 1), (64, 4), (128, 8)])
@@ -163,8 +172,8 @@ def test_paged_head_and_query_counts(H, q_len):
                        max_blocks=4)
     ro, rl = _paged_ref(w)
     o, lse = _paged_run(w)
-    assert max_err(o, ro) <= TOL_O_QUANT
-    assert max_err(lse, rl) <= TOL_LSE
+    check("o", o, ro, TOL_O_QUANT)
+    check("lse", lse, rl, TOL_LSE)
 
 
 @pytest.mark.parametrize("ns", [None, 200])
@@ -176,8 +185,8 @@ def test_paged_one_long_request_spans_every_range(ns):
                        seq_lens=[16000, 40], max_blocks=250)
     ro, rl = _paged_ref(w)
     o, lse = _paged_run(w, ns)
-    assert max_err(o, ro) <= TOL_O_QUANT
-    assert max_err(lse, rl) <= TOL_LSE
+    check("o", o, ro, TOL_O_QUANT)
+    check("lse", lse, rl, TOL_LSE)
 
 
 def test_paged_empty_and_short_requests():
@@ -187,8 +196,8 @@ def test_paged_empty_and_short_requests():
     ro, rl = _paged_ref(w)
     for ns in (None, 1, 2, 3):
         o, lse = _paged_run(w, ns)
-        assert max_err(o, ro) <= TOL_O_BF16, ns
-        assert max_err(lse, rl) <= TOL_LSE, ns
+        check(f"o {ns}", o, ro, TOL_O_BF16)
+        check(f"lse {ns}", lse, rl, TOL_LSE)
         assert (o[0] == 0).all() and np.isneginf(lse[0]).all()
         assert np.isneginf(lse[1, 0]).all() and (o[1, 0] == 0).all()
 
@@ -214,7 +223,8 @@ def test_paged_padded_page_stride():
                        page_stride=64 * 324 + 48)
     ro, rl = _paged_ref(w)
     o, lse = _paged_run(w)
-    assert max_err(o, ro) <= TOL_O_QUANT and max_err(lse, rl) <= TOL_LSE
+    check("o", o, ro, TOL_O_QUANT)
+    check("lse", lse, rl, TOL_LSE)
 
 
 def test_paged_fp8_every_code():
@@ -228,7 +238,8 @@ def test_paged_fp8_every_code():
     w.kv_scale = 1.0 / 128  # |values| <= 3.5 keeps the bf16 rounding of O inside the tolerance
     ro, rl = _paged_ref(w)
     o, lse = _paged_run(w)
-    assert max_err(o, ro) <= TOL_O_QUANT and max_err(lse, rl) <= TOL_LSE
+    check("o", o, ro, TOL_O_QUANT)
+    check("lse", lse, rl, TOL_LSE)
 
 
 def test_paged_nvfp4_every_code_and_scale():
@@ -243,21 +254,20 @@ def test_paged_nvfp4_every_code_and_scale():
     w.block_tables[:] = 0
     ro, rl = _paged_ref(w)
     o, lse = _paged_run(w)
-    assert max_err(o, ro) <= TOL_O_QUANT and max_err(lse, rl) <= TOL_LSE
+    check("o", o, ro, TOL_O_QUANT)
+    check("lse", lse, rl, TOL_LSE)
 
 
-def test_paged_fp8_b64_h128_full_size_sampled():
-    """The benchmark workload at full size and in its benchmark launch configuration;
-    the shortest, the longest and a middle request are compared in full."""
-    say("paged_fp8_b64_h128 full size")
+def test_paged_fp8_b64_h128_full_size():
+    """The benchmark workload at full size and in its benchmark launch configuration:
+    every one of its 64 requests against the oracle."""
+    say("paged_fp8_b64_h128 full size, all 64 requests")
     w = gen.make_workload("paged_fp8_b64_h128_s1k_32k")
     o, lse = _paged_run(w, mla.plan_paged(256, w.B, w.q_len, w.H))
     assert np.isfinite(o).all()
-    order = np.argsort(w.seq_lens)
-    pick = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
-    ro, rl = _paged_ref(w, requests=pick)
-    assert max_err(o[pick], ro) <= TOL_O_QUANT
-    assert max_err(lse[pick], rl) <= TOL_LSE
+    ro, rl = _paged_ref(w)
+    check("O (64 requests)", o, ro, TOL_O_QUANT)
+    check("LSE (64 requests)", lse, rl, TOL_LSE)
 
 
 def _scale_bf16(bits, k):
@@ -281,8 +291,8 @@ def test_paged_fp8_query_magnitudes_and_peaked_rows(qexp, scale_exp):
     w.sm_scale = w.sm_scale * 2.0 ** scale_exp
     ro, rl = _paged_ref(w)
     o, lse = _paged_run(w)
-    assert max_err(o, ro) <= TOL_O_QUANT
-    assert max_err(lse, rl) <= TOL_LSE
+    check("o", o, ro, TOL_O_QUANT)
+    check("lse", lse, rl, TOL_LSE)
 
 
 @pytest.mark.parametrize("q_len,page_size", [(1, 64), (2, 32)])
@@ -311,8 +321,8 @@ def test_paged_fp8_rising_scores(q_len, page_size):
     ro, rl = _paged_ref(w)
     for ns in (None, 1):
         o, lse = _paged_run(w, ns)
-        assert max_err(o, ro) <= TOL_O_QUANT, ns
-        assert max_err(lse, rl) <= TOL_LSE, ns
+        check(f"o {ns}", o, ro, TOL_O_QUANT)
+        check(f"lse {ns}", lse, rl, TOL_LSE)
 
 
 @pytest.mark.parametrize("fmt", [gen.FMT_FP8, oracle.FMT_FP8_QFP8])
@@ -384,8 +394,8 @@ def test_paged_window_and_sinks_match_oracle(fmt, q_len):
                                      sinks=None if sk is None else sk.astype(np.float64))
         for ns in (None, 1, 7):
             o, lse = _paged_run_ext(w, window, sk, ns)
-            assert max_err(o, ro) <= _tol_o(base_fmt), (window, ns)
-            assert max_err(lse, rl) <= TOL_LSE, (window, ns)
+            check(f"o {(window, ns)}", o, ro, _tol_o(base_fmt))
+            check(f"lse {(window, ns)}", lse, rl, TOL_LSE)
 
 
 def test_paged_ext_without_window_or_sinks_is_the_plain_path():
@@ -426,8 +436,8 @@ def test_paged_fp8_query_matches_oracle(q_len, page_size):
     ro, rl = _paged_ref(w)
     for ns in (None, 1, 5):
         o, lse = _paged_run(w, ns)
-        assert max_err(o, ro) <= TOL_O_QUANT, ns
-        assert max_err(lse, rl) <= TOL_LSE, ns
+        check(f"o {ns}", o, ro, TOL_O_QUANT)
+        check(f"lse {ns}", lse, rl, TOL_LSE)
     # the query really is rounded: the bf16-query path on the same pages differs
     w.fmt = gen.FMT_FP8
     o1, _ = _paged_run(w)
@@ -441,7 +451,8 @@ def test_paged_fp8_query_head_and_query_counts(H, q_len):
                              seed=150 + H + q_len, max_blocks=4))
     ro, rl = _paged_ref(w)
     o, lse = _paged_run(w)
-    assert max_err(o, ro) <= TOL_O_QUANT and max_err(lse, rl) <= TOL_LSE
+    check("o", o, ro, TOL_O_QUANT)
+    check("lse", lse, rl, TOL_LSE)
 
 
 def test_paged_fp8_query_rounding_ties_and_every_code():
@@ -464,29 +475,34 @@ def test_paged_fp8_query_rounding_ties_and_every_code():
     w.qpe = bits[w.q.size:].reshape(w.qpe.shape)
     ro, rl = _paged_ref(w)
     o, lse = _paged_run(w)
-    assert max_err(o, ro) <= TOL_O_QUANT and max_err(lse, rl) <= TOL_LSE
+    check("o", o, ro, TOL_O_QUANT)
+    check("lse", lse, rl, TOL_LSE)
 
 
 def test_paged_fp8_query_b64_h128_full_size_sampled():
-    say("paged_fp8_b64_h128 fp8-query full size")
+    """The FP8-query format on the benchmark pages: 16 requests (every fourth, sorted by
+    length, so the shortest and the longest are among them)."""
+    say("paged_fp8_b64_h128 fp8-query full size, 16 requests")
     w = _fp8q(gen.make_workload("paged_fp8_b64_h128_s1k_32k"))
     o, lse = _paged_run(w, mla.plan_paged(256, w.B, w.q_len, w.H))
     assert np.isfinite(o).all()
     order = np.argsort(w.seq_lens)
-    pick = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
+    pick = sorted({int(order[i]) for i in list(range(0, 64, 4)) + [63]})
     ro, rl = _paged_ref(w, requests=pick)
-    assert max_err(o[pick], ro) <= TOL_O_QUANT
-    assert max_err(lse[pick], rl) <= TOL_LSE
+    check(f"O ({len(pick)} requests)", o[pick], ro, TOL_O_QUANT)
+    check(f"LSE ({len(pick)} requests)", lse[pick], rl, TOL_LSE)
 
 
 @pytest.mark.slow
 def test_paged_nvfp4_b128_h128_q2_full_size_sampled():
-    say("paged_nvfp4_b128_h128_q2 full size")
+    """The NVFP4 q_len 2 workload at full size and in its benchmark launch configuration:
+    16 of its 128 requests (every eighth by length, with the shortest and the longest)."""
+    say("paged_nvfp4_b128_h128_q2 full size, 16 requests")
     w = gen.make_workload("paged_nvfp4_b128_h128_q2_s2k_64k")
     o, lse = _paged_run(w, mla.plan_paged(256, w.B, w.q_len, w.H))
     assert np.isfinite(o).all()
     order = np.argsort(w.seq_lens)
-    pick = [int(order[0]), int(order[-1])]
+    pick = sorted({int(order[i]) for i in list(range(0, 128, 8)) + [127]})
     ro, rl = _paged_ref(w, requests=pick)
-    assert max_err(o[pick], ro) <= TOL_O_QUANT
-    assert max_err(lse[pick], rl) <= TOL_LSE
+    check(f"O ({len(pick)} requests)", o[pick], ro, TOL_O_QUANT)
+    check(f"LSE ({len(pick)} requests)", lse[pick], rl, TOL_LSE)

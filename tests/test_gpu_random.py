@@ -12,7 +12,7 @@ import torch
 import oracle
 import mla_split_kv_02_amd as mla
 from workloads import gen
-from gpu_util import TOL_LSE, TOL_O_BF16, TOL_O_QUANT, bf16_dev, host, i32_dev, max_err, say, u8_dev
+from gpu_util import TOL_LSE, TOL_O_BF16, TOL_O_QUANT, bf16_dev, check, host, i32_dev, max_err, say, u8_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -58,5 +58,5 @@ def test_random_paged_case_matches_oracle(seed):
                               sinks=None if sinks is None else torch.from_numpy(sinks).to(DEV))
     torch.cuda.synchronize()
     tol = TOL_O_BF16 if base_fmt == gen.FMT_BF16 else TOL_O_QUANT
-    assert max_err(host(o), ro) <= tol
-    assert max_err(host(lse), rl) <= TOL_LSE
+    check("O", host(o), ro, tol)
+    check("LSE", host(lse), rl, TOL_LSE)
