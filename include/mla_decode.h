@@ -106,14 +106,14 @@ int mla_device_num_cus(int device, int* num_cus);
  * Host-only integer work.  num_cus, B, S_kv >= 1. */
 int mla_plan_contig(int num_cus, int B, int S_kv, int* kv_len_per_split, int* num_splits);
 
-/* Paged split planner.  The paged op cuts the whole batch's 32-token tiles into
- * `num_splits` contiguous ranges, one workgroup each, on the device from device
- * seq_lens (so no host copy of them is needed: the TokenSpeed page avoids a
- * device-to-host sync for the same reason, _init_prefill_metadata).  The ranges are of
- * about equal cost, where a request costs its tiles plus a fixed overhead of 10 tiles
- * (what starting a request in a workgroup costs: query load, pipeline fill, partial
- * store).  This returns the range count that fills the device once:
- * num_cus / ceil(q_len * H / 128), at least 1. */
+/* Paged split planner.  The paged op cuts the whole batch's tiles (64 tokens for the FP8
+ * formats, 32 for the others) into `num_splits` contiguous ranges, one workgroup each,
+ * on the device from device seq_lens (so no host copy of them is needed: the TokenSpeed
+ * page avoids a device-to-host sync for the same reason, _init_prefill_metadata).  The
+ * ranges are of about equal cost, where a request costs its tiles plus a fixed overhead
+ * of 320 tokens' worth of tiles (what starting a request in a workgroup costs: query
+ * load, pipeline fill, partial store).  This returns the range count that fills the
+ * device once: num_cus / ceil(q_len * H / 128), at least 1. */
 int mla_plan_paged(int num_cus, int B, int q_len, int H, int* num_splits);
 
 /* Bytes of workspace mla_paged_decode needs: (num_splits + B - 1) partial slots of
@@ -152,7 +152,11 @@ int mla_splitkv_combine(const float* o_part, const float* lse_part, int rows, in
  * writes, for each request b it touches, the normalised partial O and its lse into
  * slot w + b of the workspace; the workspace also records, per request, the first and
  * last range that touch it.  Useful to a caller that merges partials itself, or times
- * the two launches apart. */
+ * the two launches apart.  Workspace layout (each section starting on a 256-byte
+ * boundary, slots = num_splits + B - 1, rows = q_len * H): o_part [slots][rows][512] fp32
+ * (normalised O_j), lse_part [slots][rows] fp32, seg_first [B] int32, seg_last [B]
+ * int32, then an info block whose first int32 is the batch's total cost.  Only the slots
+ * of ranges that hold tiles of the request are written. */
 int mla_paged_decode_partials(const uint16_t* q, const uint16_t* qpe, const void* kv_cache, int fmt,
                               float kv_scale, int num_pages, int page_size,
                               int64_t page_stride_bytes, const int32_t* block_tables,

@@ -24,24 +24,24 @@
 // spread between its MFMAs in nine steps; then one barrier.  The first tile's softmax and the last tile's output product come
 // after the loop.
 //
-// FP8 cache (run_range_split): no tile is converted to bf16.  The bf16 query of each row
-// is split exactly into two E4M3 operands (hi + lo, after a power-of-two row scale), so
-// the scores run on FP8 MFMA 32x32x64 straight from the raw tile, each K operand read
-// once for both halves (18 MFMAs per tile).  The softmax weights of each row and tile are
-// scaled by a power of two 2^e that puts the tile's largest at 2^7..2^8 and split the
-// same way (about 8 significant bits, like bf16), and the output product takes the raw
-// tile's V^T through the 8-bit LDS transpose read: one scaled MFMA 32x32x64 per 32 dims
-// whose first 32-element scale block holds the tile's tokens with P_hi and whose second
-// holds them with P_lo, both with the row's E8M0 scale 2^-e (16 MFMAs per tile).  The
-// matrix-core time per token is that of the bf16 path, and no tile is converted to bf16.
+// FP8 cache (run_range_fp8): 64-token tiles, none converted to bf16.  The bf16 query of
+// each row is split exactly into two E4M3 operands (hi + lo, after a power-of-two row
+// scale), so the scores run on FP8 MFMA 32x32x64 straight from the raw tile, each K
+// operand read once for both terms (36 MFMAs per tile, two 32-token halves).  The softmax
+// weights of each row and tile are scaled by a power of two 2^e that puts the tile's
+// largest at 2^7..2^8 and split the same way (about 8 significant bits, like bf16), and
+// the output product takes the raw tile's V^T through the 8-bit LDS transpose read: per
+// 32 dims one V^T operand holding the tile's 64 tokens feeds two scaled MFMA 32x32x64,
+// one with P_hi and one with P_lo, with the row's E8M0 scale 2^-e (32 MFMAs per tile).
+// The matrix-core time per token is that of the bf16 path.
 //
 // Paged ranges are balanced by cost: a request costs its tiles plus a fixed overhead for
 // its segment's query load, pipeline fill and partial store (decode_paged_kernel).
 //
-// FP8 query (cache format kFmtFp8Q, the TokenSpeed page's FP8 decode): the same split
-// loop with the query rounded to E4M3 once per range (72 registers) instead of split, so
-// its scores take 9 FP8 MFMA 32x32x64 per tile instead of 18; the weights and the output
-// product are the split path's.
+// FP8 query (cache format kFmtFp8Q, the TokenSpeed page's FP8 decode): the same loop
+// with the query rounded to E4M3 once per range (72 registers) instead of split, so its
+// scores take 18 FP8 MFMA 32x32x64 per 64-token tile instead of 36; the weights and the
+// output product are those of the FP8 cache path.
 //
 // A sliding window (paged) starts each request's tiles at the one holding its first
 // visible token and masks below the window; attention sinks enter in the combine.
@@ -101,11 +101,12 @@ template <> struct Pipe<kFmtNvfp4> {
   static constexpr int kTiles = 3, kStride = kTileBytes, kRaw = 3, kRawBytes = kNvRawBytes, kAhead = 3,
                        kLoads = kNvDataLoads + kNvScaleLoads;
 };
-// FP8 cache (split path): raw tiles only (no bf16 copy); a tile is read by its score
-// block and by the next iteration's output product, and the loads run four tiles ahead:
-// six buffers.
+// FP8 cache: raw 64-token tiles only (no bf16 copy); a tile is read by its score block
+// and by the next iteration's output product, and the loads run two tiles ahead: four
+// buffers of 36 KiB.
 template <> struct Pipe<kFmtFp8> {
-  static constexpr int kTiles = 0, kStride = 0, kRaw = 6, kRawBytes = kFp8RawBytes, kAhead = 4, kLoads = kFp8Loads;
+  static constexpr int kTiles = 0, kStride = 0, kRaw = 4, kRawBytes = 2 * kFp8RawBytes, kAhead = 2,
+                       kLoads = kFp8Loads / 2;
 };
 // The FP8 query runs the same loop on the same raw tiles.
 template <> struct Pipe<kFmtFp8Q> : Pipe<kFmtFp8> {};
@@ -514,66 +515,6 @@ __device__ __forceinline__ f32x16 qk_tile(const bf16x8* q, uint32_t tile, const 
 }
 
 
-// Scores of one tile with the FP8 query: S^T[token][row] on 9 MFMA 32x32x64 FP8 (E4M3 x
-// E4M3), A = the raw K codes of the lane's token row straight from the staging buffer,
-// B = the query codes (in registers).  K-step k covers dims 64k .. 64k+63 (raw chunk
-// group k); lane half h takes dims 64k + 32h .. + 31 as bytes 0..31 of its operand, in
-// both operands (the matrix core pairs equal byte positions of equal lane halves), read
-// as chunks 2h, 2h+1 at f[e] + 2048 k.  The operand buffers are five fixed 8-register
-// blocks (v216..v255) so that each 16-byte read can fill half of one: reads run three
-// K-steps ahead and a buffer is refilled two steps after its last MFMA; every wait counts
-// the reads issued after the one it needs (they complete in order).  Accumulation is in
-// vector registers, as in qk_tile; the closing s_nop run covers the wait states a vector
-// read of the result needs after this 16-pass MFMA.
-__device__ __forceinline__ f32x16 qk_tile_f8(const i32x8* q, uint32_t raw, const uint32_t* f) {
-  const uint32_t f0 = raw + f[0], f1 = raw + f[1];
-  f32x16 s;
-  asm volatile(
-      "ds_read_b128 v[216:219], %[f0] offset:0\n\t"
-      "ds_read_b128 v[220:223], %[f1] offset:0\n\t"
-      "ds_read_b128 v[224:227], %[f0] offset:2048\n\t"
-      "ds_read_b128 v[228:231], %[f1] offset:2048\n\t"
-      "ds_read_b128 v[232:235], %[f0] offset:4096\n\t"
-      "ds_read_b128 v[236:239], %[f1] offset:4096\n\t"
-      "ds_read_b128 v[240:243], %[f0] offset:6144\n\t"
-      "ds_read_b128 v[244:247], %[f1] offset:6144\n\t"
-      "s_waitcnt lgkmcnt(6)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[216:223], %[q0], 0\n\t"
-      "ds_read_b128 v[248:251], %[f0] offset:8192\n\t"
-      "ds_read_b128 v[252:255], %[f1] offset:8192\n\t"
-      "s_waitcnt lgkmcnt(6)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[224:231], %[q1], %[s]\n\t"
-      "ds_read_b128 v[216:219], %[f0] offset:10240\n\t"
-      "ds_read_b128 v[220:223], %[f1] offset:10240\n\t"
-      "s_waitcnt lgkmcnt(6)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[232:239], %[q2], %[s]\n\t"
-      "ds_read_b128 v[224:227], %[f0] offset:12288\n\t"
-      "ds_read_b128 v[228:231], %[f1] offset:12288\n\t"
-      "s_waitcnt lgkmcnt(6)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[240:247], %[q3], %[s]\n\t"
-      "ds_read_b128 v[232:235], %[f0] offset:14336\n\t"
-      "ds_read_b128 v[236:239], %[f1] offset:14336\n\t"
-      "s_waitcnt lgkmcnt(6)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[248:255], %[q4], %[s]\n\t"
-      "ds_read_b128 v[240:243], %[f0] offset:16384\n\t"
-      "ds_read_b128 v[244:247], %[f1] offset:16384\n\t"
-      "s_waitcnt lgkmcnt(6)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[216:223], %[q5], %[s]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[224:231], %[q6], %[s]\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[232:239], %[q7], %[s]\n\t"
-      "s_waitcnt lgkmcnt(0)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[240:247], %[q8], %[s]\n\t"
-      "s_nop 7\n\ts_nop 7\n\ts_nop 7"
-      : [s] "=&v"(s)
-      : [f0] "v"(f0), [f1] "v"(f1),
-        [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]),
-        [q5] "v"(q[5]), [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8])
-      : "memory", "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255");
-  return s;
-}
-
 // Output product of one tile: O^T[dim][row] += V^T[dim][token] . P^T[token][row] for the
 // 16 blocks of 32 dims and the two K-steps of 16 tokens.  V^T comes from two transpose
 // reads per operand (vb[2e]: tokens 4e .. of the lane's half.  Dims 32 apart are 4
@@ -970,17 +911,18 @@ __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const un
 // the row's score scale), so every element of magnitude at least 2^-2 after scaling, i.e.
 // 2^-9 of the row's largest, is split exactly; smaller ones keep an absolute error of at
 // most 2^-10 after scaling, under 2^-17 of the row's largest.
-//   scores  S^T = K . (Q_hi + Q_lo)^T: 9 K-steps of 64 dims, each raw K operand read from
-//           LDS once and used by two MFMA 32x32x64 (hi, then lo)
-//   output  O^T += V^T . (P_hi + P_lo)^T 2^-e over a 32-token tile: one scaled MFMA
-//           32x32x64 per 32 dims, whose K = 64 is the tile's 32 tokens twice: its first
-//           scale block pairs V^T with P_hi, its second the same V^T with P_lo (see
-//           split_vt_offsets for the operand layout).  V^T is read from the raw tile with
-//           the 8-bit LDS transpose read, so no tile is ever converted to bf16.
+// The FP8 path works on 64-token tiles (two halves of 32, M-blocks of the score product):
+//   scores  S^T = K . (Q_hi + Q_lo)^T: per half, 9 K-steps of 64 dims, each raw K operand
+//           read from LDS once and used by two MFMA 32x32x64 (hi, then lo)
+//   output  O^T += V^T . (P'_hi + P'_lo)^T 2^-e: per 32 dims, two scaled MFMA 32x32x64 on
+//           one V^T operand that holds each of the tile's 64 tokens once (see
+//           split_vt_offsets for the operand layout), B = P'_hi, then B = P'_lo.  V^T is
+//           read from the raw tile with the 8-bit LDS transpose read, so no tile is ever
+//           converted to bf16.
 // The softmax weights are split the same way after a per-row, per-tile power-of-two
-// scale 2^e that puts the tile's largest weight in [2^7, 2^8) (split_piece): P' = hi + lo
-// to about 8 significant bits, like bf16, within E4M3's range, and the output MFMA's E8M0
-// operand scale takes 2^e out again.
+// scale 2^e that puts the tile's largest weight in [2^7, 2^8) (split_piece64): P' = hi +
+// lo to about 8 significant bits, like bf16, within E4M3's range, and the output MFMA's
+// E8M0 operand scale takes 2^e out again.
 // ------------------------------------------------------------------------------------
 
 // two floats -> two E4M3 codes (nearest, ties to even) in half-word `hw` of w
@@ -1079,72 +1021,228 @@ __device__ __forceinline__ void q_round_e4m3(const uint16_t* qrow, const uint16_
   }
 }
 
-// Scores of one tile on the split query: S^T = K . Q_hi^T + K . Q_lo^T.  K-step k's raw
-// operand (chunks 2h, 2h+1 of token row l % 32, at f[e] + 2048 k) goes into one of three
-// fixed 8-register buffers (v232..v255), read two K-steps ahead; a buffer is refilled one
-// K-step after its last MFMA.  Every wait counts the reads issued after the ones it needs
-// (LDS reads complete in order).  Accumulation is in vector registers (the accumulation
-// registers hold O); the closing s_nop run covers the wait states before a vector
-// instruction may read the result of this 16-pass MFMA.
-__device__ __forceinline__ f32x16 qk_tile_split(const i32x8* qh, const i32x8* ql, uint32_t raw, const uint32_t* f) {
+// ------------------------------------------------------------------------------------
+// FP8 tiles of 64 tokens.  A raw tile is two 32-token halves, each in the load_fp8_raw
+// layout (half h at byte 18432 h); M-block m of the score product is half m.  One
+// 64-token tile per iteration halves the per-token cost of everything that happens once
+// per tile (loop, block-table reads, waits, barrier, the softmax's row reductions), and
+// each V^T operand feeds two output MFMAs (P'_hi, then P'_lo) instead of carrying its
+// tokens twice.
+// ------------------------------------------------------------------------------------
+
+constexpr int kT8 = 64;                        // tokens per FP8 tile
+constexpr int kHalfBytes = kFp8RawBytes;       // 18432: one 32-token half
+constexpr int kT8Bytes = 2 * kHalfBytes;       // 36864
+constexpr int kT8Ahead = 2;                    // loads of tile i + 2 go out in iteration i
+constexpr int kT8Loads = kFp8Loads / 2;        // 9 load instructions per wavefront and tile
+
+// Raw 64-token tile starting at token tb.  Half h's 18 load instructions are dealt to the
+// wavefronts as in load_fp8_raw but rotated by 2h, so every wavefront issues nine.  A
+// second half that starts past the request's last token reloads the first half (its
+// scores are masked), so every address stays inside the request's pages.  e0, e1: the
+// block-table entries of the halves' first tokens (e1 = e0 if the second half reloads).
+__device__ __forceinline__ int half1_start(const Src& S, int tb) { return tb + 32 < S.n ? tb + 32 : tb; }
+__device__ __forceinline__ void load_fp8_tile64(const Src& S, int tb, int e0, int e1, uint32_t st, int wave,
+                                                int lane) {
+  load_fp8_raw(S, tb, page_start(S, e0), st, wave, lane);
+  load_fp8_raw(S, half1_start(S, tb), page_start(S, e1), st + kHalfBytes, (wave + 2) & 3, lane);
+}
+
+// Scores of one 64-token tile on the split query: S^T_m = K_m . Q_hi^T + K_m . Q_lo^T for
+// the halves m = 0, 1 (accumulated in s0, s1).  Per K-step of 64 dims: the raw K operand
+// of each half (chunks 2h, 2h+1 of token row l % 32 at f[e] + 2048 k + 18432 m), read from
+// LDS once and used by the hi and the lo MFMA.  Operand buffers are two fixed sets of
+// 2 x 8 registers (v224..v255); the reads of a half run one M-block ahead, a buffer is
+// refilled only after two later MFMAs were issued, and every wait counts the reads issued
+// after the ones it needs (LDS reads complete in order).  The closing s_nop run covers the
+// wait states before vector instructions may read s0 and s1.
+__device__ __forceinline__ void qk_tile64_split(const i32x8* qh, const i32x8* ql, uint32_t raw, const uint32_t* f,
+                                                f32x16& s0, f32x16& s1) {
   const uint32_t f0 = raw + f[0], f1 = raw + f[1];
-  f32x16 s;
   asm volatile(
-      "ds_read_b128 v[232:235], %[f0] offset:0\n\t"
-      "ds_read_b128 v[236:239], %[f1] offset:0\n\t"
+      "ds_read_b128 v[224:227], %[f0] offset:0\n\t"
+      "ds_read_b128 v[228:231], %[f1] offset:0\n\t"
+      "ds_read_b128 v[232:235], %[f0] offset:18432\n\t"
+      "ds_read_b128 v[236:239], %[f1] offset:18432\n\t"
       "ds_read_b128 v[240:243], %[f0] offset:2048\n\t"
       "ds_read_b128 v[244:247], %[f1] offset:2048\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[232:239], %[h0], 0\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[232:239], %[l0], %[s]\n\t"
-      "ds_read_b128 v[248:251], %[f0] offset:4096\n\t"
-      "ds_read_b128 v[252:255], %[f1] offset:4096\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[240:247], %[h1], %[s]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[240:247], %[l1], %[s]\n\t"
-      "ds_read_b128 v[232:235], %[f0] offset:6144\n\t"
-      "ds_read_b128 v[236:239], %[f1] offset:6144\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[248:255], %[h2], %[s]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[248:255], %[l2], %[s]\n\t"
-      "ds_read_b128 v[240:243], %[f0] offset:8192\n\t"
-      "ds_read_b128 v[244:247], %[f1] offset:8192\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[232:239], %[h3], %[s]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[232:239], %[l3], %[s]\n\t"
-      "ds_read_b128 v[248:251], %[f0] offset:10240\n\t"
-      "ds_read_b128 v[252:255], %[f1] offset:10240\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[240:247], %[h4], %[s]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[240:247], %[l4], %[s]\n\t"
-      "ds_read_b128 v[232:235], %[f0] offset:12288\n\t"
-      "ds_read_b128 v[236:239], %[f1] offset:12288\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[248:255], %[h5], %[s]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[248:255], %[l5], %[s]\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[224:231], %[h0], 0\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[224:231], %[l0], %[s0]\n\t"
+      "ds_read_b128 v[248:251], %[f0] offset:20480\n\t"
+      "ds_read_b128 v[252:255], %[f1] offset:20480\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[h0], 0\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[l0], %[s1]\n\t"
+      "ds_read_b128 v[224:227], %[f0] offset:4096\n\t"
+      "ds_read_b128 v[228:231], %[f1] offset:4096\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[240:247], %[h1], %[s0]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[240:247], %[l1], %[s0]\n\t"
+      "ds_read_b128 v[232:235], %[f0] offset:22528\n\t"
+      "ds_read_b128 v[236:239], %[f1] offset:22528\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[h1], %[s1]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[l1], %[s1]\n\t"
+      "ds_read_b128 v[240:243], %[f0] offset:6144\n\t"
+      "ds_read_b128 v[244:247], %[f1] offset:6144\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[224:231], %[h2], %[s0]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[224:231], %[l2], %[s0]\n\t"
+      "ds_read_b128 v[248:251], %[f0] offset:24576\n\t"
+      "ds_read_b128 v[252:255], %[f1] offset:24576\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[h2], %[s1]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[l2], %[s1]\n\t"
+      "ds_read_b128 v[224:227], %[f0] offset:8192\n\t"
+      "ds_read_b128 v[228:231], %[f1] offset:8192\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[240:247], %[h3], %[s0]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[240:247], %[l3], %[s0]\n\t"
+      "ds_read_b128 v[232:235], %[f0] offset:26624\n\t"
+      "ds_read_b128 v[236:239], %[f1] offset:26624\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[h3], %[s1]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[l3], %[s1]\n\t"
+      "ds_read_b128 v[240:243], %[f0] offset:10240\n\t"
+      "ds_read_b128 v[244:247], %[f1] offset:10240\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[224:231], %[h4], %[s0]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[224:231], %[l4], %[s0]\n\t"
+      "ds_read_b128 v[248:251], %[f0] offset:28672\n\t"
+      "ds_read_b128 v[252:255], %[f1] offset:28672\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[h4], %[s1]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[l4], %[s1]\n\t"
+      "ds_read_b128 v[224:227], %[f0] offset:12288\n\t"
+      "ds_read_b128 v[228:231], %[f1] offset:12288\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[240:247], %[h5], %[s0]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[240:247], %[l5], %[s0]\n\t"
+      "ds_read_b128 v[232:235], %[f0] offset:30720\n\t"
+      "ds_read_b128 v[236:239], %[f1] offset:30720\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[h5], %[s1]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[l5], %[s1]\n\t"
       "ds_read_b128 v[240:243], %[f0] offset:14336\n\t"
       "ds_read_b128 v[244:247], %[f1] offset:14336\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[224:231], %[h6], %[s0]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[224:231], %[l6], %[s0]\n\t"
+      "ds_read_b128 v[248:251], %[f0] offset:32768\n\t"
+      "ds_read_b128 v[252:255], %[f1] offset:32768\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[h6], %[s1]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[l6], %[s1]\n\t"
+      "ds_read_b128 v[224:227], %[f0] offset:16384\n\t"
+      "ds_read_b128 v[228:231], %[f1] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[240:247], %[h7], %[s0]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[240:247], %[l7], %[s0]\n\t"
+      "ds_read_b128 v[232:235], %[f0] offset:34816\n\t"
+      "ds_read_b128 v[236:239], %[f1] offset:34816\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[h7], %[s1]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[l7], %[s1]\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[232:239], %[h6], %[s]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[232:239], %[l6], %[s]\n\t"
-      "ds_read_b128 v[248:251], %[f0] offset:16384\n\t"
-      "ds_read_b128 v[252:255], %[f1] offset:16384\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[240:247], %[h7], %[s]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[240:247], %[l7], %[s]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[224:231], %[h8], %[s0]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[224:231], %[l8], %[s0]\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[248:255], %[h8], %[s]\n\t"
-      "v_mfma_f32_32x32x64_f8f6f4 %[s], v[248:255], %[l8], %[s]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[h8], %[s1]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[l8], %[s1]\n\t"
       "s_nop 7\n\ts_nop 7\n\ts_nop 7"
-      : [s] "=&v"(s)
+      : [s0] "=&v"(s0), [s1] "=&v"(s1)
       : [f0] "v"(f0), [f1] "v"(f1),
         [h0] "v"(qh[0]), [h1] "v"(qh[1]), [h2] "v"(qh[2]), [h3] "v"(qh[3]), [h4] "v"(qh[4]),
         [h5] "v"(qh[5]), [h6] "v"(qh[6]), [h7] "v"(qh[7]), [h8] "v"(qh[8]),
         [l0] "v"(ql[0]), [l1] "v"(ql[1]), [l2] "v"(ql[2]), [l3] "v"(ql[3]), [l4] "v"(ql[4]),
         [l5] "v"(ql[5]), [l6] "v"(ql[6]), [l7] "v"(ql[7]), [l8] "v"(ql[8])
-      : "memory", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243",
-        "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255");
-  return s;
+      : "memory", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234", "v235",
+        "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248",
+        "v249", "v250", "v251", "v252", "v253", "v254", "v255");
+}
+
+// Scores of one 64-token tile with the FP8 query (cache format 3): one MFMA per half and
+// K-step, A = the raw K codes, B = the query codes.  The matrix core pairs equal byte
+// positions of equal lane halves, so query and key take the same dims per byte.  Three
+// fixed buffer sets of 2 x 8 registers (v208..v255), reads two K-steps ahead, a set
+// refilled two MFMAs after its last use.
+__device__ __forceinline__ void qk_tile64_f8(const i32x8* q, uint32_t raw, const uint32_t* f, f32x16& s0,
+                                             f32x16& s1) {
+  const uint32_t f0 = raw + f[0], f1 = raw + f[1];
+  asm volatile(
+      "ds_read_b128 v[208:211], %[f0] offset:0\n\t"
+      "ds_read_b128 v[212:215], %[f1] offset:0\n\t"
+      "ds_read_b128 v[216:219], %[f0] offset:18432\n\t"
+      "ds_read_b128 v[220:223], %[f1] offset:18432\n\t"
+      "ds_read_b128 v[224:227], %[f0] offset:2048\n\t"
+      "ds_read_b128 v[228:231], %[f1] offset:2048\n\t"
+      "ds_read_b128 v[232:235], %[f0] offset:20480\n\t"
+      "ds_read_b128 v[236:239], %[f1] offset:20480\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[208:215], %[q0], 0\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[216:223], %[q0], 0\n\t"
+      "ds_read_b128 v[240:243], %[f0] offset:4096\n\t"
+      "ds_read_b128 v[244:247], %[f1] offset:4096\n\t"
+      "ds_read_b128 v[248:251], %[f0] offset:22528\n\t"
+      "ds_read_b128 v[252:255], %[f1] offset:22528\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[224:231], %[q1], %[s0]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q1], %[s1]\n\t"
+      "ds_read_b128 v[208:211], %[f0] offset:6144\n\t"
+      "ds_read_b128 v[212:215], %[f1] offset:6144\n\t"
+      "ds_read_b128 v[216:219], %[f0] offset:24576\n\t"
+      "ds_read_b128 v[220:223], %[f1] offset:24576\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[240:247], %[q2], %[s0]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q2], %[s1]\n\t"
+      "ds_read_b128 v[224:227], %[f0] offset:8192\n\t"
+      "ds_read_b128 v[228:231], %[f1] offset:8192\n\t"
+      "ds_read_b128 v[232:235], %[f0] offset:26624\n\t"
+      "ds_read_b128 v[236:239], %[f1] offset:26624\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[208:215], %[q3], %[s0]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[216:223], %[q3], %[s1]\n\t"
+      "ds_read_b128 v[240:243], %[f0] offset:10240\n\t"
+      "ds_read_b128 v[244:247], %[f1] offset:10240\n\t"
+      "ds_read_b128 v[248:251], %[f0] offset:28672\n\t"
+      "ds_read_b128 v[252:255], %[f1] offset:28672\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[224:231], %[q4], %[s0]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q4], %[s1]\n\t"
+      "ds_read_b128 v[208:211], %[f0] offset:12288\n\t"
+      "ds_read_b128 v[212:215], %[f1] offset:12288\n\t"
+      "ds_read_b128 v[216:219], %[f0] offset:30720\n\t"
+      "ds_read_b128 v[220:223], %[f1] offset:30720\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[240:247], %[q5], %[s0]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q5], %[s1]\n\t"
+      "ds_read_b128 v[224:227], %[f0] offset:14336\n\t"
+      "ds_read_b128 v[228:231], %[f1] offset:14336\n\t"
+      "ds_read_b128 v[232:235], %[f0] offset:32768\n\t"
+      "ds_read_b128 v[236:239], %[f1] offset:32768\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[208:215], %[q6], %[s0]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[216:223], %[q6], %[s1]\n\t"
+      "ds_read_b128 v[240:243], %[f0] offset:16384\n\t"
+      "ds_read_b128 v[244:247], %[f1] offset:16384\n\t"
+      "ds_read_b128 v[248:251], %[f0] offset:34816\n\t"
+      "ds_read_b128 v[252:255], %[f1] offset:34816\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[224:231], %[q7], %[s0]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[232:239], %[q7], %[s1]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s0], v[240:247], %[q8], %[s0]\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %[s1], v[248:255], %[q8], %[s1]\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : [s0] "=&v"(s0), [s1] "=&v"(s1)
+      : [f0] "v"(f0), [f1] "v"(f1),
+        [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]),
+        [q5] "v"(q[5]), [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8])
+      : "memory", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218", "v219",
+        "v220", "v221", "v222", "v223", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232",
+        "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245",
+        "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255");
 }
 
 // Operand layout of MFMA 32x32x64 with 8-bit operands (probed on the box with one-hot
@@ -1153,18 +1251,17 @@ __device__ __forceinline__ f32x16 qk_tile_split(const i32x8* qh, const i32x8* ql
 // scale block and bytes 16..31 the second; the scale of block b for row (A) or column
 // (B) j comes from lane 32 b + j.
 //
-// Output product of the split path: per 32 dims, one MFMA whose first scale block holds
-// the tile's 32 tokens with P_hi and whose second block holds the same tokens with P_lo,
-// so A = V^T carries each token twice (bytes t and t + 16) and B = [hi codes | lo codes].
-// The tokens of lane half h are the 16 whose scores that half already holds (tokens
-// 4h + 8g + r, g, r = 0..3, in the scores' register order), so P needs no lane exchange.
-// V^T of output MFMA db (dims 32 db + l % 32) takes two 8-bit transpose reads per lane:
-// read t covers tokens 4h + 16t + {0..3, 8..11}; in each 16-lane group g, lane s addresses
-// token 4h + 16t + u % 4 + 8 (u / 4), u = s / 2, and dims 32 db + 16 (g % 2) + 8 (s % 2)
-// .. + 8 (raw chunk 2 db + g % 2, whose position in the row is swizzled with sswz), and
-// lane j receives dim 32 db + 16 (g % 2) + j of the 8 tokens.  vs[2t + (db & 1)] is the
-// lane's offset inside chunk group db / 2 (odd blocks flip position bit 1, byte-offset
-// bit 5).
+// Output product of a 64-token tile, per 32 dims: two MFMAs on the same V^T operand, one
+// with B = P'_hi, one with B = P'_lo.  Lane half h's bytes 0..15 are the 16 tokens of half
+// 0 whose scores that lane half holds (tokens 4h + 8g + r, g, r = 0..3, in the scores'
+// register order) and bytes 16..31 the same positions in half 1, so P needs no lane
+// exchange and V^T carries every token once.  V^T of dim block db (dims 32 db + l % 32)
+// takes four 8-bit transpose reads per lane: read (t, m) covers tokens 4h + 16t +
+// {0..3, 8..11} of half m; in each 16-lane group g, lane s addresses token
+// 4h + 16t + u % 4 + 8 (u / 4), u = s / 2, and dims 32 db + 16 (g % 2) + 8 (s % 2) .. + 8
+// (raw chunk 2 db + g % 2, whose position in the row is swizzled with sswz), and lane j
+// receives dim 32 db + 16 (g % 2) + j of the 8 tokens.  vs[2t + (db & 1)] is the lane's
+// offset inside chunk group db / 2 (odd blocks flip position bit 1, byte-offset bit 5).
 __device__ __forceinline__ void split_vt_offsets(int lane, int* vs) {
   const int g = lane >> 4, s = lane & 15, h = lane >> 5, u = s >> 1;
 #pragma unroll
@@ -1175,32 +1272,32 @@ __device__ __forceinline__ void split_vt_offsets(int lane, int* vs) {
     vs[2 * t + 1] = off ^ 32;
   }
 }
-// base[0..3]: the four offsets above plus the tile; dup[0..3]: the same addresses in
-// other registers (opaque to the compiler), so that the second copy of each operand half
-// is a load of its own straight into its registers rather than a register copy.
-__device__ __forceinline__ i32x8 split_vt_read(const uint32_t* base, const uint32_t* dup, int db) {
+__device__ __forceinline__ i32x8 vt64_read(const uint32_t* base, int db) {
   i32x2 r[4];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    r[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(at<i32x2>(base[2 * t + (db & 1)] + 2048 * (db >> 1)));
-    r[2 + t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(at<i32x2>(dup[2 * t + (db & 1)] + 2048 * (db >> 1)));
-  }
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      r[2 * m + t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          at<i32x2>(base[2 * t + (db & 1)] + 2048 * (db >> 1) + kHalfBytes * m));
   return i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
 }
-__device__ __forceinline__ uint32_t opaque(uint32_t x) {
-  uint32_t r;
-  asm("v_mov_b32 %0, %1" : "=v"(r) : "v"(x));
+
+// The lane id, computed where it is called (a volatile statement is never moved out of a
+// loop), for per-lane offsets that are cheaper to recompute than to keep in registers.
+__device__ __forceinline__ int lane_id_here() {
+  int r;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(r));
   return r;
 }
 
-// Output MFMA of the split path, c += V^T . P'^T: A = V^T codes at unit scale (E8M0
-// 127 in ua), B = P'^T codes with this lane's E8M0 scale sb.  Written as an assembly
-// statement, which stays where the schedule puts it (the compiler sinks the builtin
-// form past the softmax work it is meant to interleave with).  Hazards the compiler
-// cannot see: a vector instruction writing an operand needs two wait states before the
-// MFMA reads it (NOP: the first MFMA of a phase, whose P operand may just have been
-// assembled), and a read of the accumulators after the last MFMA waits for it
-// (mfma_drain).
+// Output MFMA of the FP8 path, c += V^T . P'^T: A = V^T codes at unit scale (E8M0 127 in
+// ua), B = P' codes with this row's E8M0 scale sb.  Written as an assembly statement,
+// which stays where the schedule puts it (the compiler sinks the builtin form past the
+// softmax work it is meant to interleave with).  Hazards the compiler cannot see: a
+// vector instruction writing an operand needs two wait states before the MFMA reads it
+// (NOP: the first MFMA of a phase, whose P operand may just have been assembled), and a
+// read of the accumulators after the last MFMA waits for it (mfma_drain).
 template <bool NOP = false>
 __device__ __forceinline__ void mfma_f8s(f32x16& c, const i32x8& a, const i32x8& b, int ua, int sb) {
   if (NOP)
@@ -1213,47 +1310,48 @@ __device__ __forceinline__ void mfma_f8s(f32x16& c, const i32x8& a, const i32x8&
 // wait states (more than the 16-pass MFMA's 19) before an accumulator may be read
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
-// Online softmax of one tile for the split path, in 16 pieces (one per output MFMA).  x:
-// raw scores of this lane (row l % 32, tokens 8 (v / 4) + 4 (l / 32) + v % 4), masked ones
-// -inf; c > 0 the row's score scale in log2 units.  Weights are p = 2^(x c - m) with the
-// reference m moved only when the tile's max exceeds it by more than 8, and then to
-// that max - 1, so p <= 2^8 and the row's max may grow by 7 before the accumulators
-// need rescaling (any row of the wavefront then rescales all 256 accumulators).
-// Each row's weights of the tile are carried as p' = p 2^e, with the integer e chosen so
-// that the tile's largest p' lies in [2^7, 2^8): p' = hi + lo, hi and lo E4M3, so every
-// weight within 2^-8 of the tile's largest keeps 8 significant bits and smaller ones an
-// absolute error of at most 2^-10, i.e. 2^-17 of the tile's largest, however far the tile
-// lies below the row's reference.  The output MFMA undoes 2^e with the B operand's E8M0
-// scale.
-// Output: alpha (factor for the accumulators before this tile's product), P'^T in pn
-// (dwords 0..3: the hi codes of the lane's 16 values in register order, dwords 4..7 their
-// lo codes: the output MFMA's two scale blocks) and sb, the E8M0 code of 2^-e (the low
-// lane half gives the hi block's scale, the high half the lo block's: the same).
+// Online softmax of one 64-token tile, in 32 pieces (one per output MFMA).  x: raw scores
+// of this lane (x[16 m + v]: half m, token 8 (v / 4) + 4 (l / 32) + v % 4 of it, row
+// l % 32), masked ones -inf; c > 0 the row's score scale in log2 units.  Weights are
+// p = 2^(x c - m) with the reference m moved only when the tile's max exceeds it by more
+// than 8, and then to that max - 1, so p <= 2^8 and the row's max may grow by 7 before the
+// accumulators need rescaling (any row of the wavefront then rescales all 256
+// accumulators).  Each row's weights of the tile are carried as p' = p 2^e, with the
+// integer e chosen so that the tile's largest p' lies in [2^7, 2^8): p' = hi + lo, hi and
+// lo E4M3, so every weight within 2^-8 of the tile's largest keeps 8 significant bits and
+// smaller ones an absolute error of at most 2^-10, i.e. 2^-17 of the tile's largest,
+// however far the tile lies below the row's reference.  The output MFMAs undo 2^e with the
+// B operand's E8M0 scale.  Output: alpha (factor for the accumulators before this tile's
+// product), the codes of hi (ph) and lo (pl), dword j holding values 4j .. 4j+3 (so
+// bytes 0..15 are half 0's values, bytes 16..31 half 1's), and sb, the E8M0 code of 2^-e.
 struct SplitPieces {
   float mt, m_new, ex, nm, acc, esc;
   bool need;
-  unsigned h[4], l[4];  // dword j: codes of values 4j .. 4j+3
 };
-__device__ __forceinline__ void split_piece(int k, Softmax& S, float* x, float c, SplitPieces& w, unsigned* pn,
-                                            float& alpha, int& sb) {
+__device__ __forceinline__ void split_piece64(int k, Softmax& S, float* x, float c, SplitPieces& w, unsigned* ph,
+                                              unsigned* pl, float& alpha, int& sb) {
   auto split4 = [&](int j) {  // values 4j .. 4j+3 -> dword j of the hi and lo codes
     unsigned hc = 0, lc = 0;
     e4m3_split_pair<false>(hc, lc, x[4 * j], x[4 * j + 1]);
     e4m3_split_pair<true>(hc, lc, x[4 * j + 2], x[4 * j + 3]);
-    w.h[j] = hc;
-    w.l[j] = lc;
+    ph[j] = hc;
+    pl[j] = lc;
   };
   if (k == 0) {
-    w.mt = max3(max3(max3(x[0], x[1], x[2]), x[3], x[4]), x[5], x[6]);
+    w.mt = max3(max3(max3(max3(x[0], x[1], x[2]), x[3], x[4]), x[5], x[6]), x[7], x[8]);
   } else if (k == 1) {
-    w.mt = max3(max3(max3(max3(w.mt, x[7], x[8]), x[9], x[10]), x[11], x[12]), x[13], max3(x[14], x[15], x[15]));
+    w.mt = max3(max3(max3(max3(max3(w.mt, x[9], x[10]), x[11], x[12]), x[13], x[14]), x[15], x[16]), x[17], x[18]);
   } else if (k == 2) {
-    w.mt = pair_max(w.mt) * c;  // -inf stays -inf (c > 0)
+    w.mt = max3(max3(max3(max3(max3(max3(w.mt, x[19], x[20]), x[21], x[22]), x[23], x[24]), x[25], x[26]), x[27],
+                     x[28]),
+                x[29], max3(x[30], x[31], x[31]));
   } else if (k == 3) {
+    w.mt = pair_max(w.mt) * c;  // -inf stays -inf (c > 0)
+  } else if (k == 4) {
     w.need = w.mt > S.m_used + 8.0f;
     w.m_new = w.need ? w.mt - 1.0f : S.m_used;
     w.ex = __builtin_amdgcn_exp2f(S.m_used - w.m_new);
-  } else if (k == 4) {
+  } else if (k == 5) {
     // (while no token has been seen the accumulators are zero and need no factor)
     alpha = (w.need && S.m_used != -INFINITY) ? w.ex : 1.0f;
     S.l_sum *= alpha;
@@ -1266,82 +1364,75 @@ __device__ __forceinline__ void split_piece(int k, Softmax& S, float* x, float c
     w.nm = (w.m_new == -INFINITY) ? 0.f : (float)e - w.m_new;
     sb = 127 - e;
     w.acc = 0.f;
-  } else if (k >= 5 && k < 13) {
-    const int v = 2 * (k - 5);
+  } else if (k >= 6 && k < 22) {
+    const int v = 2 * (k - 6);
     x[v] = __builtin_amdgcn_exp2f(fmaf(x[v], c, w.nm));
     x[v + 1] = __builtin_amdgcn_exp2f(fmaf(x[v + 1], c, w.nm));
     w.acc += x[v];
     w.acc += x[v + 1];
-    if (k == 8) split4(0);   // values 0..3 are done from step 6 on
-    if (k == 10) split4(1);
-    if (k == 12) split4(2);
-  } else if (k == 13) {
-    split4(3);
+    if (k >= 8 && (k & 1) == 0) split4((k - 8) / 2);  // values 4j .. 4j+3 are done from step 7 + 2j on
+  } else if (k == 22) {
+    split4(7);
     S.l_sum = fmaf(w.acc, w.esc, S.l_sum);  // sum of p = 2^-e sum of p'
-  } else if (k == 14) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      pn[j] = w.h[j];
-      pn[4 + j] = w.l[j];
-    }
   }
 }
 
-// Output product of tile i-1 (raw tile `raw`, P'^T in pp with B scales sbp) for the split
-// path, with the softmax of tile i in pieces between its 16 MFMAs; V^T reads run kAhead
-// MFMAs ahead.
+// Output product of tile i-1 (raw tile `raw`, P' codes ph/pl with scale sbp) for the FP8
+// path, with the softmax of tile i in pieces between its 32 MFMAs; V^T reads run kAhead
+// dim blocks ahead.
 template <int kAhead>
-__device__ __forceinline__ void output_phase_split(f32x16* o, uint32_t raw, const unsigned* pp, int sbp,
-                                                   const int* vs, float* x, Softmax& S, float c, unsigned* pn,
-                                                   float& alpha, int& sb) {
-  uint32_t base[4], dup[4];
+__device__ __forceinline__ void output_phase64(f32x16* o, uint32_t raw, const unsigned* ph, const unsigned* pl,
+                                               int sbp, const int* vs, float* x, Softmax& S, float c, unsigned* nh,
+                                               unsigned* nl, float& alpha, int& sb) {
+  uint32_t base[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    base[v] = raw + vs[v];
-    dup[v] = opaque(base[v]);
-  }
-  const i32x8 pb = {(int)pp[0], (int)pp[1], (int)pp[2], (int)pp[3], (int)pp[4], (int)pp[5], (int)pp[6], (int)pp[7]};
+  for (int v = 0; v < 4; ++v) base[v] = raw + vs[v];
+  const i32x8 bh = {(int)ph[0], (int)ph[1], (int)ph[2], (int)ph[3], (int)ph[4], (int)ph[5], (int)ph[6], (int)ph[7]};
+  const i32x8 bl = {(int)pl[0], (int)pl[1], (int)pl[2], (int)pl[3], (int)pl[4], (int)pl[5], (int)pl[6], (int)pl[7]};
   const int ua = 127;
   SplitPieces w;
   i32x8 va[kDimBlocks];
 #pragma unroll
-  for (int k = 0; k < kAhead; ++k) va[k] = split_vt_read(base, dup, k);
+  for (int k = 0; k < kAhead; ++k) va[k] = vt64_read(base, k);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int k = 0; k < kDimBlocks; ++k) {
-    if (k == 0) mfma_f8s<true>(o[k], va[k], pb, ua, sbp);
-    else mfma_f8s(o[k], va[k], pb, ua, sbp);
-    if (k + kAhead < kDimBlocks) va[k + kAhead] = split_vt_read(base, dup, k + kAhead);
-    split_piece(k, S, x, c, w, pn, alpha, sb);
+  for (int db = 0; db < kDimBlocks; ++db) {
+    if (db == 0) mfma_f8s<true>(o[db], va[db], bh, ua, sbp);
+    else mfma_f8s(o[db], va[db], bh, ua, sbp);
+    split_piece64(2 * db, S, x, c, w, nh, nl, alpha, sb);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_f8s(o[db], va[db], bl, ua, sbp);
+    if (db + kAhead < kDimBlocks) va[db + kAhead] = vt64_read(base, db + kAhead);
+    split_piece64(2 * db + 1, S, x, c, w, nh, nl, alpha, sb);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // The softmax of one tile on its own (the first tile of a range).
-__device__ __forceinline__ float softmax_split(Softmax& S, float* x, float c, unsigned* pn, int& sb) {
+__device__ __forceinline__ float softmax64(Softmax& S, float* x, float c, unsigned* nh, unsigned* nl, int& sb) {
   SplitPieces w;
   float alpha = 1.f;
 #pragma unroll
-  for (int k = 0; k < kDimBlocks; ++k) split_piece(k, S, x, c, w, pn, alpha, sb);
+  for (int k = 0; k < 2 * kDimBlocks; ++k) split_piece64(k, S, x, c, w, nh, nl, alpha, sb);
   return alpha;
 }
 
 // The output product of one tile on its own (the last tile of a range); the accumulators
 // may be read right after it.
-__device__ __forceinline__ void pv_split(f32x16* o, uint32_t raw, const unsigned* pp, int sbp, const int* vs) {
-  uint32_t base[4], dup[4];
+__device__ __forceinline__ void pv64(f32x16* o, uint32_t raw, const unsigned* ph, const unsigned* pl, int sbp,
+                                     const int* vs) {
+  uint32_t base[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    base[v] = raw + vs[v];
-    dup[v] = opaque(base[v]);
-  }
-  const i32x8 pb = {(int)pp[0], (int)pp[1], (int)pp[2], (int)pp[3], (int)pp[4], (int)pp[5], (int)pp[6], (int)pp[7]};
+  for (int v = 0; v < 4; ++v) base[v] = raw + vs[v];
+  const i32x8 bh = {(int)ph[0], (int)ph[1], (int)ph[2], (int)ph[3], (int)ph[4], (int)ph[5], (int)ph[6], (int)ph[7]};
+  const i32x8 bl = {(int)pl[0], (int)pl[1], (int)pl[2], (int)pl[3], (int)pl[4], (int)pl[5], (int)pl[6], (int)pl[7]};
   const int ua = 127;
 #pragma unroll
   for (int db = 0; db < kDimBlocks; ++db) {
-    const i32x8 va = split_vt_read(base, dup, db);
-    if (db == 0) mfma_f8s<true>(o[db], va, pb, ua, sbp);
-    else mfma_f8s(o[db], va, pb, ua, sbp);
+    const i32x8 va = vt64_read(base, db);
+    if (db == 0) mfma_f8s<true>(o[db], va, bh, ua, sbp);
+    else mfma_f8s(o[db], va, bh, ua, sbp);
+    mfma_f8s(o[db], va, bl, ua, sbp);
   }
   mfma_drain();
 }
@@ -1536,15 +1627,14 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
   __syncthreads();  // the next range reuses the LDS buffers
 }
 
-// One token range of one request on the FP8 split path (paged FP8 cache): the same
-// schedule as run_range (scores of tile i, then the output product of tile i-1 with the
-// softmax of tile i between its MFMAs), on raw tiles only, loads four tiles ahead.
-// kQ8 (cache format 3): the query rounded to E4M3 instead of split, scores on nine FP8
-// MFMAs (qk_tile_f8); everything else is the same.
+// One token range of one request on the FP8 path (paged FP8 cache, 64-token tiles
+// lt0 .. lt1 - 1 of the request): per tile i, the loads of tile i + 2, the scores of tile
+// i, then the output product of tile i-1 with the softmax of tile i between its MFMAs,
+// then one barrier.  kQ8 (cache format 3): the query rounded to E4M3 instead of split,
+// one score MFMA per half and K-step; everything else is the same.
 template <bool kQ8>
-__device__ __forceinline__ void run_range_split(const DecodeParams& p, uint32_t smem, int b, int n, int rg, int lt0,
-                                                int lt1, int64_t slot) {
-  using PP = Pipe<kFmtFp8>;
+__device__ __forceinline__ void run_range_fp8(const DecodeParams& p, uint32_t smem, int b, int n, int rg, int lt0,
+                                              int lt1, int64_t slot) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
@@ -1554,7 +1644,7 @@ __device__ __forceinline__ void run_range_split(const DecodeParams& p, uint32_t 
   const int rc = min(row0 + my_row, p.rows - 1);  // rows past the end repeat the last row
   const int nt = lt1 - lt0;
   i32x8 qh[9], ql[kQ8 ? 1 : 9];  // the query row, split (q_split) or rounded (q_round_e4m3, in qh)
-  float c = 0.f;       // its score scale (set with the split)
+  float c = 0.f;                  // its score scale (set with the split)
 
   const int vis = max(n - p.q_len + rc / p.H + 1, 0);
   const int lo = p.window > 0 ? max(vis - p.window, 0) : 0;
@@ -1565,81 +1655,102 @@ __device__ __forceinline__ void run_range_split(const DecodeParams& p, uint32_t 
     max_lo = max(max_lo, __shfl_xor(max_lo, o));
   }
 
-  uint32_t fq[2];  // score reads: chunks 2h, 2h+1 of token row l % 32 (as in qk_tile_f8, swizzled with sswz)
+  // per-lane LDS offsets of the score and transpose reads; recomputed in each tile from the
+  // lane id (a few integer instructions) rather than held in registers across the loop
+  // (lane_id_here keeps the compiler from hoisting them out of it again)
+  auto score_offsets = [&](uint32_t* fq) {
+    const int l = lane_id_here(), r = l & 31, h = l >> 5;
 #pragma unroll
-  for (int e = 0; e < 2; ++e) fq[e] = 64 * lr + 16 * ((2 * lh + e) ^ sswz(lr));
-  int vs[4];
-  split_vt_offsets(lane, vs);
+    for (int e = 0; e < 2; ++e) fq[e] = 64 * r + 16 * ((2 * h + e) ^ sswz(r));
+  };
 
   f32x16 o[kDimBlocks];
 #pragma unroll
   for (int db = 0; db < kDimBlocks; ++db) o[db] = f32x16{};
   Softmax S{-INFINITY, 0.f, 0.f};
-  unsigned pp[8];
-  int sb_prev = 127;  // B operand scales of pp
+  unsigned ph[8], pl[8];  // P' codes of the previous tile (hi, lo)
+  int sb_prev = 127;      // and their E8M0 scale
   float alpha_prev = 1.f;
 
   const Src src{&p, b, n};
-  const int nloads = (PP::kLoads - wave + kWaves - 1) / kWaves;  // load instructions per tile here
   auto raw_buf = [&](int i) {
-    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(smem + (uint32_t)((i % PP::kRaw) * PP::kRawBytes)));
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(smem + (uint32_t)((i & 3) * kT8Bytes)));
   };
-  auto entry = [&](int i) { return table_entry(src, (lt0 + min(i, nt - 1)) * kTileTokens); };
-  auto issue = [&](int i, int e) {
-    load_fp8_raw(src, (lt0 + i) * kTileTokens, page_start(src, e), raw_buf(i), wave, lane);
+  static_assert(Pipe<kFmtFp8>::kRaw == 4 && Pipe<kFmtFp8>::kRawBytes == kT8Bytes, "four 64-token raw tiles");
+  // block-table entries of tile i's halves (tiles past the range repeat the last one);
+  // both are read, even when one page holds the whole tile, so that neither read waits
+  // for the other (they are waited for where the next tile's loads use them)
+  auto entry0 = [&](int i) { return table_entry(src, (lt0 + min(i, nt - 1)) * kT8); };
+  auto entry1 = [&](int i) { return table_entry(src, half1_start(src, (lt0 + min(i, nt - 1)) * kT8)); };
+  auto issue = [&](int i, int e0, int e1) {
+    load_fp8_tile64(src, (lt0 + i) * kT8, e0, e1, raw_buf(i), wave, lane);
   };
-  int e_next = 0;
+  int en0 = 0, en1 = 0;  // entries of the next tile to load
 
   auto body = [&](int i, auto FIRST) {
     constexpr bool first = decltype(FIRST)::value;
-    float x[16];
-    if (i + PP::kAhead < nt) {
-      issue(i + PP::kAhead, e_next);
-      e_next = entry(i + PP::kAhead + 1);
+    float x[32];
+    if (i + kT8Ahead < nt) {
+      issue(i + kT8Ahead, en0, en1);
+      en0 = entry0(i + kT8Ahead + 1);
+      en1 = entry1(i + kT8Ahead + 1);
     }
     if (!first && __any(alpha_prev != 1.f)) rescale(o, alpha_prev);
-    f32x16 s;
-    if constexpr (kQ8) s = qk_tile_f8(qh, raw_buf(i), fq);
-    else s = qk_tile_split(qh, ql, raw_buf(i), fq);
+    f32x16 s0, s1;
+    {
+      uint32_t fq[2];
+      score_offsets(fq);
+      if constexpr (kQ8) qk_tile64_f8(qh, raw_buf(i), fq, s0, s1);
+      else qk_tile64_split(qh, ql, raw_buf(i), fq, s0, s1);
+    }
 #pragma unroll
-    for (int v = 0; v < 16; ++v) x[v] = s[v];
-    const int tbase = (lt0 + i) * kTileTokens;
-    if (tbase + kTileTokens > min_vis || tbase < max_lo) {
-      // value v (token tbase + 4 (l / 32) + 8 (v/4) + v%4 of the lane) visible iff in [flo, lim)
+    for (int v = 0; v < 16; ++v) {
+      x[v] = s0[v];
+      x[16 + v] = s1[v];
+    }
+    const int tbase = (lt0 + i) * kT8;
+    if (tbase + kT8 > min_vis || tbase < max_lo) {
+      // value 16 m + v: token tbase + 32 m + 8 (v / 4) + 4 (l / 32) + v % 4 of the lane,
+      // visible iff in [lo, vis)
       const int lim = vis - tbase - 4 * lh, flo = lo - tbase - 4 * lh;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int t = 8 * (v >> 2) + (v & 3);
+      for (int v = 0; v < 32; ++v) {
+        const int t = 32 * (v >> 4) + 8 * ((v >> 2) & 3) + (v & 3);
         x[v] = (t < lim && t >= flo) ? x[v] : -INFINITY;
       }
     }
-    unsigned pn[8];
+    unsigned nh[8], nl[8];
     float alpha = 1.f;
     int sbn = 127;
-    if (first) alpha = softmax_split(S, x, c, pn, sbn);
-    else output_phase_split<2>(o, raw_buf(i - 1), pp, sb_prev, vs, x, S, c, pn, alpha, sbn);
+    if (first) {
+      alpha = softmax64(S, x, c, nh, nl, sbn);
+    } else {
+      int vs[4];
+      split_vt_offsets(lane_id_here(), vs);
+      output_phase64<2>(o, raw_buf(i - 1), ph, pl, sb_prev, vs, x, S, c, nh, nl, alpha, sbn);
+    }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) pp[k] = pn[k];
+    for (int k = 0; k < 8; ++k) {
+      ph[k] = nh[k];
+      pl[k] = nl[k];
+    }
     sb_prev = sbn;
     alpha_prev = alpha;
-    // tile i+1 must have landed (its loads were issued kAhead - 1 tiles ago); the loads of
-    // the tiles after it may stay in flight (near the end of the range: wait for all)
-    static_assert(PP::kAhead == 4 && kFp8Loads == 18, "load counts below");
-    if (i + PP::kAhead < nt) {
-      if (wave < 2) asm volatile("s_waitcnt vmcnt(15)" ::: "memory");  // 3 tiles x 5 loads
-      else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");           // 3 tiles x 4 loads
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+    // tile i+1 must have landed (its loads were issued one tile ago); the loads of tile
+    // i+2 may stay in flight
+    static_assert(kT8Ahead == 2 && kT8Loads == 9, "load counts below");
+    if (i + kT8Ahead < nt) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
 
   // the first tiles' loads go out before the query is read and split, so that their
   // latency and the query's overlap
-  const int pro = min(nt, PP::kAhead);
+  const int pro = min(nt, kT8Ahead);
   if (nt > 0) {
-    for (int k = 0; k < pro; ++k) issue(k, entry(k));
-    e_next = entry(PP::kAhead);
+    for (int k = 0; k < pro; ++k) issue(k, entry0(k), entry1(k));
+    en0 = entry0(kT8Ahead);
+    en1 = entry1(kT8Ahead);
   }
   const uint16_t* qrow = p.q + ((int64_t)b * p.rows + rc) * kLatent;
   const uint16_t* prow = p.qpe + ((int64_t)b * p.rows + rc) * kRope;
@@ -1654,12 +1765,15 @@ __device__ __forceinline__ void run_range_split(const DecodeParams& p, uint32_t 
   }
 
   if (nt > 0) {
-    wait_vmcnt((pro - 1) * nloads);  // tile 0
+    if (pro > 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // tile 0
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     body(0, std::true_type{});
     for (int i = 1; i < nt; ++i) body(i, std::false_type{});
     if (__any(alpha_prev != 1.f)) rescale(o, alpha_prev);
-    pv_split(o, raw_buf(nt - 1), pp, sb_prev, vs);
+    int vs[4];
+    split_vt_offsets(lane, vs);
+    pv64(o, raw_buf(nt - 1), ph, pl, sb_prev, vs);
   }
 
   // ---- epilogue: normalised partial O and its lse (normalised by the unrounded sum) ----
@@ -1712,8 +1826,9 @@ void decode_contig_kernel(const DecodeParams p) {
 // unique because the ranges are ordered.  seg_first[b] / seg_last[b] record the first
 // and last range touching request b; info[0] records W.
 //
-// kSegmentCost is what a segment's fixed work costs in tiles: its query load, the
-// pipeline fill and drain, and the partial store.  Measured per workgroup on the
+// kSegmentCost is what a segment's fixed work costs in 32-token tiles (the FP8 formats,
+// whose tiles hold 64 tokens, count half as many): its query load, the pipeline fill and
+// drain, and the partial store.  Measured per workgroup on the
 // B=64, H=128 FP8 workload (with the bf16-dequantising kernel this path had before the
 // split one): about 17 us per extra segment against about 1.6 us per tile.
 // An empty range can only sit where one request ends and the next begins, so every
@@ -1725,16 +1840,21 @@ template <int FMT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_paged_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<FMT>()];
+  // tokens per tile (the FP8 formats stream 64-token tiles) and the per-segment cost in
+  // those tiles (the same 320 tokens' worth for every format)
+  constexpr bool kFp8Fmt = FMT == kFmtFp8 || FMT == kFmtFp8Q;
+  constexpr int TT = kFp8Fmt ? kT8 : kTileTokens;
+  constexpr int SC = kSegmentCost * kTileTokens / TT;
   __shared__ int wsum[2][kWaves];
   __shared__ int found[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int max_len = p.max_blocks * p.page_size;
   // with a window, a request's tiles start at the one holding its first visible token
   // (query 0 at position n - q_len sees from n - q_len - window + 1)
-  auto first_tile = [&](int n) { return p.window > 0 ? max(n - p.q_len - p.window + 1, 0) / kTileTokens : 0; };
+  auto first_tile = [&](int n) { return p.window > 0 ? max(n - p.q_len - p.window + 1, 0) / TT : 0; };
   auto tiles_of = [&](int b) {
     const int n = min(max(p.seq_lens[b], 0), max_len);
-    return n > 0 ? (n + kTileTokens - 1) / kTileTokens - first_tile(n) : 0;
+    return n > 0 ? (n + TT - 1) / TT - first_tile(n) : 0;
   };
 
   // workgroup id -> (range w, row group rg); the row groups of one range sit 8 ids
@@ -1747,7 +1867,7 @@ void decode_paged_kernel(const DecodeParams p) {
 
   // tile counts and costs: thread t sums requests [s0, s1); exclusive scans give each
   // chunk's first tile and first cost position, and the totals T and W
-  auto cost_of = [](int nb) { return nb > 0 ? nb + kSegmentCost : 0; };
+  auto cost_of = [](int nb) { return nb > 0 ? nb + SC : 0; };
   if (tid == 0) found[0] = found[1] = found[2] = found[3] = 0;  // an empty range unless set below
   const int per = (p.B + kThreads - 1) / kThreads;
   const int s0 = min(tid * per, p.B), s1 = min(s0 + per, p.B);
@@ -1786,7 +1906,7 @@ void decode_paged_kernel(const DecodeParams p) {
       if (c < cb + cost_of(nb)) {
         req = b;
         first = tb;
-        tile = tb + (int)max(c - cb - kSegmentCost, (int64_t)0);
+        tile = tb + (int)max(c - cb - SC, (int64_t)0);
         return;
       }
       cb += cost_of(nb);
@@ -1818,9 +1938,9 @@ void decode_paged_kernel(const DecodeParams p) {
     // these are the same in every lane (read from LDS words and tables that all lanes
     // share); saying so keeps the page addresses in scalar registers
     auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
-    if constexpr (FMT == kFmtFp8 || FMT == kFmtFp8Q)
-      run_range_split<FMT == kFmtFp8Q>(p, lds_addr((lds_ptr)smem), uni(b), uni(n), rg, uni(t - base + tf),
-                                        uni(seg_end - base + tf), (int64_t)w + uni(b));
+    if constexpr (kFp8Fmt)
+      run_range_fp8<FMT == kFmtFp8Q>(p, lds_addr((lds_ptr)smem), uni(b), uni(n), rg, uni(t - base + tf),
+                                      uni(seg_end - base + tf), (int64_t)w + uni(b));
     else
       run_range<FMT, true>(p, lds_addr((lds_ptr)smem), uni(b), uni(n), rg, uni(t - base + tf),
                            uni(seg_end - base + tf), (int64_t)w + uni(b));

@@ -3,9 +3,10 @@ library's documented interface (include/mla_decode.h: mla_plan_paged,
 mla_paged_workspace_bytes, mla_paged_decode_partials), for bit-exact checks of the
 integer work the decode launch does on the device.  Test infrastructure only.
 
-The plan: request b holds tiles(b) = ceil(n_b / 32) 32-token tiles (with a sliding
-window, counted from the tile holding its first visible token) and costs
-tiles(b) + 10 when it has any.  On the cost axis each request is its 10-unit overhead
+The plan: request b holds tiles(b) = ceil(n_b / T) tiles of T tokens (T = 64 for the FP8
+cache formats, 32 for the others; with a sliding window, counted from the tile holding its
+first visible token) and costs tiles(b) + C when it has any, C = 320 / T (the same
+320 tokens' worth of segment overhead for every format).  On the cost axis each request is its C-unit overhead
 part followed by its tiles; range w of the NS ranges covers the cost interval
 [w W / NS, (w + 1) W / NS) of the total cost W and takes the tiles that fall in it.  A
 range that covers parts of several requests runs one segment per request; segment
@@ -25,6 +26,15 @@ import numpy as np
 
 TILE = 32
 SEGMENT_COST = 10
+
+
+def tile_tokens(fmt: int) -> int:
+    """Tokens per tile of a cache format: 64 for FP8 (formats 1 and 3), else 32."""
+    return 64 if fmt in (1, 3) else 32
+
+
+def segment_cost(tile: int) -> int:
+    return SEGMENT_COST * TILE // tile
 
 
 def _round_up(x: int, a: int) -> int:
@@ -52,18 +62,19 @@ class Segment:
     t1: int       # one past the last token, clipped to the request's length
 
 
-def plan(seq_lens, max_len: int, num_splits: int, q_len: int = 1, window: int = 0):
+def plan(seq_lens, max_len: int, num_splits: int, q_len: int = 1, window: int = 0, tile: int = TILE):
     """Returns (segments, seg_first, seg_last, W): the segments in range order, the
     first / last range per request (-1 where the request has no tiles), and the total
     cost."""
     n = [min(max(int(x), 0), max_len) for x in seq_lens]
     B = len(n)
+    sc = segment_cost(tile)
 
     def first_tile(nb):
-        return max(nb - q_len - window + 1, 0) // TILE if window > 0 else 0
+        return max(nb - q_len - window + 1, 0) // tile if window > 0 else 0
 
-    tiles = [(-(-nb // TILE)) - first_tile(nb) if nb > 0 else 0 for nb in n]
-    cost = [t + SEGMENT_COST if t > 0 else 0 for t in tiles]
+    tiles = [(-(-nb // tile)) - first_tile(nb) if nb > 0 else 0 for nb in n]
+    cost = [t + sc if t > 0 else 0 for t in tiles]
     W = sum(cost)
     T = sum(tiles)
     cstart = np.concatenate([[0], np.cumsum(cost)]).astype(np.int64)
@@ -73,7 +84,7 @@ def plan(seq_lens, max_len: int, num_splits: int, q_len: int = 1, window: int = 
         # the request whose cost span holds c, its first tile, and the tile c maps to
         for b in range(B):
             if cost[b] and c < cstart[b] + cost[b]:
-                return b, int(tstart[b]), int(tstart[b] + max(c - cstart[b] - SEGMENT_COST, 0))
+                return b, int(tstart[b]), int(tstart[b] + max(c - cstart[b] - sc, 0))
         raise AssertionError("cost position past the batch")
 
     segs = []
@@ -95,7 +106,7 @@ def plan(seq_lens, max_len: int, num_splits: int, q_len: int = 1, window: int = 
                 continue
             seg_end = min(t1, base + nb)
             tf = first_tile(n[b])
-            segs.append(Segment(w, b, w + b, (t - base + tf) * TILE, min((seg_end - base + tf) * TILE, n[b])))
+            segs.append(Segment(w, b, w + b, (t - base + tf) * tile, min((seg_end - base + tf) * tile, n[b])))
             if t == base:
                 seg_first[b] = w
             if seg_end == base + nb:

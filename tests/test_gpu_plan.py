@@ -50,7 +50,7 @@ def _check_plan_and_slots(w, ns, max_slots=None, seed=0):
     # the separate launches give exactly what mla_paged_decode gives
     assert np.array_equal(o_c, o_r) and np.array_equal(l_c, l_r)
     max_len = w.max_blocks * w.page_size
-    segs, first, last, W = pm.plan(w.seq_lens, max_len, ns, w.q_len)
+    segs, first, last, W = pm.plan(w.seq_lens, max_len, ns, w.q_len, tile=pm.tile_tokens(w.fmt))
     o_part, lse_part, dfirst, dlast, info = _parse(ws, w.B, w.q_len, w.H, ns)
     assert int(info[0]) == W
     for b in range(w.B):

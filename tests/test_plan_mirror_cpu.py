@@ -11,8 +11,8 @@ import mla_split_kv_02_amd as mla
 import plan_mirror as pm
 
 
-def _check_partition(lens, ns, q_len=1, window=0, max_len=1 << 20):
-    segs, first, last, W = pm.plan(lens, max_len, ns, q_len, window)
+def _check_partition(lens, ns, q_len=1, window=0, max_len=1 << 20, tile=32):
+    segs, first, last, W = pm.plan(lens, max_len, ns, q_len, window, tile)
     n = [min(max(x, 0), max_len) for x in lens]
     cover = {b: [] for b in range(len(lens))}
     slots = set()
@@ -26,15 +26,16 @@ def _check_partition(lens, ns, q_len=1, window=0, max_len=1 << 20):
         if n[b] == 0:
             assert not parts and first[b] == -1 and last[b] == -1
             continue
-        lo = (max(n[b] - q_len - window + 1, 0) // 32) * 32 if window > 0 else 0
+        lo = (max(n[b] - q_len - window + 1, 0) // tile) * tile if window > 0 else 0
         parts.sort()
         assert parts[0][0] == lo and parts[-1][1] == n[b]
         for a, c in zip(parts, parts[1:]):
             assert a[1] == c[0] and a[2] < c[2]          # contiguous, ranges increasing
-            assert a[1] % 32 == 0                        # cuts fall on tile boundaries
+            assert a[1] % tile == 0                      # cuts fall on tile boundaries
         assert first[b] == parts[0][2] and last[b] == parts[-1][2]
-    tiles = [-(-x // 32) - ((max(x - q_len - window + 1, 0) // 32) if window > 0 else 0) if x > 0 else 0 for x in n]
-    assert W == sum(t + pm.SEGMENT_COST for t in tiles if t > 0)
+    tiles = [-(-x // tile) - ((max(x - q_len - window + 1, 0) // tile) if window > 0 else 0) if x > 0 else 0
+             for x in n]
+    assert W == sum(t + pm.segment_cost(tile) for t in tiles if t > 0)
     return segs
 
 
@@ -44,9 +45,10 @@ def test_mirror_partitions_random_batches(seed):
     B = int(rng.integers(1, 40))
     lens = rng.integers(0, 3000, size=B)
     lens[rng.random(B) < 0.2] = 0
-    for ns in (1, 2, 3, 7, 64, 256, 1000):
-        _check_partition(lens.tolist(), ns)
-        _check_partition(lens.tolist(), ns, q_len=2, window=int(rng.integers(1, 500)))
+    for tile in (32, 64):
+        for ns in (1, 2, 3, 7, 64, 256, 1000):
+            _check_partition(lens.tolist(), ns, tile=tile)
+            _check_partition(lens.tolist(), ns, q_len=2, window=int(rng.integers(1, 500)), tile=tile)
 
 
 def test_mirror_one_range_is_one_segment_per_request():
@@ -61,6 +63,13 @@ def test_mirror_balances_cost():
     the overhead part), i.e. at tiles 242, 495 and 747."""
     segs = _check_partition([32000], 4)
     assert [(s.t0 // 32, s.t1 // 32) for s in segs] == [(0, 242), (242, 495), (495, 747), (747, 1000)]
+
+
+def test_mirror_balances_cost_64_token_tiles():
+    """The same request in 64-token tiles (500 tiles + 5 overhead units = 505): the cost
+    cuts fall at 126, 252 and 378, i.e. at tiles 121, 247 and 373."""
+    segs = _check_partition([32000], 4, tile=64)
+    assert [(s.t0 // 64, s.t1 // 64) for s in segs] == [(0, 121), (121, 247), (247, 373), (373, 500)]
 
 
 def test_layout_matches_library_size():
