@@ -111,8 +111,8 @@ int mla_plan_contig(int num_cus, int B, int S_kv, int* kv_len_per_split, int* nu
  * on the device from device seq_lens (so no host copy of them is needed: the TokenSpeed
  * page avoids a device-to-host sync for the same reason, _init_prefill_metadata).  The
  * ranges are of about equal cost, where a request costs its tiles plus a fixed overhead
- * of 320 tokens' worth of tiles (what starting a request in a workgroup costs: query
- * load, pipeline fill, partial store).  This returns the range count that fills the
+ * (what starting a request in a workgroup costs: query load, pipeline fill, partial
+ * store) of 8 tiles for the FP8 formats and 10 for the others.  This returns the range count that fills the
  * device once: num_cus / ceil(q_len * H / 128), at least 1. */
 int mla_plan_paged(int num_cus, int B, int q_len, int H, int* num_splits);
 

@@ -278,15 +278,14 @@ __device__ __forceinline__ void load_bf16_tile(const Src& S, int tb, const uint8
 // 16 p, p = (c % 4) ^ sswz(r).  Instruction j = 4m + w covers chunk group j / 2 of rows
 // 16 (j % 2) ..: lane l takes row 16 (w % 2) + l / 4 and the chunk 4 (w / 2 + 2m) + c % 4
 // that belongs at position l % 4.
-// The swizzle: row bit 2 flips position bit 1 and row bit 3 position bit 0 (and row bit 4
-// position bit 0 again).  The score reads (two 16-byte chunks of one row per lane and
-// step) stay conflict-free: rows r, r+4, r+8, r+12 at one logical chunk take four
-// different positions.  So do the 8-bit transpose reads, where one half-wavefront reads
-// two adjacent chunks (lane groups g = 0, 1) of rows 8t .. 8t+7: rows u and u+4 share a
-// bank row (256 bytes apart), and their positions differ in bit 1 while the two chunks
-// differ in bit 0, so the four (row, chunk) pairs of a bank row take four different
-// positions.
-__device__ __forceinline__ int sswz(int r) { return (((r >> 1) & 2) | ((r >> 3) & 1)) ^ ((r >> 4) & 1); }
+// The swizzle: row bits 2 and 3 flip position bits 0 and 1 (and row bit 4 position bit 0
+// again).  A row is 64 bytes, so the bank of (row r, position p) depends on r % 4 and p.
+// The score reads (16 lanes per cycle: rows r .. r+15 at one logical chunk) are
+// conflict-free: the four rows of each residue mod 4 take four different positions.  So
+// are the 8-bit transpose reads of the 64-token loop (32 lanes per cycle: tokens
+// b + {0..3, 8..11} with b % 16 in {0, 4}, two adjacent chunks, two 8-byte halves): the
+// tokens j and j + 8 of one residue differ in position bit 1 and the two chunks in bit 0.
+__device__ __forceinline__ int sswz(int r) { return ((r >> 2) & 3) ^ ((r >> 4) & 1); }
 
 __device__ __forceinline__ void load_fp8_raw(const Src& S, int tb, const uint8_t* pg, uint32_t st, int wave, int lane) {
   const int rip = tb & (S.p->page_size - 1);
@@ -1826,25 +1825,27 @@ void decode_contig_kernel(const DecodeParams p) {
 // unique because the ranges are ordered.  seg_first[b] / seg_last[b] record the first
 // and last range touching request b; info[0] records W.
 //
-// kSegmentCost is what a segment's fixed work costs in 32-token tiles (the FP8 formats,
-// whose tiles hold 64 tokens, count half as many): its query load, the pipeline fill and
-// drain, and the partial store.  Measured per workgroup on the
-// B=64, H=128 FP8 workload (with the bf16-dequantising kernel this path had before the
-// split one): about 17 us per extra segment against about 1.6 us per tile.
+// kSegmentCost is what a segment's fixed work costs in 32-token tiles, kSegmentCostT8 the
+// same for the FP8 formats in their 64-token tiles: the query load and split, the
+// pipeline fill and drain, and the partial store.  Measured per workgroup (end time
+// against tokens and segments over the 256 ranges of the B=64, H=128 FP8 workload):
+// about 24 us per segment against about 2.8 us per 64-token tile, i.e. 8 tiles; the
+// 32-token figure (17 us against 1.6 us per tile) is from the bf16-dequantising loop.
 // An empty range can only sit where one request ends and the next begins, so every
 // range between seg_first[b] and seg_last[b] holds tiles of b exactly when its cost
 // interval is not empty (the combine relies on this).
 constexpr int kSegmentCost = 10;
+constexpr int kSegmentCostT8 = 8;
 
 template <int FMT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_paged_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<FMT>()];
   // tokens per tile (the FP8 formats stream 64-token tiles) and the per-segment cost in
-  // those tiles (the same 320 tokens' worth for every format)
+  // those tiles
   constexpr bool kFp8Fmt = FMT == kFmtFp8 || FMT == kFmtFp8Q;
   constexpr int TT = kFp8Fmt ? kT8 : kTileTokens;
-  constexpr int SC = kSegmentCost * kTileTokens / TT;
+  constexpr int SC = kFp8Fmt ? kSegmentCostT8 : kSegmentCost;
   __shared__ int wsum[2][kWaves];
   __shared__ int found[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;

@@ -5,8 +5,8 @@ integer work the decode launch does on the device.  Test infrastructure only.
 
 The plan: request b holds tiles(b) = ceil(n_b / T) tiles of T tokens (T = 64 for the FP8
 cache formats, 32 for the others; with a sliding window, counted from the tile holding its
-first visible token) and costs tiles(b) + C when it has any, C = 320 / T (the same
-320 tokens' worth of segment overhead for every format).  On the cost axis each request is its C-unit overhead
+first visible token) and costs tiles(b) + C when it has any, C = 8 for T = 64 and 10 for
+T = 32 (the segment overhead in tiles).  On the cost axis each request is its C-unit overhead
 part followed by its tiles; range w of the NS ranges covers the cost interval
 [w W / NS, (w + 1) W / NS) of the total cost W and takes the tiles that fall in it.  A
 range that covers parts of several requests runs one segment per request; segment
@@ -25,7 +25,7 @@ from dataclasses import dataclass
 import numpy as np
 
 TILE = 32
-SEGMENT_COST = 10
+SEGMENT_COST = {32: 10, 64: 8}  # per-segment overhead in tiles, by tile size
 
 
 def tile_tokens(fmt: int) -> int:
@@ -34,7 +34,7 @@ def tile_tokens(fmt: int) -> int:
 
 
 def segment_cost(tile: int) -> int:
-    return SEGMENT_COST * TILE // tile
+    return SEGMENT_COST[tile]
 
 
 def _round_up(x: int, a: int) -> int:

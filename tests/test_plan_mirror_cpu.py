@@ -66,10 +66,10 @@ def test_mirror_balances_cost():
 
 
 def test_mirror_balances_cost_64_token_tiles():
-    """The same request in 64-token tiles (500 tiles + 5 overhead units = 505): the cost
-    cuts fall at 126, 252 and 378, i.e. at tiles 121, 247 and 373."""
+    """The same request in 64-token tiles (500 tiles + 8 overhead units = 508): the cost
+    cuts fall at 127, 254 and 381, i.e. at tiles 119, 246 and 373."""
     segs = _check_partition([32000], 4, tile=64)
-    assert [(s.t0 // 64, s.t1 // 64) for s in segs] == [(0, 121), (121, 247), (247, 373), (373, 500)]
+    assert [(s.t0 // 64, s.t1 // 64) for s in segs] == [(0, 119), (119, 246), (246, 373), (373, 500)]
 
 
 def test_layout_matches_library_size():
