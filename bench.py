@@ -22,9 +22,11 @@ Timing.  Before the warm-up, steps run for --settle-ms of wall time so that the 
 have settled (the first launches on a fresh GPU run ~20% slower); the settle steps are
 reported apart from the warm-up.  The decode and combine launches are bracketed with
 HIP events on the launch stream; per-launch decode times go to stderr.  Workloads whose
-streamed bytes would fit twice in the 256 MB MALL are flushed between steps (a 1 GiB
-write); their value and times then come from the events (the wall clock includes the
-flush), and their warm time is reported too.
+streamed bytes would fit twice in the 256 MB MALL are flushed between steps by reading
+a 1 GiB buffer (a read leaves the caches holding clean lines; a write would leave
+dirty ones whose write-back then competes with the decode's own reads); their value and
+times then come from the events (the wall clock includes the flush), and their warm
+time is reported too.
 """
 
 from __future__ import annotations
@@ -222,7 +224,7 @@ def timed_steps(torch, steps, decode, combine, flush_buf=None):
     t0 = time.perf_counter()
     for k in range(steps):
         if flush_buf is not None:
-            flush_buf.fill_(k & 0x7F)
+            flush_buf[1].copy_(flush_buf[0].max())  # reads the whole buffer
         ev[k][0].record()
         decode()
         ev[k][1].record()
@@ -275,7 +277,9 @@ def run(args, w, mla, torch, np, gen):
                "kv_len_per_split": L, "num_splits": int(op.shape[2])}
     step = lambda: (decode(), combine())
     flush = {"on": True, "off": False}.get(args.flush, kvbytes < 2 * MALL_BYTES)
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if flush else None
+    # [0]: 1 GiB read before each timed step, [1]: where the read's result goes
+    flush_buf = (torch.ones(1 << 28, dtype=torch.int32, device=dev), torch.zeros((), dtype=torch.int32, device=dev)) \
+        if flush else None
 
     n_settle, settle_ms = settle(step, torch, args.settle_ms)
     log(f"[bench] settle: {n_settle} steps in {settle_ms} ms")
@@ -296,7 +300,7 @@ def run(args, w, mla, torch, np, gen):
         _, wdec, wcomb = timed_steps(torch, args.steps, decode, combine, None)
         cfg["warm_decode_ms"] = round(float(np.mean(wdec)), 5)
         cfg["warm_combine_ms"] = round(float(np.mean(wcomb)), 5)
-        cfg["value_from"] = "hip events (decode + combine), L2/MALL flushed before each step"
+        cfg["value_from"] = "hip events (decode + combine), L2/MALL flushed (1 GiB read) before each step"
     else:
         ms_step = wall / args.steps * 1e3
         cfg["value_from"] = "wall clock over the timed steps"

@@ -520,16 +520,18 @@ __device__ __forceinline__ f32x16 qk_tile(const bf16x8* q, uint32_t tile, const 
 // chunks apart, i.e. position bit 2 (byte-offset bit 6) flipped inside the same group;
 // 64 dims apart are one group further; tokens 16 apart have position bit 2 of the
 // swizzle flipped, so the second K-step flips byte-offset bit 6 as well; vb[2e + 1] is
-// vb[2e] with that bit flipped).  pp holds P^T.
-__device__ __forceinline__ void pv_tile(f32x16* o, uint32_t tile, const unsigned* pp, const int* vb) {
+// vb[2e] with that bit flipped).  pp holds P^T.  NB blocks from block db0 (even) into
+// o[0 .. NB): the wavefront's share of the 512 dims when several share one row block.
+template <int NB = kDimBlocks>
+__device__ __forceinline__ void pv_tile(f32x16* o, uint32_t tile, const unsigned* pp, const int* vb, int db0 = 0) {
   uint32_t base[4];  // [e][db & 1]
 #pragma unroll
-  for (int x = 0; x < 4; ++x) base[x] = tile + vb[x];
+  for (int x = 0; x < 4; ++x) base[x] = tile + vb[x] + kGroupBytes * (db0 >> 1);
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pp[4 * ks], pp[4 * ks + 1], pp[4 * ks + 2], pp[4 * ks + 3]});
 #pragma unroll
-    for (int db = 0; db < kDimBlocks; ++db) {
+    for (int db = 0; db < NB; ++db) {
       const uint32_t off = kGroupBytes * (db >> 1) + 16 * 128 * ks;
       const int flip = (db & 1) ^ ks;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at<s16x4>(base[flip] + off));
@@ -544,12 +546,13 @@ __device__ __forceinline__ void pv_tile(f32x16* o, uint32_t tile, const unsigned
 // statement (the FP8 split path's output product), which the compiler cannot see.
 __device__ __forceinline__ void mfma_drain_any() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
-// o *= alpha in place in the accumulation registers, one value at a time through one
-// vector register.
+// o *= alpha in place in the accumulation registers (NB blocks), one value at a time
+// through one vector register.
+template <int NB = kDimBlocks>
 __device__ __forceinline__ void rescale(f32x16* o, float alpha) {
   mfma_drain_any();
 #pragma unroll
-  for (int db = 0; db < kDimBlocks; ++db)
+  for (int db = 0; db < NB; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       float e = o[db][v], t;
@@ -860,38 +863,40 @@ __device__ __forceinline__ f32x16 qk_softmax_tile(const bf16x8* q, uint32_t tile
   return s;
 }
 
-// Output product of tile i-1 (vtile, P^T in pp): 32 MFMAs, V^T from the transpose reads
-// four MFMAs ahead (bf16 and NVFP4 caches; the softmax ran in the score block).
-// nv: the NVFP4 dequantisation of the next tile, spread over the MFMAs (step m after
-// MFMA 3m + 2, its reads two steps earlier); null for the other formats.
+// Output product of tile i-1 (vtile, P^T in pp): 2 NB MFMAs (NB dim blocks from block
+// db0, even), V^T from the transpose reads four MFMAs ahead (bf16 and NVFP4 caches; the
+// softmax ran in the score block).  nv: the NVFP4 dequantisation of the next tile, spread
+// over the MFMAs (step m after MFMA 3m + 2, its reads two steps earlier); null for the
+// other formats, and only with all 16 blocks.
+template <int NB = kDimBlocks>
 __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const unsigned* pp, const int* vb,
-                                             NvDequant* nv = nullptr) {
+                                             NvDequant* nv = nullptr, int db0 = 0) {
   constexpr int kAhead = 4;
   uint32_t base[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) base[v] = vtile + vb[v];
+  for (int v = 0; v < 4; ++v) base[v] = vtile + vb[v] + kGroupBytes * (db0 >> 1);
   const bf16x8 pb0 = __builtin_bit_cast(bf16x8, u32x4{pp[0], pp[1], pp[2], pp[3]});
   const bf16x8 pb1 = __builtin_bit_cast(bf16x8, u32x4{pp[4], pp[5], pp[6], pp[7]});
-  auto tr = [&](int k) {  // V^T operand of output MFMA k (dims block k % 16, K-step k / 16)
-    const int db = k & 15, ks = k >> 4, flip = (db & 1) ^ ks;
+  auto tr = [&](int k) {  // V^T operand of output MFMA k (dims block k % NB, K-step k / NB)
+    const int db = k % NB, ks = k / NB, flip = (db & 1) ^ ks;
     const uint32_t off = kGroupBytes * (db >> 1) + 16 * 128 * ks;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at<s16x4>(base[flip] + off));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at<s16x4>(base[2 + flip] + off));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  bf16x8 va[2 * kDimBlocks];
+  bf16x8 va[2 * NB];
 #pragma unroll
   for (int k = 0; k < kAhead; ++k) va[k] = tr(k);
-  if (nv) {
+  if (NB == kDimBlocks && nv) {
     nv->read(0);
     nv->read(1);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int k = 0; k < 2 * kDimBlocks; ++k) {
-    o[k & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k], (k < kDimBlocks) ? pb0 : pb1, o[k & 15], 0, 0, 0);
-    if (k + kAhead < 2 * kDimBlocks) va[k + kAhead] = tr(k + kAhead);
-    if (nv && k % 3 == 2 && k / 3 < 9) {
+  for (int k = 0; k < 2 * NB; ++k) {
+    o[k % NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k], (k < NB) ? pb0 : pb1, o[k % NB], 0, 0, 0);
+    if (k + kAhead < 2 * NB) va[k + kAhead] = tr(k + kAhead);
+    if (NB == kDimBlocks && nv && k % 3 == 2 && k / 3 < 9) {
       nv->put(k / 3);
       if (k / 3 + 2 < 9) nv->read(k / 3 + 2);
     }
@@ -1438,18 +1443,28 @@ __device__ __forceinline__ void pv64(f32x16* o, uint32_t raw, const unsigned* ph
 
 // ------------------------------------------------------------------------------------
 // One token range of one request: Q load, pipelined tile loop, partial epilogue.
+// D: wavefronts per block of 32 rows.  With D = 1 a workgroup holds 128 rows, one block
+// per wavefront; with few rows (D = 2: at most 64, D = 4: at most 32) the D wavefronts of
+// a row block share it by output dims, each holding the accumulators of 512 / D of them
+// (the scores and the softmax are the same in all D, so they run in each).
 // ------------------------------------------------------------------------------------
 
-template <int FMT, bool PAGED>
+template <int FMT, bool PAGED, int D = 1>
 __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, int b, int n, int rg, int lt0,
                                           int lt1, int64_t slot) {
   using PP = Pipe<FMT>;
+  static_assert(D == 1 || D == 2 || D == 4, "wavefronts per row block");
+  static_assert(D == 1 || FMT == kFmtBf16, "shared row blocks on the bf16 cache only");
+  constexpr int NB = kDimBlocks / D;                      // dim blocks of this wavefront
+  constexpr int kGroupRows = kRowsPerGroup / D;           // rows of a workgroup
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform, and known so
   const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
-  const int row0 = rg * kRowsPerGroup;                    // first row of this workgroup
-  const int rows_here = min(kRowsPerGroup, p.rows - row0);
-  const int my_row = kWaveRows * wave + lr;               // this lane's row (in the group)
+  const int rblk = wave % (kWaves / D), dpart = wave / (kWaves / D);
+  const int db0 = NB * dpart;                             // first dim block of this wavefront
+  const int row0 = rg * kGroupRows;                       // first row of this workgroup
+  const int rows_here = min(kGroupRows, p.rows - row0);
+  const int my_row = kWaveRows * rblk + lr;               // this lane's row (in the group)
   const int rc = min(row0 + my_row, p.rows - 1);          // rows past the end repeat the last row
   const float c = fmaxf(p.score_scale, 1e-30f);           // sm_scale = 0 gives the plain mean
   const int nt = lt1 - lt0;
@@ -1500,9 +1515,9 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
     }
   }
 
-  f32x16 o[kDimBlocks];
+  f32x16 o[NB];
 #pragma unroll
-  for (int db = 0; db < kDimBlocks; ++db) o[db] = f32x16{};
+  for (int db = 0; db < NB; ++db) o[db] = f32x16{};
   Softmax S{-INFINITY, 0.f, 0.f};
   unsigned pp[8];
 
@@ -1536,12 +1551,15 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
   float x[16];
 
   // one tile; FIRST: there is no previous tile to multiply
+  // loads run kAhead tiles ahead; a bf16 range of at most kTiles tiles loads them all at
+  // once (no buffer is reused, so their latencies overlap)
+  const int ahead = (FMT == kFmtBf16 && nt <= PP::kTiles) ? nt : PP::kAhead;
   auto body = [&](int i, auto FIRST) {
     constexpr bool first = decltype(FIRST)::value;
-    const bool more = i + PP::kAhead < nt;
+    const bool more = i + ahead < nt;
     if (more) {
-      issue(i + PP::kAhead, e_next);
-      e_next = entry(i + PP::kAhead + 1);
+      issue(i + ahead, e_next);
+      e_next = entry(i + ahead + 1);
     }
     f32x16 s;
     if (first) {
@@ -1550,7 +1568,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
       // scores of tile i, softmax of tile i-1 (x) -> P^T in pp and its factor
       float alpha;
       s = qk_softmax_tile(q, tile_buf(i), ab, x, S, c, pp, alpha);
-      if (__any(alpha != 1.f)) rescale(o, alpha);
+      if (__any(alpha != 1.f)) rescale<NB>(o, alpha);
     }
 #pragma unroll
     for (int v = 0; v < 16; ++v) x[v] = s[v];
@@ -1572,18 +1590,19 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
       NvDequant nv(raw_buf(i + 1), tile_buf(i + 1), tid);
       output_phase(o, tile_buf(i - 1), pp, vb, &nv);
     } else {
-      output_phase(o, tile_buf(i - 1), pp, vb);
+      output_phase<NB>(o, tile_buf(i - 1), pp, vb, nullptr, db0);
     }
-    // the loads the next tile depends on: bf16 tile i+1 (issued one tile ago), raw NVFP4
-    // tile i+2 (one tile ago)
-    wait_vmcnt(more ? nloads : 0);
+    // the loads the next tile depends on: bf16 tile i+1, raw NVFP4 tile i+2; the tiles
+    // issued after it may stay in flight
+    const int need = FMT == kFmtBf16 ? i + 1 : i + 2;
+    wait_vmcnt(max(min(nt - 1, i + ahead) - need, 0) * nloads);
     __syncthreads();
   };
 
   if (nt > 0) {
-    const int pro = min(nt, PP::kAhead);
+    const int pro = min(nt, ahead);
     for (int k = 0; k < pro; ++k) issue(k, entry(k));
-    e_next = entry(PP::kAhead);
+    e_next = entry(ahead);
     wait_vmcnt((pro - 1) * nloads);  // tile 0
     __syncthreads();
     if (FMT != kFmtBf16) {
@@ -1594,8 +1613,8 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
     body(0, std::true_type{});
     for (int i = 1; i < nt; ++i) body(i, std::false_type{});
     const float alpha = softmax_tile(S, x, c, pp);  // the last tile's softmax
-    if (__any(alpha != 1.f)) rescale(o, alpha);
-    pv_tile(o, tile_buf(nt - 1), pp, vb);
+    if (__any(alpha != 1.f)) rescale<NB>(o, alpha);
+    pv_tile<NB>(o, tile_buf(nt - 1), pp, vb, db0);
   }
 
   // ---- epilogue: normalised partial O and its lse ----
@@ -1604,14 +1623,14 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
   const bool ok = l_tot > 0.f;
   if (my_row < rows_here) {
     const int row = row0 + my_row;
-    if (lh == 0)
+    if (lh == 0 && dpart == 0)
       p.lse_part[slot * p.l_slot + (int64_t)row * p.l_row] = ok ? (S.m_used + __log2f(l_tot)) * kLn2 : -INFINITY;
     const float f = ok ? p.v_scale / l_rnd : 0.f;  // normalisation, applied on the way out
-    float* orow = p.o_part + slot * p.o_slot + (int64_t)row * p.o_row + 4 * lh;
+    float* orow = p.o_part + slot * p.o_slot + (int64_t)row * p.o_row + 4 * lh + 32 * db0;
     // four dim blocks at a time: 64 values scaled into vector registers, then 16 stores
     // issued back to back
 #pragma unroll
-    for (int g = 0; g < kDimBlocks; g += 4) {
+    for (int g = 0; g < NB; g += 4) {
       f32x4 t[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -1804,7 +1823,9 @@ __device__ __forceinline__ void run_range_fp8(const DecodeParams& p, uint32_t sm
 // decode kernels
 // ------------------------------------------------------------------------------------
 
-// Contiguous: grid (row_groups, num_splits, B); split j covers [j*L, min((j+1)*L, S)).
+// Contiguous: grid (row groups of 128 / D rows, num_splits, B); split j covers
+// [j*L, min((j+1)*L, S)).
+template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_contig_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<kFmtBf16>()];
@@ -1812,8 +1833,8 @@ void decode_contig_kernel(const DecodeParams p) {
   const int t0 = j * p.kv_len_per_split;
   const int t1 = min(t0 + p.kv_len_per_split, p.S);
   // slot b*H*NS + j with row = head addresses o_part [B, H, NS, 512]
-  run_range<kFmtBf16, false>(p, lds_addr((lds_ptr)smem), b, p.S, rg, t0 / kTileTokens,
-                             (t1 + kTileTokens - 1) / kTileTokens, (int64_t)b * p.rows * p.num_splits + j);
+  run_range<kFmtBf16, false, D>(p, lds_addr((lds_ptr)smem), b, p.S, rg, t0 / kTileTokens,
+                                (t1 + kTileTokens - 1) / kTileTokens, (int64_t)b * p.rows * p.num_splits + j);
 }
 
 // Paged: the batch's tiles (request b has ceil(n_b / 32)) are cut into num_splits
@@ -2061,9 +2082,14 @@ __global__ __launch_bounds__(256) void combine_paged_kernel(const CombineParams 
 // launchers
 // ------------------------------------------------------------------------------------
 
+// Few heads: the wavefronts of a row block share its output dims (D = 4 up to 32 rows,
+// 2 up to 64) instead of repeating its last row.
 hipError_t launch_decode_contig(const DecodeParams& p, hipStream_t stream) {
-  dim3 grid(p.row_groups, p.num_splits, p.B);
-  hipLaunchKernelGGL(decode_contig_kernel, grid, dim3(kThreads), 0, stream, p);
+  const int D = p.rows <= kWaveRows ? 4 : p.rows <= 2 * kWaveRows ? 2 : 1;
+  dim3 grid((p.rows + kRowsPerGroup / D - 1) / (kRowsPerGroup / D), p.num_splits, p.B);
+  if (D == 4) hipLaunchKernelGGL(decode_contig_kernel<4>, grid, dim3(kThreads), 0, stream, p);
+  else if (D == 2) hipLaunchKernelGGL(decode_contig_kernel<2>, grid, dim3(kThreads), 0, stream, p);
+  else hipLaunchKernelGGL(decode_contig_kernel<1>, grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

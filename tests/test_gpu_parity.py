@@ -34,6 +34,9 @@ def _contig_run(c, L):
     (1, 48, 200, 128),     # rows not a multiple of 32: one wave half idle, two waves idle
     (2, 128, 1000, 256),   # full head group, 4 splits, ragged
     (3, 64, 129, 128),     # one token in the last split
+    (2, 16, 4096, 1024),   # few heads over long splits: 4 wavefronts share each row block
+    (2, 32, 65, 128),      # 3 tiles in one split, all loaded at once, ragged
+    (1, 96, 500, 128),     # three row blocks, one wavefront idle
 ])
 def test_contig_splitkv_matches_oracle(B, H, S, L):
     say(f"contig B={B} H={H} S={S} L={L}")
