@@ -200,6 +200,8 @@ def roofline(flops, nbytes, t_ms, contraction, ceilings, traffic):
              "frac": round(a / peak, 4), "traffic": traffic, "contraction": contraction}
         m = ceilings.get(f"mfma_{contraction}_TFLOPs") if ceilings else None
     r["roof_us"] = round(max(t_hbm, t_mfma) * 1e6, 2)
+    r["algorithmic_bytes"] = int(nbytes)
+    r["algorithmic_flops"] = float(flops)
     if m:
         r["measured_peak"] = m
         r["frac_of_measured"] = round(a / m, 4)
