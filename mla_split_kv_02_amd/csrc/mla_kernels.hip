@@ -935,7 +935,7 @@ __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const un
 template <bool HW>
 __device__ __forceinline__ unsigned e4m3_pair(unsigned w, float a, float b) {
   if (HW) asm("v_cvt_scalef32_pk_fp8_f32 %0, %1, %2, 1.0 op_sel:[0,0,0,1]" : "+v"(w) : "v"(a), "v"(b));
-  else asm("v_cvt_scalef32_pk_fp8_f32 %0, %1, %2, 1.0" : "+v"(w) : "v"(a), "v"(b));
+  else asm("v_cvt_scalef32_pk_fp8_f32 %0, %1, %2, 1.0" : "=v"(w) : "v"(a), "v"(b));
   return w;
 }
 template <bool HW>
