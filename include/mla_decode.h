@@ -148,8 +148,8 @@ int mla_splitkv_combine(const float* o_part, const float* lse_part, int rows, in
 
 /* First launch of the paged decode alone: writes the split partials of every request
  * into `workspace` (same arguments and checks as mla_paged_decode, without the
- * outputs).  Range w of the num_splits ranges of the batch's 32-token tiles
- * writes, for each request b it touches, the normalised partial O and its lse into
+ * outputs).  Range w of the num_splits ranges of the batch's tiles (64 tokens for the FP8
+ * formats, 32 for the others) writes, for each request b it touches, the normalised partial O and its lse into
  * slot w + b of the workspace; the workspace also records, per request, the first and
  * last range that touch it.  Useful to a caller that merges partials itself, or times
  * the two launches apart.  Workspace layout (each section starting on a 256-byte
@@ -238,6 +238,45 @@ int mla_paged_decode_noalloc(const uint16_t* q, const uint16_t* qpe, const void*
                              const int32_t* block_tables, int max_blocks_per_seq,
                              const int32_t* seq_lens, int B, int q_len, int H, float sm_scale,
                              int num_splits, uint16_t* o, float* lse, void* stream);
+
+/* Paged split planner in the pages' own split form (TileGym page,
+ * _mla_decoding_split_kv.forward, with the batch's longest sequence as S_kv; SURVEY's
+ * host-planner signature): from a host copy of seq_lens,
+ *   max_len = max(1, max_b seq_lens_host[b]);  estimate = max(1, num_cus / B);
+ *   kv_len_per_split = max(next_power_of_2(max_len / estimate), 128);
+ *   max_splits = ceil(max_len / kv_len_per_split).
+ * kv_len_per_split is a power of two >= 128, so a multiple of either page size.  q_len and
+ * page_size are checked (1..8; 32 or 64) and do not enter the formula.  Host-only integer
+ * work.  Returns MLA_ERR_INVALID_ARG for max_splits > 65535. */
+int mla_plan_paged_splits(int num_cus, int B, int q_len, const int32_t* seq_lens_host, int page_size,
+                          int* kv_len_per_split, int* max_splits);
+
+/* Bytes of workspace mla_paged_decode_splits needs: B * q_len * H * max_splits partials of
+ * 512 + 1 fp32 values (TokenSpeed page, module note on the decode workspace: (D + 1)
+ * accumulator values per split and head), laid out as o_part [B, q_len, H, max_splits, 512]
+ * fp32 followed, at the next 256-byte boundary, by lse_part [B, q_len, H, max_splits] fp32.
+ * Returns 0 for invalid arguments. */
+size_t mla_paged_splits_workspace_bytes(int B, int q_len, int H, int max_splits);
+
+/* Paged decode with fixed-length splits, the pages' own split form (TileGym page,
+ * forward: kv_len_per_split; TokenSpeed page, forward_decode), in two launches on
+ * `stream`: split j of request b covers tokens [j*L, min((j+1)*L, seq_lens[b])) of it,
+ * L = kv_len_per_split, and writes its normalised partial O_j and lse_j into the workspace
+ * (layout of mla_paged_splits_workspace_bytes; a split past the request's end writes only
+ * lse_j = -inf); the split-K reduce then merges each row's max_splits partials into o and
+ * lse.  Every other argument, precondition and result is that of mla_paged_decode (no
+ * sliding window, no sinks).  Checked on the host besides mla_paged_decode's checks:
+ * kv_len_per_split a power of two >= 128 (the page's assertions); 1 <= max_splits <=
+ * 65535; max_splits * kv_len_per_split >= max_blocks_per_seq * page_size (the splits cover
+ * every admissible length); workspace_bytes >= mla_paged_splits_workspace_bytes(B, q_len,
+ * H, max_splits).  mla_plan_paged / mla_paged_decode cut the batch into cost-balanced
+ * ranges instead, which keeps every workgroup busy when lengths differ. */
+int mla_paged_decode_splits(const uint16_t* q, const uint16_t* qpe, const void* kv_cache, int fmt,
+                            float kv_scale, int num_pages, int page_size, int64_t page_stride_bytes,
+                            const int32_t* block_tables, int max_blocks_per_seq,
+                            const int32_t* seq_lens, int B, int q_len, int H, float sm_scale,
+                            int kv_len_per_split, int max_splits, void* workspace, size_t workspace_bytes,
+                            uint16_t* o, float* lse, void* stream);
 
 /* KV-cache append: store T new tokens into the paged pool before decoding them
  * (TokenSpeed page, forward_decode: each new token's latent and rope key are written into

@@ -28,10 +28,13 @@ from ._lib import (  # noqa: F401
     lib,
     paged_decode,
     paged_decode_noalloc,
+    paged_decode_splits,
+    paged_splits_workspace_bytes,
     paged_workspace,
     paged_workspace_bytes,
     plan_contig,
     plan_paged,
+    plan_paged_splits,
     splitkv_combine,
     status_string,
 )

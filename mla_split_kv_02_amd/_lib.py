@@ -45,6 +45,9 @@ EXPORTED_SYMBOLS = (
     "mla_paged_decode",
     "mla_paged_decode_ext",
     "mla_paged_decode_noalloc",
+    "mla_plan_paged_splits",
+    "mla_paged_splits_workspace_bytes",
+    "mla_paged_decode_splits",
     "mla_kv_append",
 )
 
@@ -96,6 +99,13 @@ def lib() -> ctypes.CDLL:
     L.mla_paged_decode_noalloc.restype = c_int
     L.mla_paged_decode_noalloc.argtypes = [vp, vp, vp, c_int, c_float, c_int, c_int, c_i64, vp, c_int, vp, c_int,
                                            c_int, c_int, c_float, c_int, vp, vp, vp]
+    L.mla_plan_paged_splits.restype = c_int
+    L.mla_plan_paged_splits.argtypes = [c_int, c_int, c_int, vp, c_int, pint, pint]
+    L.mla_paged_splits_workspace_bytes.restype = c_size
+    L.mla_paged_splits_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int]
+    L.mla_paged_decode_splits.restype = c_int
+    L.mla_paged_decode_splits.argtypes = [vp, vp, vp, c_int, c_float, c_int, c_int, c_i64, vp, c_int, vp, c_int,
+                                          c_int, c_int, c_float, c_int, c_int, vp, c_size, vp, vp, vp]
     L.mla_kv_append.restype = c_int
     L.mla_kv_append.argtypes = [vp, vp, vp, c_int, vp, c_int, c_float, c_int, c_int, c_i64, vp]
     _lib = L
@@ -160,6 +170,19 @@ def paged_workspace_bytes(B: int, q_len: int, H: int, num_splits: int) -> int:
     return int(lib().mla_paged_workspace_bytes(B, q_len, H, num_splits))
 
 
+def plan_paged_splits(num_cus: int, B: int, q_len: int, seq_lens_host, page_size: int):
+    """Fixed-length paged splits from a host copy of seq_lens: (kv_len_per_split, max_splits)."""
+    sl = (ctypes.c_int32 * B)(*[int(x) for x in seq_lens_host])
+    L, ns = ctypes.c_int(), ctypes.c_int()
+    _check(lib().mla_plan_paged_splits(num_cus, B, q_len, ctypes.cast(sl, ctypes.c_void_p), page_size,
+                                       ctypes.byref(L), ctypes.byref(ns)), "mla_plan_paged_splits")
+    return L.value, ns.value
+
+
+def paged_splits_workspace_bytes(B: int, q_len: int, H: int, max_splits: int) -> int:
+    return int(lib().mla_paged_splits_workspace_bytes(B, q_len, H, max_splits))
+
+
 # ----------------------------------------------------------------------------------
 # device calls
 # ----------------------------------------------------------------------------------
@@ -222,6 +245,39 @@ def paged_workspace(B, q_len, H, num_splits, device):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def _paged_inputs(q, qpe, kv_cache, fmt, block_tables, seq_lens, page_size, page_stride, sm_scale):
+    """Checks the paged decode's tensors; returns (B, q_len, H, device, page_stride, sm_scale)."""
+    B, q_len, H, _ = q.shape
+    dev = q.device
+    _need(q, "q", torch.bfloat16, (B, q_len, H, LATENT))
+    _need(qpe, "qpe", torch.bfloat16, (B, q_len, H, ROPE), dev)
+    _need(kv_cache, "kv_cache", torch.uint8, None, dev)
+    _need(block_tables, "block_tables", torch.int32, None, dev)
+    _need(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks]")
+    rb = {MLA_KV_BF16: 2 * ROW, MLA_KV_FP8_E4M3: ROW, MLA_KV_NVFP4: ROW // 2 + ROW // 16,
+          MLA_KV_FP8_E4M3_QFP8: ROW}.get(fmt)
+    if rb is None:
+        raise MlaError(MLA_ERR_UNSUPPORTED, "cache format")
+    if page_stride is None:
+        page_stride = page_size * rb
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(LATENT + ROPE)
+    return B, q_len, H, dev, page_stride, sm_scale
+
+
+def _outputs(o, lse, want_lse, B, q_len, H, dev):
+    if o is None:
+        o = torch.empty((B, q_len, H, LATENT), dtype=torch.bfloat16, device=dev)
+    _need(o, "o", torch.bfloat16, (B, q_len, H, LATENT), dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, q_len, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, q_len, H), dev)
+    return o, lse
+
+
 class PagedCall:
     """Checked, marshalled arguments of one paged decode; ``partials()`` and
     ``combine()`` enqueue its two launches, ``run()`` both through mla_paged_decode."""
@@ -229,35 +285,14 @@ class PagedCall:
     def __init__(self, q, qpe, kv_cache, fmt, block_tables, seq_lens, page_size, page_stride=None, kv_scale=1.0,
                  sm_scale=None, num_splits=None, workspace=None, o=None, lse=None, want_lse=True, num_cus=None,
                  window=0, sinks=None):
-        B, q_len, H, _ = q.shape
-        dev = q.device
-        _need(q, "q", torch.bfloat16, (B, q_len, H, LATENT))
-        _need(qpe, "qpe", torch.bfloat16, (B, q_len, H, ROPE), dev)
-        _need(kv_cache, "kv_cache", torch.uint8, None, dev)
-        _need(block_tables, "block_tables", torch.int32, None, dev)
-        _need(seq_lens, "seq_lens", torch.int32, (B,), dev)
-        if block_tables.dim() != 2 or block_tables.shape[0] != B:
-            raise ValueError("block_tables must be [B, max_blocks]")
-        rb = {MLA_KV_BF16: 2 * ROW, MLA_KV_FP8_E4M3: ROW, MLA_KV_NVFP4: ROW // 2 + ROW // 16,
-              MLA_KV_FP8_E4M3_QFP8: ROW}.get(fmt)
-        if rb is None:
-            raise MlaError(MLA_ERR_UNSUPPORTED, "cache format")
-        if page_stride is None:
-            page_stride = page_size * rb
-        if sm_scale is None:
-            sm_scale = 1.0 / math.sqrt(LATENT + ROPE)
+        B, q_len, H, dev, page_stride, sm_scale = _paged_inputs(q, qpe, kv_cache, fmt, block_tables, seq_lens,
+                                                                 page_size, page_stride, sm_scale)
         if num_splits is None:
             num_splits = plan_paged(num_cus or device_num_cus(dev.index or 0), B, q_len, H)
         if workspace is None:
             workspace = paged_workspace(B, q_len, H, num_splits, dev)
         _need(workspace, "workspace", torch.uint8, None, dev)
-        if o is None:
-            o = torch.empty((B, q_len, H, LATENT), dtype=torch.bfloat16, device=dev)
-        _need(o, "o", torch.bfloat16, (B, q_len, H, LATENT), dev)
-        if lse is None and want_lse:
-            lse = torch.empty((B, q_len, H), dtype=torch.float32, device=dev)
-        if lse is not None:
-            _need(lse, "lse", torch.float32, (B, q_len, H), dev)
+        o, lse = _outputs(o, lse, want_lse, B, q_len, H, dev)
         self.dev = dev
         self.o, self.lse, self.workspace = o, lse, workspace
         self.num_splits = num_splits
@@ -313,38 +348,52 @@ def paged_decode_noalloc(q, qpe, kv_cache, fmt, block_tables, seq_lens, page_siz
     """paged_decode through mla_paged_decode_noalloc: the workspace is the library's own
     per-GPU scratch array (no workspace tensor).  Outputs are allocated here when not
     given; the C call itself allocates nothing."""
-    B, q_len, H, _ = q.shape
-    dev = q.device
-    _need(q, "q", torch.bfloat16, (B, q_len, H, LATENT))
-    _need(qpe, "qpe", torch.bfloat16, (B, q_len, H, ROPE), dev)
-    _need(kv_cache, "kv_cache", torch.uint8, None, dev)
-    _need(block_tables, "block_tables", torch.int32, None, dev)
-    _need(seq_lens, "seq_lens", torch.int32, (B,), dev)
-    if block_tables.dim() != 2 or block_tables.shape[0] != B:
-        raise ValueError("block_tables must be [B, max_blocks]")
-    rb = {MLA_KV_BF16: 2 * ROW, MLA_KV_FP8_E4M3: ROW, MLA_KV_NVFP4: ROW // 2 + ROW // 16,
-          MLA_KV_FP8_E4M3_QFP8: ROW}.get(fmt)
-    if rb is None:
-        raise MlaError(MLA_ERR_UNSUPPORTED, "cache format")
-    if page_stride is None:
-        page_stride = page_size * rb
-    if sm_scale is None:
-        sm_scale = 1.0 / math.sqrt(LATENT + ROPE)
+    B, q_len, H, dev, page_stride, sm_scale = _paged_inputs(q, qpe, kv_cache, fmt, block_tables, seq_lens,
+                                                             page_size, page_stride, sm_scale)
     if num_splits is None:
         num_splits = plan_paged(num_cus or device_num_cus(dev.index or 0), B, q_len, H)
-    if o is None:
-        o = torch.empty((B, q_len, H, LATENT), dtype=torch.bfloat16, device=dev)
-    _need(o, "o", torch.bfloat16, (B, q_len, H, LATENT), dev)
-    if lse is None and want_lse:
-        lse = torch.empty((B, q_len, H), dtype=torch.float32, device=dev)
-    if lse is not None:
-        _need(lse, "lse", torch.float32, (B, q_len, H), dev)
+    o, lse = _outputs(o, lse, want_lse, B, q_len, H, dev)
     _check(lib().mla_paged_decode_noalloc(_ptr(q), _ptr(qpe), _ptr(kv_cache), int(fmt), float(kv_scale),
                                           int(kv_cache.numel() // page_stride), int(page_size), int(page_stride),
                                           _ptr(block_tables), int(block_tables.shape[1]), _ptr(seq_lens), B, q_len,
                                           H, float(sm_scale), int(num_splits), _ptr(o), _ptr(lse), _stream(dev)),
            "mla_paged_decode_noalloc")
     return o, lse
+
+
+def paged_decode_splits(q, qpe, kv_cache, fmt, block_tables, seq_lens, page_size, page_stride=None, kv_scale=1.0,
+                        sm_scale=None, kv_len_per_split=None, max_splits=None, seq_lens_host=None, workspace=None,
+                        o=None, lse=None, want_lse=True, num_cus=None):
+    """Paged decode with fixed-length splits (mla_paged_decode_splits).  Without
+    kv_len_per_split / max_splits they come from mla_plan_paged_splits on seq_lens_host
+    (a host copy of seq_lens; read from the device here when not given), and max_splits
+    is raised to cover max_blocks * page_size.  The workspace holds the partials:
+    o_part [B,q_len,H,max_splits,512] f32, then lse_part [B,q_len,H,max_splits] f32 at
+    the next 256-byte boundary.  Returns (o, lse, kv_len_per_split, max_splits)."""
+    B, q_len, H, dev, page_stride, sm_scale = _paged_inputs(q, qpe, kv_cache, fmt, block_tables, seq_lens,
+                                                             page_size, page_stride, sm_scale)
+    max_len = int(block_tables.shape[1]) * int(page_size)
+    if kv_len_per_split is None:
+        if seq_lens_host is None:
+            seq_lens_host = seq_lens.cpu().tolist()
+        kv_len_per_split, _ = plan_paged_splits(num_cus or device_num_cus(dev.index or 0), B, q_len,
+                                                seq_lens_host, page_size)
+    if max_splits is None:
+        max_splits = -(-max_len // kv_len_per_split)
+    if workspace is None:
+        n = paged_splits_workspace_bytes(B, q_len, H, max_splits)
+        if n == 0:
+            raise MlaError(MLA_ERR_INVALID_ARG, "mla_paged_splits_workspace_bytes")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
+    o, lse = _outputs(o, lse, want_lse, B, q_len, H, dev)
+    _check(lib().mla_paged_decode_splits(_ptr(q), _ptr(qpe), _ptr(kv_cache), int(fmt), float(kv_scale),
+                                         int(kv_cache.numel() // page_stride), int(page_size), int(page_stride),
+                                         _ptr(block_tables), int(block_tables.shape[1]), _ptr(seq_lens), B, q_len, H,
+                                         float(sm_scale), int(kv_len_per_split), int(max_splits), _ptr(workspace),
+                                         workspace.numel(), _ptr(o), _ptr(lse), _stream(dev)),
+           "mla_paged_decode_splits")
+    return o, lse, kv_len_per_split, max_splits
 
 
 def kv_append(latent, rope, slots, kv_cache, fmt, page_size, page_stride=None, kv_scale=1.0):

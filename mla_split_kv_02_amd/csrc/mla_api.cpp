@@ -41,6 +41,21 @@ struct PagedLayout {
   int64_t slots;
 };
 
+// fixed-length paged splits: o_part [B][rows][NS][512] f32 | lse_part [B][rows][NS] f32,
+// the second section 256-byte aligned
+struct SplitsLayout {
+  size_t lse_off, total;
+};
+bool splits_layout(int B, int q_len, int H, int max_splits, SplitsLayout* L) {
+  if (B < 1 || B > MLA_MAX_BATCH || q_len < 1 || q_len > MLA_MAX_Q_LEN || H < 16 || H > MLA_MAX_HEADS ||
+      H % 16 != 0 || max_splits < 1 || max_splits > 65535)
+    return false;
+  const int64_t n = (int64_t)B * q_len * H * max_splits;
+  L->lse_off = round_up((size_t)(n * kLatent * 4), 256);
+  L->total = L->lse_off + round_up((size_t)(n * 4), 256);
+  return true;
+}
+
 // workspace: o_part [slots][rows][512] f32 | lse_part [slots][rows] f32 | first [B] i32 |
 // last [B] i32 | info [64] i32, each section 256-byte aligned
 bool paged_layout(int B, int q_len, int H, int num_splits, PagedLayout* L) {
@@ -186,11 +201,10 @@ int check_paged_shape(int B, int q_len, int H, int num_splits, const void* works
   return MLA_OK;
 }
 
-int paged_partials(const uint16_t* q, const uint16_t* qpe, const void* kv_cache, int fmt, float kv_scale,
-                   int num_pages, int page_size, int64_t page_stride_bytes, const int32_t* block_tables,
-                   int max_blocks_per_seq, const int32_t* seq_lens, int B, int q_len, int H, float sm_scale,
-                   int window, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
-  if (window < 0) return MLA_ERR_INVALID_ARG;
+// Checks of the cache, table and scale arguments shared by the paged decodes.
+int check_paged_cache(const uint16_t* q, const uint16_t* qpe, const void* kv_cache, int fmt, float kv_scale,
+                      int num_pages, int page_size, int64_t page_stride_bytes, const int32_t* block_tables,
+                      int max_blocks_per_seq, const int32_t* seq_lens, int B, float sm_scale) {
   if (!q || !qpe || !kv_cache || !block_tables || !seq_lens) return MLA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(qpe, 16) || !aligned(kv_cache, 16) || !aligned(block_tables, 4) ||
       !aligned(seq_lens, 4))
@@ -204,11 +218,14 @@ int paged_partials(const uint16_t* q, const uint16_t* qpe, const void* kv_cache,
   if (!isfinite(sm_scale) || sm_scale < 0.f) return MLA_ERR_INVALID_ARG;
   const bool fp8 = (fmt == MLA_KV_FP8_E4M3 || fmt == MLA_KV_FP8_E4M3_QFP8);
   if (fp8 && !(isfinite(kv_scale) && kv_scale > 0.f)) return MLA_ERR_INVALID_ARG;
-  PagedLayout L;
-  const int st = check_paged_shape(B, q_len, H, num_splits, workspace, workspace_bytes, &L);
-  if (st != MLA_OK) return st;
+  return MLA_OK;
+}
 
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
+// The paged decode's parameters that do not depend on the split form.
+DecodeParams paged_params(const uint16_t* q, const uint16_t* qpe, const void* kv_cache, int fmt, float kv_scale,
+                          int num_pages, int page_size, int64_t page_stride_bytes, const int32_t* block_tables,
+                          int max_blocks_per_seq, const int32_t* seq_lens, int B, int q_len, int H, float sm_scale) {
+  const bool fp8 = (fmt == MLA_KV_FP8_E4M3 || fmt == MLA_KV_FP8_E4M3_QFP8);
   const float vs = fp8 ? kv_scale : 1.f;
   DecodeParams p{};
   p.q = q;
@@ -226,10 +243,28 @@ int paged_partials(const uint16_t* q, const uint16_t* qpe, const void* kv_cache,
   p.H = H;
   p.rows = q_len * H;
   p.row_groups = (p.rows + kRowsPerGroup - 1) / kRowsPerGroup;
-  p.num_splits = num_splits;
-  p.window = window;
   p.score_scale = sm_scale * vs * kLog2e;
   p.v_scale = vs;
+  return p;
+}
+
+int paged_partials(const uint16_t* q, const uint16_t* qpe, const void* kv_cache, int fmt, float kv_scale,
+                   int num_pages, int page_size, int64_t page_stride_bytes, const int32_t* block_tables,
+                   int max_blocks_per_seq, const int32_t* seq_lens, int B, int q_len, int H, float sm_scale,
+                   int window, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (window < 0) return MLA_ERR_INVALID_ARG;
+  int st = check_paged_cache(q, qpe, kv_cache, fmt, kv_scale, num_pages, page_size, page_stride_bytes, block_tables,
+                             max_blocks_per_seq, seq_lens, B, sm_scale);
+  if (st != MLA_OK) return st;
+  PagedLayout L;
+  st = check_paged_shape(B, q_len, H, num_splits, workspace, workspace_bytes, &L);
+  if (st != MLA_OK) return st;
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  DecodeParams p = paged_params(q, qpe, kv_cache, fmt, kv_scale, num_pages, page_size, page_stride_bytes,
+                                block_tables, max_blocks_per_seq, seq_lens, B, q_len, H, sm_scale);
+  p.num_splits = num_splits;
+  p.window = window;
   p.o_part = reinterpret_cast<float*>(ws + L.o_off);
   p.lse_part = reinterpret_cast<float*>(ws + L.lse_off);
   p.o_slot = (int64_t)p.rows * kLatent;
@@ -303,6 +338,78 @@ int mla_paged_decode(const uint16_t* q, const uint16_t* qpe, const void* kv_cach
   return mla_paged_decode_ext(q, qpe, kv_cache, fmt, kv_scale, num_pages, page_size, page_stride_bytes, block_tables,
                               max_blocks_per_seq, seq_lens, B, q_len, H, sm_scale, 0, nullptr, num_splits, workspace,
                               workspace_bytes, o, lse, stream);
+}
+
+int mla_plan_paged_splits(int num_cus, int B, int q_len, const int32_t* seq_lens_host, int page_size,
+                          int* kv_len_per_split, int* max_splits) {
+  if (!seq_lens_host || !kv_len_per_split || !max_splits || num_cus < 1 || B < 1 || B > MLA_MAX_BATCH)
+    return MLA_ERR_INVALID_ARG;
+  if (q_len < 1 || q_len > MLA_MAX_Q_LEN) return MLA_ERR_UNSUPPORTED;
+  if (page_size != 32 && page_size != 64) return MLA_ERR_UNSUPPORTED;
+  int64_t max_len = 1;
+  for (int b = 0; b < B; ++b)
+    if (seq_lens_host[b] > max_len) max_len = seq_lens_host[b];
+  // TileGym page, _mla_decoding_split_kv.forward, with the batch's longest sequence as S_kv
+  const int est = num_cus / B > 1 ? num_cus / B : 1;
+  int64_t L = next_pow2(max_len / est);
+  if (L < 128) L = 128;
+  const int64_t ns = (max_len + L - 1) / L;
+  if (ns > 65535) return MLA_ERR_INVALID_ARG;
+  *kv_len_per_split = (int)L;
+  *max_splits = (int)ns;
+  return MLA_OK;
+}
+
+size_t mla_paged_splits_workspace_bytes(int B, int q_len, int H, int max_splits) {
+  SplitsLayout L;
+  if (!splits_layout(B, q_len, H, max_splits, &L)) return 0;
+  return L.total;
+}
+
+int mla_paged_decode_splits(const uint16_t* q, const uint16_t* qpe, const void* kv_cache, int fmt, float kv_scale,
+                            int num_pages, int page_size, int64_t page_stride_bytes, const int32_t* block_tables,
+                            int max_blocks_per_seq, const int32_t* seq_lens, int B, int q_len, int H, float sm_scale,
+                            int kv_len_per_split, int max_splits, void* workspace, size_t workspace_bytes,
+                            uint16_t* o, float* lse, void* stream) {
+  int st = check_paged_cache(q, qpe, kv_cache, fmt, kv_scale, num_pages, page_size, page_stride_bytes, block_tables,
+                             max_blocks_per_seq, seq_lens, B, sm_scale);
+  if (st != MLA_OK) return st;
+  if (!o || !aligned(o, 16) || (lse && !aligned(lse, 4))) return MLA_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 256)) return MLA_ERR_INVALID_ARG;
+  if (q_len < 1 || q_len > MLA_MAX_Q_LEN) return MLA_ERR_UNSUPPORTED;
+  if (H < 16 || H > MLA_MAX_HEADS || H % 16 != 0) return MLA_ERR_UNSUPPORTED;
+  if (B < 1 || B > MLA_MAX_BATCH) return MLA_ERR_INVALID_ARG;
+  // the page's assertions on the split length; the splits must cover every admissible length
+  if (kv_len_per_split < 128 || (kv_len_per_split & (kv_len_per_split - 1)) != 0) return MLA_ERR_INVALID_ARG;
+  if (max_splits < 1 || max_splits > 65535) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)max_splits * kv_len_per_split < (int64_t)max_blocks_per_seq * page_size) return MLA_ERR_INVALID_ARG;
+  SplitsLayout W;
+  if (!splits_layout(B, q_len, H, max_splits, &W)) return MLA_ERR_INVALID_ARG;
+  if (workspace_bytes < W.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  DecodeParams p = paged_params(q, qpe, kv_cache, fmt, kv_scale, num_pages, page_size, page_stride_bytes,
+                                block_tables, max_blocks_per_seq, seq_lens, B, q_len, H, sm_scale);
+  p.kv_len_per_split = kv_len_per_split;
+  p.num_splits = max_splits;
+  p.window = 0;
+  // element (b, row, j) at slot b * rows * NS + j, row stride NS (o_part [B, rows, NS, 512])
+  p.o_part = reinterpret_cast<float*>(ws);
+  p.lse_part = reinterpret_cast<float*>(ws + W.lse_off);
+  p.o_slot = kLatent;
+  p.o_row = (int64_t)max_splits * kLatent;
+  p.l_slot = 1;
+  p.l_row = max_splits;
+  if (launch_decode_paged_splits(fmt, p, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
+  CombineParams c{};
+  c.o_part = p.o_part;
+  c.lse_part = p.lse_part;
+  c.o = o;
+  c.lse = lse;
+  c.rows = B * q_len * H;
+  c.num_splits = max_splits;
+  if (launch_combine_generic(c, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
 }
 
 int mla_paged_decode_ext(const uint16_t* q, const uint16_t* qpe, const void* kv_cache, int fmt, float kv_scale,

@@ -44,7 +44,7 @@ struct DecodeParams {
   int B, q_len, H;
   int rows;           // q_len * H
   int row_groups;     // ceil(rows / kRowsPerGroup)
-  int num_splits;     // contiguous: splits per request; paged: token-balanced ranges
+  int num_splits;     // contiguous and fixed-split paged: splits per request; paged: token-balanced ranges
   int window;         // paged: query at position p sees tokens p - window + 1 .. p (0: all)
   float score_scale;  // sm_scale * kv_scale * log2(e)
   float v_scale;      // kv_scale (FP8) or 1
@@ -87,6 +87,7 @@ struct AppendParams {
 
 hipError_t launch_decode_contig(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_paged(int fmt, const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_paged_splits(int fmt, const DecodeParams& p, hipStream_t stream);
 hipError_t launch_combine_generic(const CombineParams& p, hipStream_t stream);
 hipError_t launch_combine_paged(const CombineParams& p, hipStream_t stream);
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);

@@ -1976,6 +1976,36 @@ void decode_paged_kernel(const DecodeParams p) {
   }
 }
 
+// Paged, fixed-length splits (the pages' own split form): grid (row groups, max_splits,
+// B); split j of request b covers tokens [j L, min((j + 1) L, n_b)), L = kv_len_per_split
+// (a power of two >= 128, so a whole number of tiles of either size), and writes slot
+// b * rows * NS + j of o_part [B, rows, NS, 512] / lse_part [B, rows, NS].  A split past
+// the request's end writes lse = -inf for its rows and leaves its O_j, which the combine
+// then weighs 0, unwritten.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_paged_splits_kernel(const DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<FMT>()];
+  constexpr bool kFp8Fmt = FMT == kFmtFp8 || FMT == kFmtFp8Q;
+  constexpr int TT = kFp8Fmt ? kT8 : kTileTokens;
+  const int rg = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int n = min(max(p.seq_lens[b], 0), p.max_blocks * p.page_size);
+  const int t0 = j * p.kv_len_per_split, t1 = min(t0 + p.kv_len_per_split, n);
+  const int64_t slot = (int64_t)b * p.rows * p.num_splits + j;
+  if (t0 >= t1) {  // uniform over the workgroup
+    const int row = rg * kRowsPerGroup + (int)threadIdx.x;
+    if ((int)threadIdx.x < kRowsPerGroup && row < p.rows) p.lse_part[slot * p.l_slot + (int64_t)row * p.l_row] = -INFINITY;
+    return;
+  }
+  auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  if constexpr (kFp8Fmt)
+    run_range_fp8<FMT == kFmtFp8Q>(p, lds_addr((lds_ptr)smem), uni(b), uni(n), rg, uni(t0 / TT),
+                                    uni((t1 + TT - 1) / TT), slot);
+  else
+    run_range<FMT, true>(p, lds_addr((lds_ptr)smem), uni(b), uni(n), rg, uni(t0 / TT), uni((t1 + TT - 1) / TT),
+                         slot);
+}
+
 // ------------------------------------------------------------------------------------
 // combine kernels (one wavefront per output row)
 // ------------------------------------------------------------------------------------
@@ -2107,6 +2137,25 @@ hipError_t launch_decode_paged(int fmt, const DecodeParams& p, hipStream_t strea
       break;
     default:
       hipLaunchKernelGGL(decode_paged_kernel<kFmtFp8Q>, dim3(blocks), dim3(kThreads), 0, stream, p);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_paged_splits(int fmt, const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid(p.row_groups, p.num_splits, p.B);
+  switch (fmt) {
+    case kFmtBf16:
+      hipLaunchKernelGGL(decode_paged_splits_kernel<kFmtBf16>, grid, dim3(kThreads), 0, stream, p);
+      break;
+    case kFmtFp8:
+      hipLaunchKernelGGL(decode_paged_splits_kernel<kFmtFp8>, grid, dim3(kThreads), 0, stream, p);
+      break;
+    case kFmtNvfp4:
+      hipLaunchKernelGGL(decode_paged_splits_kernel<kFmtNvfp4>, grid, dim3(kThreads), 0, stream, p);
+      break;
+    default:
+      hipLaunchKernelGGL(decode_paged_splits_kernel<kFmtFp8Q>, grid, dim3(kThreads), 0, stream, p);
       break;
   }
   return hipGetLastError();

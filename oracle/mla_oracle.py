@@ -408,6 +408,37 @@ def paged_decode(q, qpe, cache, fmt: int, kv_scale: float, page_size: int, page_
     return np.stack(outs), np.stack(lses)
 
 
+def paged_decode_split_partials(q, qpe, cache, fmt: int, kv_scale: float, page_size: int, page_stride: int,
+                                block_tables, seq_lens, sm_scale: float, kv_len_per_split: int, num_splits: int):
+    """Per-split partials of the paged op with fixed-length splits (TileGym page,
+    ``forward``: split j of a sequence covers tokens [j*L, (j+1)*L) with L =
+    kv_len_per_split, each writing a normalised partial and its LSE; TokenSpeed page,
+    ``forward_decode``: the query rows and the paged cache).  A request of n tokens
+    clips split j to [j*L, min((j+1)*L, n)); splits past n, and rows that see no token
+    of a split (q_len > 1), are empty: O_j = 0, lse_j = -inf.  Returns o_part
+    [B,q_len,H,NS,512] and lse_part [B,q_len,H,NS] (float64)."""
+    q = np.asarray(q, np.float64)
+    qpe = np.asarray(qpe, np.float64)
+    if fmt == FMT_FP8_QFP8:
+        q = decode_e4m3fn(quantize_e4m3(q.astype(np.float32)))
+        qpe = decode_e4m3fn(quantize_e4m3(qpe.astype(np.float32)))
+    B, q_len, H, _ = q.shape
+    L, NS = kv_len_per_split, num_splits
+    o_part = np.zeros((B, q_len, H, NS, LATENT))
+    lse_part = np.full((B, q_len, H, NS), -np.inf)
+    for b in range(B):
+        n = int(seq_lens[b])
+        kv = gather_request(cache, fmt, kv_scale, page_size, page_stride, block_tables[b], n)
+        vis = np.repeat(visible_counts(n, q_len), H)
+        qf = _qfull(q[b], qpe[b]).reshape(q_len * H, ROW)
+        for j in range(NS):
+            lo, hi = min(j * L, n), min((j + 1) * L, n)
+            o, l = attend_range(qf, kv, vis, sm_scale, lo, hi)
+            o_part[b, :, :, j] = o.reshape(q_len, H, LATENT)
+            lse_part[b, :, :, j] = l.reshape(q_len, H)
+    return o_part, lse_part
+
+
 # ----------------------------------------------------------------------------------
 # KV-cache append: the write that precedes the decode
 # ----------------------------------------------------------------------------------

@@ -268,3 +268,83 @@ def _ext(**kw):
 ])
 def test_paged_decode_ext_rejects(kw, status):
     assert _ext(**kw) == status
+
+
+def test_plan_paged_splits_is_the_tilegym_formula_on_the_longest_sequence():
+    # hand-worked: est = 256 / 64 = 4, 32768 / 4 = 8192 -> L = 8192, 4 splits
+    assert mla.plan_paged_splits(256, 64, 1, [1000] * 63 + [32768], 64) == (8192, 4)
+    # est = 64, 4096 / 64 = 64 -> 128 (the page's floor), 32 splits
+    assert mla.plan_paged_splits(256, 4, 1, [4096] * 4, 64) == (128, 32)
+    # all lengths 0: the longest counts as 1 -> one split of 128
+    assert mla.plan_paged_splits(1, 3, 2, [0, 0, 0], 32) == (128, 1)
+    # est = 300 / 7 = 42, 70000 / 42 = 1666 -> 2048, ceil(70000 / 2048) = 35
+    assert mla.plan_paged_splits(300, 7, 1, [5000, 129, 70000, 3, 8, 9, 10], 32) == (2048, 35)
+    # the contiguous planner (pinned by the golden file) with S_kv = the longest sequence
+    for cus in (1, 80, 256):
+        for lens in ([1], [100, 7], [4096] * 4, [33, 70000, 5], [65536] * 64):
+            assert mla.plan_paged_splits(cus, len(lens), 1, lens, 64) == \
+                oracle.plan_contig(cus, len(lens), max(1, max(lens))), (cus, lens)
+
+
+def test_plan_paged_splits_rejects():
+    L = mla.lib()
+    a, b = ctypes.c_int(), ctypes.c_int()
+    sl = (ctypes.c_int32 * 2)(5, 6)
+    p = ctypes.cast(sl, ctypes.c_void_p)
+    assert L.mla_plan_paged_splits(256, 2, 1, None, 64, ctypes.byref(a), ctypes.byref(b)) == mla.MLA_ERR_INVALID_ARG
+    assert L.mla_plan_paged_splits(0, 2, 1, p, 64, ctypes.byref(a), ctypes.byref(b)) == mla.MLA_ERR_INVALID_ARG
+    assert L.mla_plan_paged_splits(256, 2, 9, p, 64, ctypes.byref(a), ctypes.byref(b)) == mla.MLA_ERR_UNSUPPORTED
+    assert L.mla_plan_paged_splits(256, 2, 1, p, 48, ctypes.byref(a), ctypes.byref(b)) == mla.MLA_ERR_UNSUPPORTED
+    assert L.mla_plan_paged_splits(256, 2, 1, p, 64, None, ctypes.byref(b)) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_paged_splits_workspace_bytes():
+    n = mla.paged_splits_workspace_bytes(64, 1, 128, 4)
+    parts = 64 * 128 * 4
+    assert n == -(-parts * 512 * 4 // 256) * 256 + -(-parts * 4 // 256) * 256
+    assert n >= parts * oracle.workspace_floats_per_split(1, 1) * 4  # (D + 1) fp32 per split and head
+    assert mla.paged_splits_workspace_bytes(0, 1, 128, 4) == 0
+    assert mla.paged_splits_workspace_bytes(4, 1, 24, 4) == 0
+    assert mla.paged_splits_workspace_bytes(4, 1, 128, 0) == 0
+
+
+def _splits(**kw):
+    a = dict(q=F, qpe=F, cache=F, fmt=1, kv_scale=1.0, num_pages=10, page_size=64, stride=64 * 576, bt=F, mb=4,
+             sl=F, B=2, q_len=1, H=128, sm=0.07, L=128, ns=2, ws=F, ws_bytes=1 << 30, o=F, lse=F)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return mla.lib().mla_paged_decode_splits(vp(a["q"]), vp(a["qpe"]), vp(a["cache"]), a["fmt"], a["kv_scale"],
+                                             a["num_pages"], a["page_size"], a["stride"], vp(a["bt"]), a["mb"],
+                                             vp(a["sl"]), a["B"], a["q_len"], a["H"], a["sm"], a["L"], a["ns"],
+                                             vp(a["ws"]), a["ws_bytes"], vp(a["o"]), vp(a["lse"]), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(cache=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(ws=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(ws=F + 16), mla.MLA_ERR_INVALID_ARG),
+    (dict(o=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(lse=F + 2), mla.MLA_ERR_INVALID_ARG),
+    (dict(fmt=4), mla.MLA_ERR_UNSUPPORTED),
+    (dict(page_size=16), mla.MLA_ERR_UNSUPPORTED),
+    (dict(q_len=9), mla.MLA_ERR_UNSUPPORTED),
+    (dict(H=24), mla.MLA_ERR_UNSUPPORTED),
+    (dict(B=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(L=100), mla.MLA_ERR_INVALID_ARG),
+    (dict(L=64), mla.MLA_ERR_INVALID_ARG),
+    (dict(ns=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(ns=65536), mla.MLA_ERR_INVALID_ARG),
+    (dict(ns=1), mla.MLA_ERR_INVALID_ARG),            # 1 x 128 tokens < 4 blocks x 64
+    (dict(ws_bytes=1000), mla.MLA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(kv_scale=0.0), mla.MLA_ERR_INVALID_ARG),
+    (dict(sm=-1.0), mla.MLA_ERR_INVALID_ARG),
+    (dict(stride=64 * 576 - 16), mla.MLA_ERR_INVALID_ARG),
+])
+def test_paged_decode_splits_rejects(kw, status):
+    assert _splits(**kw) == status
+
+
+def test_paged_decode_splits_workspace_boundary():
+    need = mla.paged_splits_workspace_bytes(2, 1, 128, 2)
+    assert _splits(ws_bytes=need - 1) == mla.MLA_ERR_WORKSPACE_TOO_SMALL

@@ -291,6 +291,51 @@ def test_page_permutation_invariance():
     assert np.isfinite(O).all()
 
 
+def test_paged_split_partials_merge_to_the_whole_and_clip_at_the_length():
+    """Fixed-length splits of the paged op: merging the partials gives the unsplit
+    result; split j of a request equals attention over that request's tokens [jL, (j+1)L)
+    alone (brute force on the gathered rows); splits at or past the length are empty."""
+    w = gen.make_paged(B=4, H=3, q_len=2, lo=1, hi=1, page_size=32, fmt=gen.FMT_FP8, seed=23,
+                       seq_lens=[0, 1, 130, 300], max_blocks=10)
+    q, qpe = w.q_f64()
+    args = (q, qpe, w.cache, w.fmt, w.kv_scale, w.page_size, w.page_stride, w.block_tables, w.seq_lens, w.sm_scale)
+    O, L = oracle.paged_decode(*args)
+    for Ls, ns in ((128, 3), (128, 5), (256, 2), (512, 1)):
+        op, lp = oracle.paged_decode_split_partials(*args, Ls, ns)
+        assert op.shape == (4, 2, 3, ns, 512) and lp.shape == (4, 2, 3, ns)
+        Oc, Lc = oracle.combine(op.reshape(-1, ns, 512), lp.reshape(-1, ns))
+        assert np.abs(Oc.reshape(O.shape) - O).max() < 1e-12, Ls
+        fin = np.isfinite(L)
+        assert np.array_equal(np.isfinite(Lc.reshape(L.shape)), fin)
+        assert np.abs(Lc.reshape(L.shape)[fin] - L[fin]).max() < 1e-12, Ls
+        for b, n in enumerate(w.seq_lens):
+            for j in range(ns):
+                if j * Ls >= n:
+                    assert np.isneginf(lp[b, :, :, j]).all() and (op[b, :, :, j] == 0).all()
+    # the FP8-query format rounds the query before splitting, as the unsplit op does
+    qargs = (q, qpe, w.cache, oracle.FMT_FP8_QFP8) + args[4:]
+    Oq, Lq = oracle.paged_decode(*qargs)
+    op, lp = oracle.paged_decode_split_partials(*qargs, 128, 3)
+    Oc, _ = oracle.combine(op.reshape(-1, 3, 512), lp.reshape(-1, 3))
+    assert np.abs(Oc.reshape(Oq.shape) - Oq).max() < 1e-12 and np.abs(Oq - O).max() > 1e-6
+    # brute force: request 3 (300 tokens), split 1 of L = 128 covers tokens 128..255; query 0
+    # sees 299 tokens, so all of them; one head
+    kv = oracle.gather_request(w.cache, w.fmt, w.kv_scale, w.page_size, w.page_stride, w.block_tables[3], 300)
+    op, lp = oracle.paged_decode_split_partials(*args, 128, 3)
+    qf = np.concatenate([q[3, 0, 1], qpe[3, 0, 1]])
+    s = np.array([w.sm_scale * float(qf @ kv[t]) for t in range(128, 256)])
+    p = np.exp(s - s.max())
+    assert abs(lp[3, 0, 1, 1] - (s.max() + math.log(p.sum()))) < 1e-12
+    assert np.abs(op[3, 0, 1, 1] - (p / p.sum()) @ kv[128:256, :512]).max() < 1e-12
+    # request 3, split 2 (256..299): query 0 sees tokens up to 298 -> 43 tokens, query 1 all 44
+    s0 = np.array([w.sm_scale * float(np.concatenate([q[3, 0, 0], qpe[3, 0, 0]]) @ kv[t]) for t in range(256, 299)])
+    assert abs(lp[3, 0, 0, 2] - (s0.max() + math.log(np.exp(s0 - s0.max()).sum()))) < 1e-12
+    # request 1 (one token): query 0 sees nothing, query 1 sees token 0 with weight 1
+    assert np.isneginf(lp[1, 0]).all() and (op[1, 0] == 0).all()
+    kv1 = oracle.gather_request(w.cache, w.fmt, w.kv_scale, w.page_size, w.page_stride, w.block_tables[1], 1)
+    assert np.abs(op[1, 1, :, 0] - kv1[0, :512]).max() < 1e-12
+
+
 def test_causal_verify_rows():
     """q_len = 2: query 0 sees n-1 tokens and equals a one-token decode over n-1 tokens;
     query 1 sees all n; zero queries give ln(n-1) and ln(n)."""
