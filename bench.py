@@ -340,6 +340,9 @@ def run(args, w, mla, torch, np, gen):
     if paged and fmt == gen.FMT_FP8 and not args.no_variant:
         out["fp8_query_variant"] = time_fp8_query_variant(mla, torch, np, w, q, qpe, cache, bt, sl, G, args, flops,
                                                           nbytes, ceilings)
+    if paged and not args.no_variant:
+        out["fixed_splits_variant"] = time_fixed_splits(mla, torch, np, w, q, qpe, cache, bt, sl, args, flops, nbytes,
+                                                        ceilings, flush_buf)
     if paged and not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
@@ -363,6 +366,29 @@ def time_fp8_query_variant(mla, torch, np, w, q, qpe, cache, bt, sl, G, args, fl
             "decode_ms": round(dec, 5), "roofline": roofline(flops, nbytes, dec, "fp8", ceilings, None)}
 
 
+def time_fixed_splits(mla, torch, np, w, q, qpe, cache, bt, sl, args, flops, nbytes, ceilings, flush_buf):
+    """The same pages through the fixed-length split interface (mla_plan_paged_splits on the
+    host lengths, then mla_paged_decode_splits): every split covers kv_len_per_split tokens,
+    so the longest request sets the time.  Same flush and event timing as the headline."""
+    dev = q.device
+    L, _ = mla.plan_paged_splits(mla.device_num_cus(0), w.B, w.q_len, w.seq_lens.tolist(), w.page_size)
+    ns = -(-w.max_blocks * w.page_size // L)
+    ws = torch.empty(mla.paged_splits_workspace_bytes(w.B, w.q_len, w.H, ns), dtype=torch.uint8, device=dev)
+    o = torch.empty((w.B, w.q_len, w.H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.q_len, w.H), dtype=torch.float32, device=dev)
+    run = lambda: mla.paged_decode_splits(q, qpe, cache, w.fmt, bt, sl, w.page_size, w.page_stride, w.kv_scale,
+                                          w.sm_scale, kv_len_per_split=L, max_splits=ns, workspace=ws, o=o, lse=lse)
+    for _ in range(max(args.warmup, 20)):
+        run()
+    _, ms, _ = timed_steps(torch, args.steps, run, lambda: None, flush_buf)
+    t = float(np.mean(ms))
+    log(f"[bench] fixed splits (L={L}, {ns} splits): decode + combine {t:.4f} ms")
+    return {"kv_len_per_split": L, "max_splits": ns, "ms_per_step": round(t, 5),
+            "value": round(flops / (t * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+            "value_from": "hip events around both launches" + (", caches flushed before each step" if flush_buf
+                                                               is not None else "")}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -378,7 +404,7 @@ def main():
     ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-variant", action="store_true",
-                    help="skip the extra timing of the FP8-query variant on FP8 workloads")
+                    help="skip the extra timings (FP8-query variant on FP8 workloads; fixed-length splits)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the decode, run torch's fill and copy kernels on buffers of this many MiB "
                          "(known HBM bytes, used to scale the FETCH_SIZE / WRITE_SIZE counters)")
