@@ -131,7 +131,8 @@ size_t mla_paged_workspace_bytes(int B, int q_len, int H, int num_splits);
  *   lse_part [B, H, NS] fp32 (out)       lse_j (natural log; -inf for no token)
  * with NS = ceil(S_kv / kv_len_per_split); split j covers tokens
  * [j*L, min((j+1)*L, S_kv)).  kv_len_per_split must be a power of two >= 128 (the
- * page's assertions); sm_scale finite and >= 0.  H: multiple of 16, <= 128.  1 <= B <= 65535; NS <= 65535. */
+ * page's assertions); sm_scale finite and >= 0.  H: multiple of 16, <= 128.  1 <= B <= 65535; NS <= 65535;
+ * NS * B <= 2^30 (one workgroup per request and split). */
 int mla_decode_splitkv(const uint16_t* q, const uint16_t* qpe, const uint16_t* kv,
                        const uint16_t* kpe, int B, int H, int S_kv, float sm_scale,
                        int kv_len_per_split, float* o_part, float* lse_part, void* stream);

@@ -138,7 +138,8 @@ int mla_decode_splitkv(const uint16_t* q, const uint16_t* qpe, const uint16_t* k
   // the page's assertions: power of two and at least TILE_N = 128
   if (kv_len_per_split < 128 || (kv_len_per_split & (kv_len_per_split - 1)) != 0) return MLA_ERR_INVALID_ARG;
   const int ns = (S_kv + kv_len_per_split - 1) / kv_len_per_split;
-  if (ns > 65535 || B > 65535) return MLA_ERR_INVALID_ARG;
+  // one workgroup per (request, split): the count must fit the kernel's int indexing
+  if (ns > 65535 || B > 65535 || (int64_t)ns * B > (int64_t)(1 << 30)) return MLA_ERR_INVALID_ARG;
 
   DecodeParams p{};
   p.q = q;
@@ -151,7 +152,7 @@ int mla_decode_splitkv(const uint16_t* q, const uint16_t* qpe, const uint16_t* k
   p.q_len = 1;
   p.H = H;
   p.rows = H;
-  p.row_groups = (H + kRowsPerGroup - 1) / kRowsPerGroup;
+  p.row_groups = 1;  // H <= 128 rows: one group (of 128 / D rows for few heads)
   p.num_splits = ns;
   p.score_scale = sm_scale * kLog2e;
   p.v_scale = 1.f;

@@ -1823,13 +1823,20 @@ __device__ __forceinline__ void run_range_fp8(const DecodeParams& p, uint32_t sm
 // decode kernels
 // ------------------------------------------------------------------------------------
 
-// Contiguous: grid (row groups of 128 / D rows, num_splits, B); split j covers
-// [j*L, min((j+1)*L, S)).
+// Contiguous: U = row_groups * num_splits * B work items (row group of 128 / D rows,
+// split j, request b); split j covers [j*L, min((j+1)*L, S)).  Workgroup ids are dealt
+// round-robin over the 8 XCDs, so id -> item is XCD-aware: XCD x takes the consecutive
+// items x * per .. x * per + per - 1 of the (request, split, row group) order, and the
+// splits of one request share that XCD's L2 (the query is read from HBM once per request
+// rather than once per split).  The grid holds 8 * per ids; ids past U exit.
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_contig_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<kFmtBf16>()];
-  const int rg = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int R = p.row_groups, U = R * p.num_splits * p.B, per = (U + 7) / 8;
+  const int u = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (u >= U) return;
+  const int rg = u % R, j = (u / R) % p.num_splits, b = u / (R * p.num_splits);
   const int t0 = j * p.kv_len_per_split;
   const int t1 = min(t0 + p.kv_len_per_split, p.S);
   // slot b*H*NS + j with row = head addresses o_part [B, H, NS, 512]
@@ -2116,7 +2123,10 @@ __global__ __launch_bounds__(256) void combine_paged_kernel(const CombineParams 
 // 2 up to 64) instead of repeating its last row.
 hipError_t launch_decode_contig(const DecodeParams& p, hipStream_t stream) {
   const int D = p.rows <= kWaveRows ? 4 : p.rows <= 2 * kWaveRows ? 2 : 1;
-  dim3 grid((p.rows + kRowsPerGroup / D - 1) / (kRowsPerGroup / D), p.num_splits, p.B);
+  // row_groups counts groups of 128 / D rows (checked by the caller against the grid's
+  // size limit)
+  const int U = p.row_groups * p.num_splits * p.B;
+  const dim3 grid((unsigned)(((U + 7) / 8) * 8));
   if (D == 4) hipLaunchKernelGGL(decode_contig_kernel<4>, grid, dim3(kThreads), 0, stream, p);
   else if (D == 2) hipLaunchKernelGGL(decode_contig_kernel<2>, grid, dim3(kThreads), 0, stream, p);
   else hipLaunchKernelGGL(decode_contig_kernel<1>, grid, dim3(kThreads), 0, stream, p);

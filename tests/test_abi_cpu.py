@@ -157,6 +157,9 @@ def _contig(**kw):
     (dict(H=136), mla.MLA_ERR_UNSUPPORTED),
     (dict(sm=float("nan")), mla.MLA_ERR_INVALID_ARG),
     (dict(sm=-1.0), mla.MLA_ERR_INVALID_ARG),
+    (dict(B=65536), mla.MLA_ERR_INVALID_ARG),
+    (dict(S=65536 * 128), mla.MLA_ERR_INVALID_ARG),        # 65536 splits
+    (dict(B=32768, S=32769 * 128), mla.MLA_ERR_INVALID_ARG),  # NS * B > 2^30 workgroups
 ])
 def test_decode_splitkv_rejects(kw, status):
     assert _contig(**kw) == status
