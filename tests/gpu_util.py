@@ -4,9 +4,11 @@ Tolerances (max-abs, from the accuracy target of this decode path):
   * bf16 cache: O <= 1e-2, LSE <= 1e-3.
   * FP8 / NVFP4 cache: O <= 2e-2 against the oracle run on the dequantised cache; LSE
     keeps 1e-3, since dequantisation to bf16 is exact and only the accumulation differs.
-Budget behind them: O is rounded to bf16 (<= 2^-9 |O|, |O| < 2 here), P is rounded to
-bf16 before the PV product (relative 2^-9 per weight), and fp32 accumulation over
-<= 64k tokens adds ~1e-5 to the LSE.
+Budget behind them: P is rounded to bf16 before the PV product (relative 2^-9 per
+weight), and fp32 accumulation over <= 64k tokens adds ~1e-5 to the LSE.  The final O is
+then rounded to bf16; check_o adds that rounding (half an ulp, <= 2^-8 |O|) to the
+tolerance, since a row that sees only a few tokens can have |O| above 2.5.  The fp32
+partials are compared without it.
 """
 
 import sys
@@ -73,6 +75,23 @@ def check(what: str, got: np.ndarray, want: np.ndarray, tol: float):
     """Assert max |got - want| <= tol, and print the margin (it shows in the test log)."""
     e = max_err(got, want)
     say(f"  {what}: max|d|={float(e):.3e} tol={tol:.0e} ({float(e) / tol:.2f} of tol)")
+    assert e <= tol, (what, e)
+    return e
+
+
+def check_o(what: str, got: np.ndarray, want: np.ndarray, tol: float):
+    """Check a final output O, which the kernels round to bf16 (nearest even): its
+    rounding alone moves a value by up to half a bf16 ulp, at most 2^-8 |O|, which passes
+    the fixed tolerances once |O| > 2.5 (a row that sees a few tokens takes the values of
+    those tokens, up to about 4.5 here).  Asserts |got - want| <= tol + 2^-8 |want| and
+    prints the margin."""
+    e = max_err(got, want)
+    if np.isfinite(float(e)) and got.size:
+        m = ~np.isneginf(want)
+        d = np.where(m, np.abs(got - np.where(m, want, 0)) - 2.0 ** -8 * np.abs(np.where(m, want, 0)), -np.inf)
+        i = np.unravel_index(int(np.argmax(d)), d.shape)
+        e = Err(max(float(d[i]), 0.0), f"at {tuple(int(x) for x in i)} got {got[i]:.6g} want {want[i]:.6g}")
+    say(f"  {what}: max(|d| - 2^-8|O|)={float(e):.3e} tol={tol:.0e} ({float(e) / tol:.2f} of tol)")
     assert e <= tol, (what, e)
     return e
 

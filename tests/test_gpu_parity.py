@@ -12,7 +12,7 @@ import torch
 import oracle
 import mla_split_kv_02_amd as mla
 from workloads import gen
-from gpu_util import (TOL_LSE, TOL_O_BF16, TOL_O_QUANT, bf16_dev, check, host, i32_dev, max_err,
+from gpu_util import (TOL_LSE, TOL_O_BF16, TOL_O_QUANT, bf16_dev, check, check_o, host, i32_dev, max_err,
                       paged_device_inputs, say, u8_dev)
 
 pytestmark = pytest.mark.gpu
@@ -47,7 +47,7 @@ def test_contig_splitkv_matches_oracle(B, H, S, L):
     ro, rl = oracle.contig_decode(q, qpe, kv, kpe, c.sm_scale)
     check("op", op, rop, TOL_O_BF16)
     check("lp", lp, rlp, TOL_LSE)
-    check("o", o, ro, TOL_O_BF16)
+    check_o("o", o, ro, TOL_O_BF16)
     check("lse", lse, rl, TOL_LSE)
 
 
@@ -59,7 +59,7 @@ def test_contig_b4_h16_s4096_full_size():
     op, lp, o, lse, _ = _contig_run(c, L)
     q, qpe, kv, kpe = c.f64()
     ro, rl = oracle.contig_decode(q, qpe, kv, kpe, c.sm_scale)
-    check("o", o, ro, TOL_O_BF16)
+    check_o("o", o, ro, TOL_O_BF16)
     check("lse", lse, rl, TOL_LSE)
     rop, rlp = oracle.contig_decode_splitkv(q[:1], qpe[:1], kv[:1], kpe[:1], c.sm_scale, L)
     check("op[:1]", op[:1], rop, TOL_O_BF16)
@@ -164,7 +164,7 @@ def test_paged_matches_oracle(fmt, q_len, page_size):
     ro, rl = _paged_ref(w)
     for ns in (None, 1, 5):
         o, lse = _paged_run(w, ns)
-        check(f"o {ns}", o, ro, _tol_o(fmt))
+        check_o(f"o {ns}", o, ro, _tol_o(fmt))
         check(f"lse {ns}", lse, rl, TOL_LSE)
 
 
@@ -175,7 +175,7 @@ def test_paged_head_and_query_counts(H, q_len):
                        max_blocks=4)
     ro, rl = _paged_ref(w)
     o, lse = _paged_run(w)
-    check("o", o, ro, TOL_O_QUANT)
+    check_o("o", o, ro, TOL_O_QUANT)
     check("lse", lse, rl, TOL_LSE)
 
 
@@ -188,7 +188,7 @@ def test_paged_one_long_request_spans_every_range(ns):
                        seq_lens=[16000, 40], max_blocks=250)
     ro, rl = _paged_ref(w)
     o, lse = _paged_run(w, ns)
-    check("o", o, ro, TOL_O_QUANT)
+    check_o("o", o, ro, TOL_O_QUANT)
     check("lse", lse, rl, TOL_LSE)
 
 
@@ -199,7 +199,7 @@ def test_paged_empty_and_short_requests():
     ro, rl = _paged_ref(w)
     for ns in (None, 1, 2, 3):
         o, lse = _paged_run(w, ns)
-        check(f"o {ns}", o, ro, TOL_O_BF16)
+        check_o(f"o {ns}", o, ro, TOL_O_BF16)
         check(f"lse {ns}", lse, rl, TOL_LSE)
         assert (o[0] == 0).all() and np.isneginf(lse[0]).all()
         assert np.isneginf(lse[1, 0]).all() and (o[1, 0] == 0).all()
@@ -226,7 +226,7 @@ def test_paged_padded_page_stride():
                        page_stride=64 * 324 + 48)
     ro, rl = _paged_ref(w)
     o, lse = _paged_run(w)
-    check("o", o, ro, TOL_O_QUANT)
+    check_o("o", o, ro, TOL_O_QUANT)
     check("lse", lse, rl, TOL_LSE)
 
 
@@ -241,7 +241,7 @@ def test_paged_fp8_every_code():
     w.kv_scale = 1.0 / 128  # |values| <= 3.5 keeps the bf16 rounding of O inside the tolerance
     ro, rl = _paged_ref(w)
     o, lse = _paged_run(w)
-    check("o", o, ro, TOL_O_QUANT)
+    check_o("o", o, ro, TOL_O_QUANT)
     check("lse", lse, rl, TOL_LSE)
 
 
@@ -257,7 +257,7 @@ def test_paged_nvfp4_every_code_and_scale():
     w.block_tables[:] = 0
     ro, rl = _paged_ref(w)
     o, lse = _paged_run(w)
-    check("o", o, ro, TOL_O_QUANT)
+    check_o("o", o, ro, TOL_O_QUANT)
     check("lse", lse, rl, TOL_LSE)
 
 
@@ -269,7 +269,7 @@ def test_paged_fp8_b64_h128_full_size():
     o, lse = _paged_run(w, mla.plan_paged(256, w.B, w.q_len, w.H))
     assert np.isfinite(o).all()
     ro, rl = _paged_ref(w)
-    check("O (64 requests)", o, ro, TOL_O_QUANT)
+    check_o("O (64 requests)", o, ro, TOL_O_QUANT)
     check("LSE (64 requests)", lse, rl, TOL_LSE)
 
 
@@ -294,7 +294,7 @@ def test_paged_fp8_query_magnitudes_and_peaked_rows(qexp, scale_exp):
     w.sm_scale = w.sm_scale * 2.0 ** scale_exp
     ro, rl = _paged_ref(w)
     o, lse = _paged_run(w)
-    check("o", o, ro, TOL_O_QUANT)
+    check_o("o", o, ro, TOL_O_QUANT)
     check("lse", lse, rl, TOL_LSE)
 
 
@@ -324,7 +324,7 @@ def test_paged_fp8_rising_scores(q_len, page_size):
     ro, rl = _paged_ref(w)
     for ns in (None, 1):
         o, lse = _paged_run(w, ns)
-        check(f"o {ns}", o, ro, TOL_O_QUANT)
+        check_o(f"o {ns}", o, ro, TOL_O_QUANT)
         check(f"lse {ns}", lse, rl, TOL_LSE)
 
 
@@ -364,7 +364,7 @@ def test_paged_fp8_dominant_token_over_long_tail(fmt, where):
     # the bulk carries a large share of the weight in most heads
     for ns in (None, 1):
         o, lse = _paged_run(w, ns)
-        check(f"O ns={ns}", o, ro, TOL_O_QUANT)
+        check_o(f"O ns={ns}", o, ro, TOL_O_QUANT)
         check(f"LSE ns={ns}", lse, rl, TOL_LSE)
 
 
@@ -397,7 +397,7 @@ def test_paged_window_and_sinks_match_oracle(fmt, q_len):
                                      sinks=None if sk is None else sk.astype(np.float64))
         for ns in (None, 1, 7):
             o, lse = _paged_run_ext(w, window, sk, ns)
-            check(f"o {(window, ns)}", o, ro, _tol_o(base_fmt))
+            check_o(f"o {(window, ns)}", o, ro, _tol_o(base_fmt))
             check(f"lse {(window, ns)}", lse, rl, TOL_LSE)
 
 
@@ -439,7 +439,7 @@ def test_paged_fp8_query_matches_oracle(q_len, page_size):
     ro, rl = _paged_ref(w)
     for ns in (None, 1, 5):
         o, lse = _paged_run(w, ns)
-        check(f"o {ns}", o, ro, TOL_O_QUANT)
+        check_o(f"o {ns}", o, ro, TOL_O_QUANT)
         check(f"lse {ns}", lse, rl, TOL_LSE)
     # the query really is rounded: the bf16-query path on the same pages differs
     w.fmt = gen.FMT_FP8
@@ -454,7 +454,7 @@ def test_paged_fp8_query_head_and_query_counts(H, q_len):
                              seed=150 + H + q_len, max_blocks=4))
     ro, rl = _paged_ref(w)
     o, lse = _paged_run(w)
-    check("o", o, ro, TOL_O_QUANT)
+    check_o("o", o, ro, TOL_O_QUANT)
     check("lse", lse, rl, TOL_LSE)
 
 
@@ -478,7 +478,7 @@ def test_paged_fp8_query_rounding_ties_and_every_code():
     w.qpe = bits[w.q.size:].reshape(w.qpe.shape)
     ro, rl = _paged_ref(w)
     o, lse = _paged_run(w)
-    check("o", o, ro, TOL_O_QUANT)
+    check_o("o", o, ro, TOL_O_QUANT)
     check("lse", lse, rl, TOL_LSE)
 
 
@@ -492,7 +492,7 @@ def test_paged_fp8_query_b64_h128_full_size_sampled():
     order = np.argsort(w.seq_lens)
     pick = sorted({int(order[i]) for i in list(range(0, 64, 4)) + [63]})
     ro, rl = _paged_ref(w, requests=pick)
-    check(f"O ({len(pick)} requests)", o[pick], ro, TOL_O_QUANT)
+    check_o(f"O ({len(pick)} requests)", o[pick], ro, TOL_O_QUANT)
     check(f"LSE ({len(pick)} requests)", lse[pick], rl, TOL_LSE)
 
 
@@ -507,5 +507,5 @@ def test_paged_nvfp4_b128_h128_q2_full_size_sampled():
     order = np.argsort(w.seq_lens)
     pick = sorted({int(order[i]) for i in list(range(0, 128, 8)) + [127]})
     ro, rl = _paged_ref(w, requests=pick)
-    check(f"O ({len(pick)} requests)", o[pick], ro, TOL_O_QUANT)
+    check_o(f"O ({len(pick)} requests)", o[pick], ro, TOL_O_QUANT)
     check(f"LSE ({len(pick)} requests)", lse[pick], rl, TOL_LSE)

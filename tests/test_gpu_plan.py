@@ -13,7 +13,7 @@ import oracle
 import mla_split_kv_02_amd as mla
 import plan_mirror as pm
 from workloads import gen
-from gpu_util import TOL_LSE, TOL_O_BF16, TOL_O_QUANT, check, host, paged_device_inputs, say
+from gpu_util import TOL_LSE, TOL_O_BF16, TOL_O_QUANT, check, check_o, host, paged_device_inputs, say
 
 pytestmark = pytest.mark.gpu
 
@@ -114,5 +114,5 @@ def test_partials_headline_full_size():
     pick = [0, 31, 63]
     ro, rl = oracle.paged_decode(*w.q_f64(), w.cache, w.fmt, w.kv_scale, w.page_size, w.page_stride,
                                  w.block_tables, w.seq_lens, w.sm_scale, requests=pick)
-    check("combine O", o[pick], ro, TOL_O_QUANT)
+    check_o("combine O", o[pick], ro, TOL_O_QUANT)
     check("combine LSE", lse[pick], rl, TOL_LSE)

@@ -10,7 +10,7 @@ import torch
 import oracle
 import mla_split_kv_02_amd as mla
 from workloads import gen
-from gpu_util import TOL_LSE, TOL_O_BF16, TOL_O_QUANT, check, host, paged_device_inputs, say
+from gpu_util import TOL_LSE, TOL_O_BF16, TOL_O_QUANT, check, check_o, host, paged_device_inputs, say
 
 pytestmark = pytest.mark.gpu
 
@@ -54,7 +54,7 @@ def _refs(w, L, ns, requests=None):
 def _check_all(w, got, refs, what=""):
     o, lse, L, ns, op, lp = got
     ro, rl, rop, rlp = refs
-    check(f"o {what}", o, ro, _tol_o(w.fmt))
+    check_o(f"o {what}", o, ro, _tol_o(w.fmt))
     check(f"lse {what}", lse, rl, TOL_LSE)
     check(f"lse_part {what}", lp, rlp, TOL_LSE)
     live = np.isfinite(rlp)
@@ -116,7 +116,7 @@ def test_paged_splits_agree_with_the_planned_path_and_repeat_bitwise():
     a = _run(w)
     b = _run(w)
     torch.cuda.synchronize()
-    check("o vs planned", a[0], host(o1), TOL_O_QUANT)
+    check_o("o vs planned", a[0], host(o1), TOL_O_QUANT)
     check("lse vs planned", a[1], host(l1), TOL_LSE)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
@@ -133,7 +133,7 @@ def test_paged_splits_fp8_b64_h128_full_size():
     assert np.isfinite(o).all()
     ro, rl = oracle.paged_decode(*w.q_f64(), w.cache, w.fmt, w.kv_scale, w.page_size, w.page_stride,
                                  w.block_tables, w.seq_lens, w.sm_scale)
-    check("O (64 requests)", o, ro, TOL_O_QUANT)
+    check_o("O (64 requests)", o, ro, TOL_O_QUANT)
     check("LSE (64 requests)", lse, rl, TOL_LSE)
     order = np.argsort(w.seq_lens)
     pick = sorted({int(order[0]), int(order[21]), int(order[42]), int(order[63])})
