@@ -2020,14 +2020,59 @@ void decode_paged_splits_kernel(const DecodeParams p) {
 // Merge ns partials of one row; lse(j) returns lse_j (-inf for an empty or dead split)
 // and opart(j) the address of O_j.  sink: an extra logit of the row that joins the
 // denominator and carries no value (-inf: none).  Lane j % 64 holds lse_j, so the row's
-// maximum, LSE and weights take wavefront reductions instead of a serial walk; the O_j
-// loads then go out four splits at a time, back to back (their addresses do not depend
-// on the weights).  An O_j of weight 0 (lse_j = -inf, or too far below the row's LSE) is
-// loaded but adds nothing, NaN included.
+// maximum, LSE and weights take wavefront reductions instead of a serial walk.  Up to 8
+// partials (the usual case), every O_j load goes out together with the lse loads, since
+// their addresses do not depend on the weights: one memory round trip instead of two.
+// Beyond that the O_j loads go out four splits at a time after the weights.  An O_j of
+// weight 0 (lse_j = -inf, or too far below the row's LSE) is loaded but adds nothing, NaN
+// included.
 template <class Lse, class OPart>
 __device__ __forceinline__ void combine_row(int ns, Lse lse, OPart opart, uint16_t* orow, float* lse_out, int lane,
                                             float sink = -INFINITY) {
+  auto store = [&](const float* acc, float LSE) {  // bf16 O (nearest even) and the row's LSE
+    u32x4 packed;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      packed[i] = (unsigned)f32_to_bf16_rne(acc[2 * i]) | ((unsigned)f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+    *reinterpret_cast<u32x4*>(orow + 8 * lane) = packed;
+    if (lse_out && lane == 0) *lse_out = LSE;
+  };
+  constexpr int kPre = 8;
+  f32x4 pa[kPre], pb[kPre];
+  if (ns <= kPre) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u)
+      if (u < ns) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(opart(u) + 8 * lane);
+        pa[u] = src[0];
+        pb[u] = src[1];
+      }
+  }
   const float l0 = lane < ns ? lse(lane) : -INFINITY;  // the first 64 splits' lse, read once
+  if (ns <= kPre) {
+    float M = fmaxf(wave_max(l0), sink);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float LSE = -INFINITY;
+    if (M != -INFINITY) {
+      const float den = wave_sum(expf(l0 - M)) + (sink != -INFINITY ? expf(sink - M) : 0.f);
+      LSE = M + logf(den);
+      const float wl = expf(l0 - LSE);
+#pragma unroll
+      for (int u = 0; u < kPre; ++u) {
+        if (u < ns) {
+          const float wgt = __shfl(wl, u);
+          const bool on = wgt != 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[e] += on ? wgt * pa[u][e] : 0.f;
+            acc[4 + e] += on ? wgt * pb[u][e] : 0.f;
+          }
+        }
+      }
+    }
+    store(acc, LSE);
+    return;
+  }
   float M = l0;
   for (int j = lane + 64; j < ns; j += 64) M = fmaxf(M, lse(j));
   M = fmaxf(wave_max(M), sink);
@@ -2068,12 +2113,7 @@ __device__ __forceinline__ void combine_row(int ns, Lse lse, OPart opart, uint16
       }
     }
   }
-  u32x4 packed;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    packed[i] = (unsigned)f32_to_bf16_rne(acc[2 * i]) | ((unsigned)f32_to_bf16_rne(acc[2 * i + 1]) << 16);
-  *reinterpret_cast<u32x4*>(orow + 8 * lane) = packed;
-  if (lse_out && lane == 0) *lse_out = LSE;
+  store(acc, LSE);
 }
 
 // generic: o_part [rows, ns, 512], lse_part [rows, ns]
