@@ -241,8 +241,8 @@ int mla_paged_decode_noalloc(const uint16_t* q, const uint16_t* qpe, const void*
                              int num_splits, uint16_t* o, float* lse, void* stream);
 
 /* Paged split planner in the pages' own split form (TileGym page,
- * _mla_decoding_split_kv.forward, with the batch's longest sequence as S_kv; SURVEY's
- * host-planner signature): from a host copy of seq_lens,
+ * _mla_decoding_split_kv.forward, with the batch's longest sequence as S_kv): from a host
+ * copy of seq_lens,
  *   max_len = max(1, max_b seq_lens_host[b]);  estimate = max(1, num_cus / B);
  *   kv_len_per_split = max(next_power_of_2(max_len / estimate), 128);
  *   max_splits = ceil(max_len / kv_len_per_split).
