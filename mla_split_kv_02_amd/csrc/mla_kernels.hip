@@ -1819,6 +1819,142 @@ __device__ __forceinline__ void run_range_fp8(const DecodeParams& p, uint32_t sm
   __syncthreads();  // the next range reuses the LDS buffers
 }
 
+// A contiguous split of at most four tiles with at most 32 rows (few heads): the four
+// wavefronts take one tile each instead of walking the tiles in turn, each with the
+// whole 32-row block and all 512 dims (scores, softmax and output product as in
+// run_range), so the split costs one tile of latency instead of four.  The four partial
+// results (the row's reference max m_w, its sums of p and of bf16(p), and O_w) are then
+// merged through the LDS: with M = max m_w each counts 2^(m_w - M) times, O_j = sum of the
+// weighted O_w over the weighted sum of bf16(p), lse_j = (M + log2 of the weighted sum of
+// p) ln 2.  The exchange takes one round of all 512 dims for at most 16 rows, else two
+// rounds of 256; a row of it is padded by 16 bytes so that the 16-byte accesses of
+// neighbouring rows fall in different banks.
+__device__ __forceinline__ void run_split_tiles_parallel(const DecodeParams& p, uint32_t smem, int b, int lt0,
+                                                         int lt1, int64_t slot) {
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
+  const int rows = p.rows;  // at most 32: one block, shared by the four wavefronts
+  const int rc = min(lr, rows - 1);
+  const float c = fmaxf(p.score_scale, 1e-30f);
+  const int nt = lt1 - lt0;  // 1 .. 4
+
+  bf16x8 q[kKSteps];
+  {
+    const uint16_t* qrow = p.q + ((int64_t)b * rows + rc) * kLatent;
+    const uint16_t* prow = p.qpe + ((int64_t)b * rows + rc) * kRope;
+#pragma unroll
+    for (int k = 0; k < kKSteps; ++k) {
+      const int d = 16 * k + 8 * lh;
+      const uint16_t* src = (d < kLatent) ? qrow + d : prow + (d - kLatent);
+      q[k] = *reinterpret_cast<const bf16x8*>(src);
+    }
+  }
+  int ab[4];
+  {
+    const int a_base = 128 * lr + ((lh ^ swz(lr)) << 4);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) ab[x] = a_base ^ (32 * x);
+  }
+  int vb[4];
+  {
+    const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int tok = 8 * (g >> 1) + 4 * e + (j >> 2);
+      const int dim = 16 * (g & 1) + 4 * (j & 3);
+      const int v_off = tile_off(tok, dim >> 3) + 2 * (dim & 7);
+      vb[2 * e] = v_off;
+      vb[2 * e + 1] = v_off ^ 64;
+    }
+  }
+
+  // every tile's loads at once (the usual split of load instructions over wavefronts)
+  const Src src{&p, b, p.S};
+  auto tile_buf = [&](int i) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)(smem + (uint32_t)(i * kTileBytes))); };
+  for (int i = 0; i < nt; ++i) load_bf16_tile<false>(src, (lt0 + i) * kTileTokens, nullptr, tile_buf(i), wave, lane);
+  wait_vmcnt(0);
+  __syncthreads();
+
+  f32x16 o[kDimBlocks];
+#pragma unroll
+  for (int db = 0; db < kDimBlocks; ++db) o[db] = f32x16{};
+  Softmax S{-INFINITY, 0.f, 0.f};
+  if (wave < nt) {
+    const uint32_t tile = tile_buf(wave);
+    const f32x16 s = qk_tile(q, tile, ab);
+    float x[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) x[v] = s[v];
+    const int tbase = (lt0 + wave) * kTileTokens;
+    if (tbase + kTileTokens > p.S) {  // the sequence's last tile: tokens from S on are masked
+      const int lim = p.S - tbase - 4 * lh;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) x[v] = (8 * (v >> 2) + (v & 3) < lim) ? x[v] : -INFINITY;
+    }
+    unsigned pp[8];
+    softmax_tile(S, x, c, pp);
+    pv_tile<kDimBlocks>(o, tile, pp, vb, 0);
+  }
+  const float lsum = pair_sum(S.l_sum), lrnd = pair_sum(S.l_rnd);
+  __syncthreads();  // every tile has been read: the buffers take the exchange
+
+  const int R = rows <= 16 ? 1 : 2;                 // rounds
+  const int DR = kLatent / R;                       // dims per round
+  const int RS = DR + 4;                            // exchange row stride (floats)
+  const int XR = R == 1 ? 16 : 32;                  // rows kept per wavefront
+  LDS_AS float* xl = at<float>(smem);              // [4][XR][RS]
+  LDS_AS float* st = at<float>(smem + 136 * 1024);  // [4][32][3]: m, sum p, sum bf16(p)
+  if (lh == 0) {
+    st[(wave * 32 + lr) * 3 + 0] = S.m_used;
+    st[(wave * 32 + lr) * 3 + 1] = lsum;
+    st[(wave * 32 + lr) * 3 + 2] = lrnd;
+  }
+  const int CPW = DR / 16;        // 4-dim chunks per wavefront and row in the merge
+  const int RSTEP = 64 / CPW;     // rows a wavefront's lanes cover at once
+  const int cc = lane % CPW, r0 = lane / CPW;
+  for (int r = 0; r < R; ++r) {
+    if (lr < rows && lr < XR) {
+#pragma unroll
+      for (int db = 0; db < kDimBlocks; ++db) {
+        if (db / (kDimBlocks / R) != r) continue;
+        const int dl = 32 * (db % (kDimBlocks / R)) + 4 * lh;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<LDS_AS f32x4*>(xl + (wave * XR + lr) * RS + dl + 8 * q4) =
+              f32x4{o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]};
+      }
+    }
+    __syncthreads();
+    for (int row = r0; row < rows; row += RSTEP) {
+      float m[4], a[4];
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        m[w] = st[(w * 32 + row) * 3];
+        M = fmaxf(M, m[w]);
+      }
+      float l_tot = 0.f, l_rnd = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        a[w] = m[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[w] - M);
+        l_tot += a[w] * st[(w * 32 + row) * 3 + 1];
+        l_rnd += a[w] * st[(w * 32 + row) * 3 + 2];
+      }
+      const bool ok = l_tot > 0.f;
+      const float f = ok ? p.v_scale / l_rnd : 0.f;
+      const int dloc = (DR / 4) * wave + 4 * cc;  // this lane's 4 dims within the round
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc += a[w] * *reinterpret_cast<LDS_AS f32x4*>(xl + (w * XR + row) * RS + dloc);
+      *reinterpret_cast<f32x4*>(p.o_part + slot * p.o_slot + (int64_t)row * p.o_row + r * DR + dloc) = acc * f;
+      if (r == 0 && wave == 0 && cc == 0)
+        p.lse_part[slot * p.l_slot + (int64_t)row * p.l_row] = ok ? (M + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    __syncthreads();  // the next round rewrites the exchange
+  }
+}
+
 // ------------------------------------------------------------------------------------
 // decode kernels
 // ------------------------------------------------------------------------------------
@@ -1840,8 +1976,15 @@ void decode_contig_kernel(const DecodeParams p) {
   const int t0 = j * p.kv_len_per_split;
   const int t1 = min(t0 + p.kv_len_per_split, p.S);
   // slot b*H*NS + j with row = head addresses o_part [B, H, NS, 512]
-  run_range<kFmtBf16, false, D>(p, lds_addr((lds_ptr)smem), b, p.S, rg, t0 / kTileTokens,
-                                (t1 + kTileTokens - 1) / kTileTokens, (int64_t)b * p.rows * p.num_splits + j);
+  const int lt0 = t0 / kTileTokens, lt1 = (t1 + kTileTokens - 1) / kTileTokens;
+  const int64_t slot = (int64_t)b * p.rows * p.num_splits + j;
+  if constexpr (D == 4) {
+    if (lt1 - lt0 <= kWaves) {  // few heads and a short split: one tile per wavefront
+      run_split_tiles_parallel(p, lds_addr((lds_ptr)smem), b, lt0, lt1, slot);
+      return;
+    }
+  }
+  run_range<kFmtBf16, false, D>(p, lds_addr((lds_ptr)smem), b, p.S, rg, lt0, lt1, slot);
 }
 
 // Paged: the batch's tiles (request b has ceil(n_b / 32)) are cut into num_splits

@@ -29,8 +29,10 @@ def _contig_run(c, L):
 
 
 @pytest.mark.parametrize("B,H,S,L", [
-    (1, 16, 256, 128),     # tiny contiguous workload: 2 splits
-    (2, 32, 300, 128),     # ragged last split (44 tokens, partial tile)
+    (1, 16, 256, 128),     # tiny contiguous workload: 2 splits (one tile per wavefront, one merge round)
+    (2, 32, 300, 128),     # ragged last split (44 tokens, partial tile; two merge rounds, two idle wavefronts)
+    (3, 16, 33, 128),      # one full tile and one token: two wavefronts idle
+    (2, 16, 4096, 256),    # few heads, 8 tiles per split: the tile loop with shared dims
     (1, 48, 200, 128),     # rows not a multiple of 32: one wave half idle, two waves idle
     (2, 128, 1000, 256),   # full head group, 4 splits, ragged
     (3, 64, 129, 128),     # one token in the last split
