@@ -2271,6 +2271,95 @@ __global__ __launch_bounds__(256) void combine_generic_kernel(const CombineParam
   combine_row(p.num_splits, lse, opart, p.o + row * kLatent, p.lse ? p.lse + row : nullptr, lane);
 }
 
+// generic, more than 8 partials per row: one workgroup per row.  Wavefront w merges the
+// partials j = w, w + 4, .. on its own (O_j loads issued with the lse loads, up to 8 per
+// round trip) relative to its own maximum M_w; the four results (M_w, D_w = sum of
+// exp(lse_j - M_w), A_w = sum of exp(lse_j - M_w) O_j) are then merged through the LDS:
+// with M = max M_w, O = sum of exp(M_w - M) A_w / D and LSE = M + log D, D = sum of
+// exp(M_w - M) D_w.  A row with a few dozen partials takes two round trips instead of
+// one per four partials.
+__global__ __launch_bounds__(256) void combine_generic_wide_kernel(const CombineParams p) {
+  __shared__ float xm[4], xd[4];
+  __shared__ f32x4 xa[4][2][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t row = blockIdx.x;
+  const int ns = p.num_splits;
+  const float* lses = p.lse_part + row * ns;
+  const float* base = p.o_part + row * ns * kLatent;
+  constexpr int kB = 8;
+  float Mw = -INFINITY, Dw = 0.f;
+  f32x4 aw = {0.f, 0.f, 0.f, 0.f}, bw = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = w; j0 < ns; j0 += 4 * kB) {  // this wavefront's partials j0, j0 + 4, .. (up to kB)
+    f32x4 a[kB], b[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int j = j0 + 4 * u;
+      if (j < ns) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(base + (int64_t)j * kLatent + 8 * lane);
+        a[u] = src[0];
+        b[u] = src[1];
+      }
+    }
+    const float l = (lane < kB && j0 + 4 * lane < ns) ? lses[j0 + 4 * lane] : -INFINITY;
+    const float Mn = fmaxf(Mw, wave_max(l));
+    if (Mn == -INFINITY) continue;  // nothing seen yet (uniform)
+    const float r = Mw == -INFINITY ? 0.f : expf(Mw - Mn);  // rescale what came before
+    const float e = expf(l - Mn);
+    Dw = Dw * r + wave_sum(e);
+    aw *= r;
+    bw *= r;
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      if (j0 + 4 * u < ns) {
+        const float wgt = __shfl(e, u);
+        if (wgt != 0.f) {  // a weight-0 partial adds nothing, whatever its O_j holds
+          aw += wgt * a[u];
+          bw += wgt * b[u];
+        }
+      }
+    }
+    Mw = Mn;
+  }
+  if (lane == 0) {
+    xm[w] = Mw;
+    xd[w] = Dw;
+  }
+  xa[w][0][lane] = aw;
+  xa[w][1][lane] = bw;
+  __syncthreads();
+  if (w != 0) return;
+  float M = fmaxf(fmaxf(xm[0], xm[1]), fmaxf(xm[2], xm[3]));
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float LSE = -INFINITY;
+  if (M != -INFINITY) {
+    float D = 0.f, s[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      s[v] = xm[v] == -INFINITY ? 0.f : expf(xm[v] - M);
+      D += s[v] * xd[v];
+    }
+    LSE = M + logf(D);
+    const float inv = 1.f / D;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const f32x4 ta = xa[v][0][lane], tb = xa[v][1][lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += s[v] * ta[e];
+        acc[4 + e] += s[v] * tb[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= inv;
+  }
+  u32x4 packed;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    packed[i] = (unsigned)f32_to_bf16_rne(acc[2 * i]) | ((unsigned)f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+  *reinterpret_cast<u32x4*>(p.o + row * kLatent + 8 * lane) = packed;
+  if (p.lse && lane == 0) p.lse[row] = LSE;
+}
+
 // paged: row (b, r) merges slots w + b for the non-empty ranges w in
 // [seg_first[b], seg_last[b]]; o_part [slots, rows, 512], lse_part [slots, rows]
 __global__ __launch_bounds__(256) void combine_paged_kernel(const CombineParams p) {
@@ -2355,7 +2444,10 @@ hipError_t launch_decode_paged_splits(int fmt, const DecodeParams& p, hipStream_
 }
 
 hipError_t launch_combine_generic(const CombineParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_generic_kernel, dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, stream, p);
+  if (p.num_splits > 8)
+    hipLaunchKernelGGL(combine_generic_wide_kernel, dim3((unsigned)p.rows), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(combine_generic_kernel, dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -105,9 +105,11 @@ def test_contig_run_to_run_bitwise_stable():
         assert np.array_equal(x, y)
 
 
-@pytest.mark.parametrize("R,NS", [(37, 9), (11, 150)])
+@pytest.mark.parametrize("R,NS", [(37, 9), (11, 150), (13, 8), (10, 33)])
 def test_combine_matches_oracle_with_empty_splits(R, NS):
-    """NS = 150 takes three rounds of 64 splits per row, the last one ragged."""
+    """Up to 8 partials a row takes one wavefront with every load issued at once; more take
+    a workgroup per row, whose four wavefronts merge every fourth partial in batches of 8
+    (NS = 150: five batches each, the last ragged) and then merge their results."""
     say(f"combine generic R={R} NS={NS}")
     rng = np.random.default_rng(4 + NS)
     op = rng.standard_normal((R, NS, 512)).astype(np.float32)
