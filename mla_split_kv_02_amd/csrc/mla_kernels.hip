@@ -2029,12 +2029,14 @@ void decode_paged_kernel(const DecodeParams p) {
     return n > 0 ? (n + TT - 1) / TT - first_tile(n) : 0;
   };
 
-  // workgroup id -> (range w, row group rg); the row groups of one range sit 8 ids
-  // apart so that they land on the same XCD (ids are dealt round-robin over 8 XCDs)
+  // workgroup id -> (range w, row group rg).  Ids are dealt round-robin over the 8 XCDs;
+  // XCD x takes the consecutive ranges x * per_xcd .. x * per_xcd + per_xcd - 1 with all
+  // their row groups, so the neighbouring ranges of one request (and its query) share
+  // that XCD's L2.  The grid holds 8 * per_xcd * row_groups ids.
   const int id = blockIdx.x;
-  const int per_blk = 8 * p.row_groups;
-  const int rg = (id % per_blk) / 8;
-  const int w = (id / per_blk) * 8 + (id % 8);
+  const int per_xcd = (p.num_splits + 7) / 8, k = id / 8;
+  const int rg = k % p.row_groups;
+  const int w = (id % 8) * per_xcd + k / p.row_groups;
   if (w >= p.num_splits) return;
 
   // tile counts and costs: thread t sums requests [s0, s1); exclusive scans give each
