@@ -2128,8 +2128,10 @@ void decode_paged_kernel(const DecodeParams p) {
   }
 }
 
-// Paged, fixed-length splits (the pages' own split form): grid (row groups, max_splits,
-// B); split j of request b covers tokens [j L, min((j + 1) L, n_b)), L = kv_len_per_split
+// Paged, fixed-length splits (the pages' own split form): U = row_groups * max_splits * B
+// work items (row group, split j, request b), dealt to the XCDs in consecutive blocks as
+// in the contiguous kernel (a request's splits share one L2); split j of request b
+// covers tokens [j L, min((j + 1) L, n_b)), L = kv_len_per_split
 // (a power of two >= 128, so a whole number of tiles of either size), and writes slot
 // b * rows * NS + j of o_part [B, rows, NS, 512] / lse_part [B, rows, NS].  A split past
 // the request's end writes lse = -inf for its rows and leaves its O_j, which the combine
@@ -2140,7 +2142,11 @@ void decode_paged_splits_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<FMT>()];
   constexpr bool kFp8Fmt = FMT == kFmtFp8 || FMT == kFmtFp8Q;
   constexpr int TT = kFp8Fmt ? kT8 : kTileTokens;
-  const int rg = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int64_t U = (int64_t)p.row_groups * p.num_splits * p.B, per = (U + 7) / 8;
+  const int64_t u = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (u >= U) return;
+  const int rg = (int)(u % p.row_groups), j = (int)((u / p.row_groups) % p.num_splits);
+  const int b = (int)(u / ((int64_t)p.row_groups * p.num_splits));
   const int n = min(max(p.seq_lens[b], 0), p.max_blocks * p.page_size);
   const int t0 = j * p.kv_len_per_split, t1 = min(t0 + p.kv_len_per_split, n);
   const int64_t slot = (int64_t)b * p.rows * p.num_splits + j;
@@ -2427,7 +2433,8 @@ hipError_t launch_decode_paged(int fmt, const DecodeParams& p, hipStream_t strea
 }
 
 hipError_t launch_decode_paged_splits(int fmt, const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid(p.row_groups, p.num_splits, p.B);
+  const int64_t U = (int64_t)p.row_groups * p.num_splits * p.B;
+  const dim3 grid((unsigned)(((U + 7) / 8) * 8));
   switch (fmt) {
     case kFmtBf16:
       hipLaunchKernelGGL(decode_paged_splits_kernel<kFmtBf16>, grid, dim3(kThreads), 0, stream, p);
