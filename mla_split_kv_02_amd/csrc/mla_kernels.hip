@@ -1987,8 +1987,9 @@ void decode_contig_kernel(const DecodeParams p) {
   run_range<kFmtBf16, false, D>(p, lds_addr((lds_ptr)smem), b, p.S, rg, lt0, lt1, slot);
 }
 
-// Paged: the batch's tiles (request b has ceil(n_b / 32)) are cut into num_splits
-// contiguous ranges of about equal cost, range w -> workgroup w (x row_groups).  A
+// Paged: the batch's tiles (request b has ceil(n_b / T), T = 32, or 64 for the FP8
+// formats) are cut into num_splits contiguous ranges of about equal cost, one workgroup
+// per range and row group (in the XCD-aware order below).  A
 // request with tiles costs them plus kSegmentCost: on the cost axis it spans its
 // overhead part, then its tiles, and range w takes the tiles that fall in
 // [w W / NS, (w + 1) W / NS) of the total cost W.  A range covering parts of several
@@ -1998,10 +1999,11 @@ void decode_contig_kernel(const DecodeParams p) {
 //
 // kSegmentCost is what a segment's fixed work costs in 32-token tiles, kSegmentCostT8 the
 // same for the FP8 formats in their 64-token tiles: the query load and split, the
-// pipeline fill and drain, and the partial store.  Measured per workgroup (end time
-// against tokens and segments over the 256 ranges of the B=64, H=128 FP8 workload):
-// about 24 us per segment against about 2.8 us per 64-token tile, i.e. 8 tiles; the
-// 32-token figure (17 us against 1.6 us per tile) is from the bf16-dequantising loop.
+// pipeline fill and drain, and the partial store.  Measured per workgroup (cycles or end
+// time against tiles and segments over the 256 ranges of the B=64, H=128 FP8 workload):
+// about 50700 cycles (24-26 us) per segment against about 6550 cycles per 64-token tile,
+// i.e. 8 tiles; the 32-token figure (17 us against 1.6 us per tile) is from the
+// bf16-dequantising loop.
 // An empty range can only sit where one request ends and the next begins, so every
 // range between seg_first[b] and seg_last[b] holds tiles of b exactly when its cost
 // interval is not empty (the combine relies on this).
