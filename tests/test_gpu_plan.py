@@ -116,3 +116,25 @@ def test_partials_headline_full_size():
                                  w.block_tables, w.seq_lens, w.sm_scale, requests=pick)
     check_o("combine O", o[pick], ro, TOL_O_QUANT)
     check("combine LSE", lse[pick], rl, TOL_LSE)
+
+
+@pytest.mark.parametrize("B,fmt", [(1000, gen.FMT_BF16), (4096, gen.FMT_FP8)])
+def test_partials_plan_many_requests(B, fmt):
+    """Batches larger than the workgroup (each thread of the device prefix scan sums 4 or
+    16 requests), short and empty requests, many segments per range (the largest batch the
+    library takes): descriptors bit-exact against the mirror, sampled slots and sampled
+    requests' outputs against the oracle."""
+    rng = np.random.default_rng(500 + B)
+    lens = rng.integers(0, 60, size=B)
+    lens[rng.random(B) < 0.1] = 0
+    lens[0] = 1
+    say(f"partials plan B={B} fmt={fmt}, {int((lens > 0).sum())} non-empty requests")
+    w = gen.make_paged(B=B, H=16, q_len=1, lo=0, hi=60, page_size=32, fmt=fmt, seed=600 + B,
+                       seq_lens=lens.tolist(), max_blocks=2, poison_tail=True)
+    ns = mla.plan_paged(256, w.B, w.q_len, w.H)
+    o, lse = _check_plan_and_slots(w, ns, max_slots=64, seed=B)
+    pick = sorted(set(rng.choice(B, 64, replace=False).tolist()) | {0, B - 1})
+    ro, rl = oracle.paged_decode(*w.q_f64(), w.cache, w.fmt, w.kv_scale, w.page_size, w.page_stride,
+                                 w.block_tables, w.seq_lens, w.sm_scale, requests=pick)
+    check_o(f"O ({len(pick)} requests)", o[pick], ro, TOL_O_BF16 if fmt == gen.FMT_BF16 else TOL_O_QUANT)
+    check(f"LSE ({len(pick)} requests)", lse[pick], rl, TOL_LSE)
