@@ -513,3 +513,26 @@ def test_paged_nvfp4_b128_h128_q2_full_size_sampled():
     ro, rl = _paged_ref(w, requests=pick)
     check_o(f"O ({len(pick)} requests)", o[pick], ro, TOL_O_QUANT)
     check(f"LSE ({len(pick)} requests)", lse[pick], rl, TOL_LSE)
+
+
+@pytest.mark.parametrize("fmt", [gen.FMT_BF16, gen.FMT_FP8])
+def test_paged_batch_with_no_tokens(fmt):
+    """Every request empty (the decode finds no tiles at all and stops after its plan): O
+    is zero and LSE -inf for every row, through all three paged entry points, with sinks
+    the LSE is the sink."""
+    say(f"paged all-empty batch fmt={fmt}")
+    w = gen.make_paged(B=3, H=16, q_len=2, lo=0, hi=0, page_size=64, fmt=fmt, seed=70, seq_lens=[0, 0, 0],
+                       max_blocks=2)
+    d = paged_device_inputs(w)
+    o, lse = mla.paged_decode(d["q"], d["qpe"], d["cache"], w.fmt, d["bt"], d["sl"], w.page_size, w.page_stride,
+                              w.kv_scale, w.sm_scale)
+    o2, lse2, _, _ = mla.paged_decode_splits(d["q"], d["qpe"], d["cache"], w.fmt, d["bt"], d["sl"], w.page_size,
+                                             w.page_stride, w.kv_scale, w.sm_scale)
+    sinks = torch.linspace(-1.0, 1.0, w.H, device=DEV)
+    o3, lse3 = mla.paged_decode(d["q"], d["qpe"], d["cache"], w.fmt, d["bt"], d["sl"], w.page_size, w.page_stride,
+                                w.kv_scale, w.sm_scale, sinks=sinks)
+    torch.cuda.synchronize()
+    for oo, ll in ((o, lse), (o2, lse2)):
+        assert (host(oo) == 0).all() and np.isneginf(host(ll)).all()
+    assert (host(o3) == 0).all()
+    assert np.array_equal(host(lse3), np.broadcast_to(host(sinks), (3, 2, w.H)))
