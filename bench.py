@@ -399,7 +399,7 @@ def main():
     ap.add_argument("--workload", default="paged_fp8_b64_h128_s1k_32k")
     ap.add_argument("--num-splits", type=int, default=None)
     ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto",
-                    help="write 1 GiB between timed steps (auto: when the cache would fit twice in the MALL)")
+                    help="read 1 GiB between timed steps (auto: when the cache would fit twice in the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -411,7 +411,9 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this decode path is built and measured on a single MI355X "
-              f"(--gpus {args.gpus} was asked for); see the design notes for how it would shard.", file=sys.stderr)
+              f"(--gpus {args.gpus} was asked for); a multi-GPU decode would split the requests' token "
+              f"ranges across GPUs and merge their partials with the same LSE combine, which is not built.",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
