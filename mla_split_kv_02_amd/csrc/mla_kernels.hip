@@ -2281,36 +2281,35 @@ __global__ __launch_bounds__(256) void combine_generic_kernel(const CombineParam
   combine_row(p.num_splits, lse, opart, p.o + row * kLatent, p.lse ? p.lse + row : nullptr, lane);
 }
 
-// generic, more than 8 partials per row: one workgroup per row.  Wavefront w merges the
-// partials j = w, w + 4, .. on its own (O_j loads issued with the lse loads, up to 8 per
-// round trip) relative to its own maximum M_w; the four results (M_w, D_w = sum of
-// exp(lse_j - M_w), A_w = sum of exp(lse_j - M_w) O_j) are then merged through the LDS:
-// with M = max M_w, O = sum of exp(M_w - M) A_w / D and LSE = M + log D, D = sum of
-// exp(M_w - M) D_w.  A row with a few dozen partials takes two round trips instead of
-// one per four partials.
-__global__ __launch_bounds__(256) void combine_generic_wide_kernel(const CombineParams p) {
-  __shared__ float xm[4], xd[4];
-  __shared__ f32x4 xa[4][2][64];
+// Many partials of one row (more than 8): one workgroup of kCW wavefronts per row.
+// Wavefront w merges the partials j = w, w + kCW, .. on its own (O_j loads issued with the
+// lse loads, up to 8 per round trip) relative to its own maximum M_w; the kCW results
+// (M_w, D_w = sum of exp(lse_j - M_w), A_w = sum of exp(lse_j - M_w) O_j) are then merged
+// through the LDS: with M = max M_w, O = sum of exp(M_w - M) A_w / D and LSE = M + log D,
+// D = sum of exp(M_w - M) D_w (+ exp(sink - M)).  A row with hundreds of partials takes
+// a few round trips instead of one per four partials.
+constexpr int kCW = 8;  // wavefronts per row
+template <class Lse, class OPart>
+__device__ __forceinline__ void combine_row_wide(int ns, Lse lse, OPart opart, uint16_t* orow, float* lse_out,
+                                                 float sink = -INFINITY) {
+  __shared__ float xm[kCW], xd[kCW];
+  __shared__ f32x4 xa[kCW][2][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t row = blockIdx.x;
-  const int ns = p.num_splits;
-  const float* lses = p.lse_part + row * ns;
-  const float* base = p.o_part + row * ns * kLatent;
   constexpr int kB = 8;
   float Mw = -INFINITY, Dw = 0.f;
   f32x4 aw = {0.f, 0.f, 0.f, 0.f}, bw = {0.f, 0.f, 0.f, 0.f};
-  for (int j0 = w; j0 < ns; j0 += 4 * kB) {  // this wavefront's partials j0, j0 + 4, .. (up to kB)
+  for (int j0 = w; j0 < ns; j0 += kCW * kB) {  // this wavefront's partials j0, j0 + kCW, .. (up to kB)
     f32x4 a[kB], b[kB];
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
-      const int j = j0 + 4 * u;
+      const int j = j0 + kCW * u;
       if (j < ns) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(base + (int64_t)j * kLatent + 8 * lane);
+        const f32x4* src = reinterpret_cast<const f32x4*>(opart(j) + 8 * lane);
         a[u] = src[0];
         b[u] = src[1];
       }
     }
-    const float l = (lane < kB && j0 + 4 * lane < ns) ? lses[j0 + 4 * lane] : -INFINITY;
+    const float l = (lane < kB && j0 + kCW * lane < ns) ? lse(j0 + kCW * lane) : -INFINITY;
     const float Mn = fmaxf(Mw, wave_max(l));
     if (Mn == -INFINITY) continue;  // nothing seen yet (uniform)
     const float r = Mw == -INFINITY ? 0.f : expf(Mw - Mn);  // rescale what came before
@@ -2320,7 +2319,7 @@ __global__ __launch_bounds__(256) void combine_generic_wide_kernel(const Combine
     bw *= r;
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
-      if (j0 + 4 * u < ns) {
+      if (j0 + kCW * u < ns) {
         const float wgt = __shfl(e, u);
         if (wgt != 0.f) {  // a weight-0 partial adds nothing, whatever its O_j holds
           aw += wgt * a[u];
@@ -2338,20 +2337,22 @@ __global__ __launch_bounds__(256) void combine_generic_wide_kernel(const Combine
   xa[w][1][lane] = bw;
   __syncthreads();
   if (w != 0) return;
-  float M = fmaxf(fmaxf(xm[0], xm[1]), fmaxf(xm[2], xm[3]));
+  float M = sink;
+#pragma unroll
+  for (int v = 0; v < kCW; ++v) M = fmaxf(M, xm[v]);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float LSE = -INFINITY;
   if (M != -INFINITY) {
-    float D = 0.f, s[4];
+    float D = sink != -INFINITY ? expf(sink - M) : 0.f, s[kCW];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < kCW; ++v) {
       s[v] = xm[v] == -INFINITY ? 0.f : expf(xm[v] - M);
       D += s[v] * xd[v];
     }
     LSE = M + logf(D);
     const float inv = 1.f / D;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < kCW; ++v) {
       const f32x4 ta = xa[v][0][lane], tb = xa[v][1][lane];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -2366,35 +2367,71 @@ __global__ __launch_bounds__(256) void combine_generic_wide_kernel(const Combine
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     packed[i] = (unsigned)f32_to_bf16_rne(acc[2 * i]) | ((unsigned)f32_to_bf16_rne(acc[2 * i + 1]) << 16);
-  *reinterpret_cast<u32x4*>(p.o + row * kLatent + 8 * lane) = packed;
-  if (p.lse && lane == 0) p.lse[row] = LSE;
+  *reinterpret_cast<u32x4*>(orow + 8 * lane) = packed;
+  if (lse_out && lane == 0) *lse_out = LSE;
+}
+
+// generic, more than 8 partials per row: one workgroup per row
+__global__ __launch_bounds__(64 * kCW) void combine_generic_wide_kernel(const CombineParams p) {
+  const int64_t row = blockIdx.x;
+  const int ns = p.num_splits;
+  const float* lses = p.lse_part + row * ns;
+  const float* base = p.o_part + row * ns * kLatent;
+  combine_row_wide(ns, [&](int j) { return lses[j]; }, [&](int j) { return base + (int64_t)j * kLatent; },
+                   p.o + row * kLatent, p.lse ? p.lse + row : nullptr);
 }
 
 // paged: row (b, r) merges slots w + b for the non-empty ranges w in
 // [seg_first[b], seg_last[b]]; o_part [slots, rows, 512], lse_part [slots, rows]
+// The partials of paged row grow (request b, row r): the ranges w0 .. w1 that touch b.
+struct PagedRow {
+  const CombineParams* p;
+  int b, r, w0, w1, W;
+  __device__ PagedRow(const CombineParams& c, int64_t grow) : p(&c) {
+    b = (int)(grow / c.rows);
+    r = (int)(grow % c.rows);
+    const int n = min(max(c.seq_lens[b], 0), c.max_len);
+    W = c.info[0];  // total cost of the batch's ranges (see decode_paged_kernel)
+    const int G = c.num_splits;
+    w0 = 0;
+    w1 = -1;
+    if (n > 0) {  // descriptors written by the decode launch; clamped so they never address outside
+      w0 = min(max(c.seg_first[b], 0), G - 1);
+      w1 = min(max(c.seg_last[b], w0), G - 1);
+    }
+  }
+  // a dead range (no tiles) wrote nothing: its lse counts as -inf (its slot is still
+  // inside the workspace, so the unused load of its O_j stays in bounds)
+  __device__ bool live(int wj) const {
+    const int G = p->num_splits;
+    return ((int64_t)wj * W) / G < ((int64_t)(wj + 1) * W) / G;  // range wj holds tiles
+  }
+  __device__ float lse(int j) const {
+    const int wj = w0 + j;
+    return live(wj) ? p->lse_part[((int64_t)wj + b) * p->rows + r] : -INFINITY;
+  }
+  __device__ const float* opart(int j) const { return p->o_part + (((int64_t)w0 + j + b) * p->rows + r) * kLatent; }
+  __device__ float sink() const { return p->sinks ? p->sinks[r % p->H] : -INFINITY; }
+};
+
+// paged: row (b, r) merges slots w + b for the non-empty ranges w in
+// [seg_first[b], seg_last[b]]; o_part [slots, rows, 512], lse_part [slots, rows].  One
+// wavefront per row.
 __global__ __launch_bounds__(256) void combine_paged_kernel(const CombineParams p) {
   const int lane = threadIdx.x & 63;
   const int64_t grow = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (grow >= (int64_t)p.B * p.rows) return;
-  const int b = (int)(grow / p.rows), r = (int)(grow % p.rows);
-  const int n = min(max(p.seq_lens[b], 0), p.max_len);
-  const int W = p.info[0];  // total cost of the batch's ranges (see decode_paged_kernel)
-  const int G = p.num_splits;
-  int w0 = 0, w1 = -1;
-  if (n > 0) {  // descriptors written by the decode launch; clamped so they never address outside
-    w0 = min(max(p.seg_first[b], 0), G - 1);
-    w1 = min(max(p.seg_last[b], w0), G - 1);
-  }
-  // a dead range (no tiles) wrote nothing: its lse counts as -inf (its slot is still
-  // inside the workspace, so the unused load of its O_j stays in bounds)
-  auto live = [&](int wj) { return ((int64_t)wj * W) / G < ((int64_t)(wj + 1) * W) / G; };  // range wj holds tiles
-  auto lse = [&](int j) {
-    const int wj = w0 + j;
-    return live(wj) ? p.lse_part[((int64_t)wj + b) * p.rows + r] : -INFINITY;
-  };
-  auto opart = [&](int j) { return p.o_part + (((int64_t)w0 + j + b) * p.rows + r) * kLatent; };
-  const float sink = p.sinks ? p.sinks[r % p.H] : -INFINITY;
-  combine_row(w1 - w0 + 1, lse, opart, p.o + grow * kLatent, p.lse ? p.lse + grow : nullptr, lane, sink);
+  const PagedRow R(p, grow);
+  combine_row(R.w1 - R.w0 + 1, [&](int j) { return R.lse(j); }, [&](int j) { return R.opart(j); },
+              p.o + grow * kLatent, p.lse ? p.lse + grow : nullptr, lane, R.sink());
+}
+
+// paged, with requests spread over many ranges: one workgroup per row (combine_row_wide)
+__global__ __launch_bounds__(64 * kCW) void combine_paged_wide_kernel(const CombineParams p) {
+  const int64_t grow = blockIdx.x;
+  const PagedRow R(p, grow);
+  combine_row_wide(R.w1 - R.w0 + 1, [&](int j) { return R.lse(j); }, [&](int j) { return R.opart(j); },
+                   p.o + grow * kLatent, p.lse ? p.lse + grow : nullptr, R.sink());
 }
 
 // ------------------------------------------------------------------------------------
@@ -2456,15 +2493,20 @@ hipError_t launch_decode_paged_splits(int fmt, const DecodeParams& p, hipStream_
 
 hipError_t launch_combine_generic(const CombineParams& p, hipStream_t stream) {
   if (p.num_splits > 8)
-    hipLaunchKernelGGL(combine_generic_wide_kernel, dim3((unsigned)p.rows), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(combine_generic_wide_kernel, dim3((unsigned)p.rows), dim3(64 * kCW), 0, stream, p);
   else
     hipLaunchKernelGGL(combine_generic_kernel, dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
+// A request spans about num_splits / B ranges; beyond 16 on average its rows take a
+// workgroup each.
 hipError_t launch_combine_paged(const CombineParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.B * p.rows;
-  hipLaunchKernelGGL(combine_paged_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p);
+  if (p.num_splits > 16 * p.B)
+    hipLaunchKernelGGL(combine_paged_wide_kernel, dim3((unsigned)rows), dim3(64 * kCW), 0, stream, p);
+  else
+    hipLaunchKernelGGL(combine_paged_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -536,3 +536,22 @@ def test_paged_batch_with_no_tokens(fmt):
         assert (host(oo) == 0).all() and np.isneginf(host(ll)).all()
     assert (host(o3) == 0).all()
     assert np.array_equal(host(lse3), np.broadcast_to(host(sinks), (3, 2, w.H)))
+
+
+@pytest.mark.parametrize("fmt,sinks", [(gen.FMT_FP8, False), (gen.FMT_BF16, True)])
+def test_paged_single_long_request_over_every_range(fmt, sinks):
+    """One 32768-token request over all the device's ranges (256 partials per row): the
+    combine takes a workgroup per row for requests this wide; with sinks as well."""
+    say(f"paged single long request fmt={fmt} sinks={sinks}")
+    w = gen.make_paged(B=1, H=128, q_len=1, lo=32768, hi=32768, page_size=64, fmt=fmt, seed=90 + fmt)
+    d = paged_device_inputs(w)
+    sk = torch.linspace(-2.0, 6.0, w.H, device=DEV) if sinks else None
+    o, lse = mla.paged_decode(d["q"], d["qpe"], d["cache"], w.fmt, d["bt"], d["sl"], w.page_size, w.page_stride,
+                              w.kv_scale, w.sm_scale, num_splits=mla.plan_paged(256, w.B, w.q_len, w.H), sinks=sk)
+    torch.cuda.synchronize()
+    q, qpe = w.q_f64()
+    ro, rl = oracle.paged_decode(q, qpe, w.cache, w.fmt, w.kv_scale, w.page_size, w.page_stride, w.block_tables,
+                                 w.seq_lens, w.sm_scale,
+                                 sinks=None if sk is None else host(sk).astype(np.float64))
+    check_o("O", host(o), ro, _tol_o(fmt))
+    check("LSE", host(lse), rl, TOL_LSE)
