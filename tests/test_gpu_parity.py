@@ -86,6 +86,36 @@ def test_contig_b32_h128_s8192_full_size():
     assert eo <= TOL_O_BF16 and el <= TOL_LSE and epo <= TOL_O_BF16 and epl <= TOL_LSE
 
 
+def test_contig_requests_past_4gib_periodic_cache():
+    """Two requests of 4,198,400 tokens (a 9.7 GB cache; request 1's latent rows start past
+    4 GiB), each cache a 4096-token random block repeated 1025 times.  Attention over m
+    copies of a block equals attention over one block with ln m added to the LSE, so the
+    oracle runs on one block: every split (16 copies, the last one copy) and the merged
+    output are checked against it."""
+    say("contig requests past 4 GiB, periodic cache")
+    P, reps = 4096, 1025
+    c = gen.make_contig(2, 128, P, seed=91)
+    q, qpe, kv, kpe = (bf16_dev(a) for a in (c.q, c.qpe, c.kv, c.kpe))
+    kv_big, kpe_big = kv.repeat(1, reps, 1), kpe.repeat(1, reps, 1)
+    S = P * reps
+    assert kv_big.shape[1] == S and S * 512 * 2 > 2 ** 32
+    del kv, kpe
+    op, lp, L = mla.decode_splitkv(q, qpe, kv_big, kpe_big, c.sm_scale)
+    o, lse = mla.splitkv_combine(op, lp)
+    torch.cuda.synchronize()
+    ns = -(-S // L)
+    assert (L, ns) == (65536, 65)
+    del kv_big, kpe_big
+    torch.cuda.empty_cache()
+    qd, qped, kvd, kped = c.f64()
+    ro, rl = oracle.contig_decode(qd, qped, kvd, kped, c.sm_scale)  # one block: [B, H, 512], [B, H]
+    copies = np.array([L // P] * (ns - 1) + [(S - (ns - 1) * L) // P], dtype=np.float64)
+    check("op", host(op), np.broadcast_to(ro[:, :, None, :], op.shape), TOL_O_BF16)
+    check("lp", host(lp), rl[:, :, None] + np.log(copies)[None, None, :], TOL_LSE)
+    check_o("o", host(o), ro, TOL_O_BF16)
+    check("lse", host(lse), rl + math.log(reps), TOL_LSE)
+
+
 def test_contig_zero_query_is_mean_of_latent():
     say("contig zero query")
     c = gen.make_contig(2, 16, 333, seed=3, zero_q=True)
@@ -232,6 +262,38 @@ def test_paged_padded_page_stride():
     o, lse = _paged_run(w)
     check_o("o", o, ro, TOL_O_QUANT)
     check("lse", lse, rl, TOL_LSE)
+
+
+@pytest.mark.parametrize("fmt", [gen.FMT_BF16, gen.FMT_FP8, gen.FMT_NVFP4])
+def test_paged_pages_past_4gib(fmt):
+    """A 4.6 GiB page pool whose used pages sit between 2 and 4 GiB and past 4 GiB into it:
+    page byte offsets beyond the int32 and uint32 ranges (the oracle reads the same pages
+    from a compact copy)."""
+    say(f"paged pages past 4 GiB fmt={gen.FMT_NAMES[fmt]}")
+    w = gen.make_paged(B=3, H=32, q_len=2, lo=1, hi=1, page_size=64, fmt=fmt, seed=64 + fmt,
+                       seq_lens=[700, 2, 1500], poison_tail=True)
+    ro, rl = _paged_ref(w)
+    stride = w.page_stride
+    big = int(4.6 * 2 ** 30) // stride
+    lo2, lo4 = -(-2 ** 31 // stride), -(-2 ** 32 // stride)
+    rng = np.random.default_rng(7)
+    n = w.num_pages
+    idx = np.concatenate([rng.choice(np.arange(lo2, lo4 - 1), n // 2, replace=False),
+                          rng.choice(np.arange(lo4, big), n - n // 2, replace=False)]).astype(np.int64)
+    rng.shuffle(idx)
+    assert idx.min() * stride >= 2 ** 31 and (idx >= lo4).sum() == n - n // 2
+    pool = torch.empty(big * stride, dtype=torch.uint8, device=DEV)
+    pool.view(big, stride)[torch.from_numpy(idx).to(DEV)] = u8_dev(w.cache).view(n, stride)
+    bt = i32_dev(idx[w.block_tables].astype(np.int32))
+    d = paged_device_inputs(w)
+    for ns in (None, 1):
+        o, lse = mla.paged_decode(d["q"], d["qpe"], pool, w.fmt, bt, d["sl"], w.page_size, stride, w.kv_scale,
+                                  w.sm_scale, num_splits=ns)
+        torch.cuda.synchronize()
+        check_o(f"o {ns}", host(o), ro, _tol_o(fmt))
+        check(f"lse {ns}", host(lse), rl, TOL_LSE)
+    del pool
+    torch.cuda.empty_cache()
 
 
 def test_paged_fp8_every_code():
