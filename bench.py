@@ -13,8 +13,9 @@ token) + Q + QPE + O (bf16) + LSE (fp32) + one int32 block-table entry per page 
 
 Roofline.  The binding roof of the decode kernel is max(bytes / HBM peak, flops / MFMA
 peak of the contraction's own operand type): FP8 MFMA (5.0 PFLOP/s) for the FP8 cache,
-whose products run on FP8 matrix cores, bf16 MFMA (2.5 PFLOP/s) for the bf16 and NVFP4
-caches.  The fraction is quoted against the published peaks and, beside them, against
+whose products run on FP8 matrix cores, bf16 MFMA (2.5 PFLOP/s) for the bf16 cache and
+f16 MFMA (2.5 PFLOP/s) for the NVFP4 cache, whose exact dequantised values and weights run
+on f16 operands.  The fraction is quoted against the published peaks and, beside them, against
 ceilings measured in the same run (a stream-read kernel and MFMA loops,
 libmla_ceiling.so).
 
@@ -42,16 +43,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0                          # MI355X HBM3E, published
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA, published
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA, published
 MALL_BYTES = 256 << 20
 METRIC = "MLA decode KV GB/s + TFLOP/s (% roofline), B=64 H=128 paged fp8"
 # operand type of each paged cache format's matrix-core products
-CONTRACTION = {0: "bf16", 1: "fp8", 2: "bf16", 3: "fp8"}
+CONTRACTION = {0: "bf16", 1: "fp8", 2: "f16", 3: "fp8"}
 ARITHMETIC = {
     0: "bf16 MFMA (bf16 query, bf16 weights), fp32 accumulation",
     1: "FP8 MFMA on the raw FP8 cache: the bf16 query as an exact two-term E4M3 split, the softmax weights "
        "(per-row, per-tile power-of-two scale) as two E4M3 terms (~8 significant bits), fp32 accumulation",
-    2: "bf16 MFMA on the NVFP4 cache dequantised exactly to bf16, fp32 accumulation",
+    2: "f16 MFMA on the NVFP4 cache dequantised exactly to f16 (the bf16 query as f16 after a per-row "
+       "power-of-two scale, the weights in f16), fp32 accumulation",
     3: "FP8 MFMA: query rounded to E4M3, weights as two E4M3 terms, fp32 accumulation",
 }
 KERNEL_SOURCES = ("mla_split_kv_02_amd/csrc/mla_kernels.hip", "mla_split_kv_02_amd/csrc/mla_internal.h")
@@ -174,7 +176,8 @@ def measure_ceilings(torch, dev):
     res = {"hbm_stream_read_GBps": round(nbytes / t_read / 1e9, 1)}
     mb = 1024  # 4 wavefronts per SIMD
     mout = torch.empty(mb * 4, dtype=torch.float32, device=dev)
-    for name, kind, iters in (("bf16", ceiling.MFMA_BF16, 2000), ("fp8", ceiling.MFMA_FP8, 1000)):
+    for name, kind, iters in (("bf16", ceiling.MFMA_BF16, 2000), ("f16", ceiling.MFMA_F16, 2000),
+                              ("fp8", ceiling.MFMA_FP8, 1000)):
         flops = mb * 4 * iters * 4 * ceiling.lib().mla_ceiling_mfma_flops(kind)
         t = timed(lambda: ceiling.mfma(kind, iters, mout, mb), 5)
         res[f"mfma_{name}_TFLOPs"] = round(flops / t / 1e12, 1)

@@ -18,6 +18,7 @@ extern "C" {
 
 #define MLA_CEILING_MFMA_BF16 0 /* v_mfma_f32_32x32x16_bf16 */
 #define MLA_CEILING_MFMA_FP8 1  /* v_mfma_f32_32x32x64_f8f6f4, E4M3 operands */
+#define MLA_CEILING_MFMA_F16 2  /* v_mfma_f32_32x32x16_f16 */
 
 /* Stream read: `blocks` workgroups of 256 threads read the `bytes` of `buf` (16-byte
  * aligned, bytes a multiple of 16) once, in 16-byte coalesced loads, grid-strided;

@@ -13,6 +13,7 @@ CEILING_LIB_PATH = os.path.join(PKG, "libmla_ceiling.so")
 
 MFMA_BF16 = 0
 MFMA_FP8 = 1
+MFMA_F16 = 2
 
 # every symbol include/mla_ceiling.h declares
 EXPORTED_SYMBOLS = ("mla_ceiling_stream_read", "mla_ceiling_mfma", "mla_ceiling_mfma_flops")

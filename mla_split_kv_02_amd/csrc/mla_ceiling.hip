@@ -1,6 +1,6 @@
 // Measured ceilings of the MI355X for the benchmark's roofline fractions: a stream-read
 // kernel (the HBM bandwidth a plain coalesced read reaches) and MFMA loops (the matrix-core
-// rate a kernel doing nothing else reaches, bf16 32x32x16 and FP8 32x32x64).  Built into
+// rate a kernel doing nothing else reaches, bf16 and f16 32x32x16, FP8 32x32x64).  Built into
 // libmla_ceiling.so, apart from the decode library; nothing in the decode path calls it.
 
 #include "mla_ceiling.h"
@@ -12,6 +12,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
@@ -57,6 +58,22 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* out, i
           : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3)
           : "v"(a), "v"(b));
     }
+  } else if (KIND == 2) {
+    f16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = (_Float16)(0.001f * (float)((lane + e + seed) & 7));
+      b[e] = (_Float16)(0.001f * (float)((lane * 3 + e) & 7));
+    }
+    for (int i = 0; i < iters; ++i) {
+      asm volatile(
+          "v_mfma_f32_32x32x16_f16 %0, %4, %5, %0\n\t"
+          "v_mfma_f32_32x32x16_f16 %1, %4, %5, %1\n\t"
+          "v_mfma_f32_32x32x16_f16 %2, %4, %5, %2\n\t"
+          "v_mfma_f32_32x32x16_f16 %3, %4, %5, %3"
+          : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3)
+          : "v"(a), "v"(b));
+    }
   } else {
     i32x8 a, b;
 #pragma unroll
@@ -94,16 +111,20 @@ int mla_ceiling_stream_read(const void* buf, size_t bytes, uint32_t* out, int bl
 }
 
 int mla_ceiling_mfma(int kind, int iters, float* out, int blocks, void* stream) {
-  if (!out || blocks < 1 || iters < 1 || (kind != MLA_CEILING_MFMA_BF16 && kind != MLA_CEILING_MFMA_FP8)) return -1;
+  if (!out || blocks < 1 || iters < 1 ||
+      (kind != MLA_CEILING_MFMA_BF16 && kind != MLA_CEILING_MFMA_FP8 && kind != MLA_CEILING_MFMA_F16))
+    return -1;
   if (kind == MLA_CEILING_MFMA_BF16)
     hipLaunchKernelGGL(mfma_loop_kernel<0>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, out, 1);
+  else if (kind == MLA_CEILING_MFMA_F16)
+    hipLaunchKernelGGL(mfma_loop_kernel<2>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, out, 1);
   else
     hipLaunchKernelGGL(mfma_loop_kernel<1>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, out, 1);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 double mla_ceiling_mfma_flops(int kind) {
-  if (kind == MLA_CEILING_MFMA_BF16) return 2.0 * 32 * 32 * 16;
+  if (kind == MLA_CEILING_MFMA_BF16 || kind == MLA_CEILING_MFMA_F16) return 2.0 * 32 * 32 * 16;
   if (kind == MLA_CEILING_MFMA_FP8) return 2.0 * 32 * 32 * 64;
   return 0.0;
 }

@@ -3,7 +3,9 @@
 // Decode kernel.  One workgroup = 4 wavefronts, one per SIMD, so every wavefront has its
 // SIMD's whole register file: its output accumulators (O^T, 512 dims x 32 rows, fp32 =
 // 256 registers) live in the accumulation registers and its Q^T operand (32 rows x 576
-// dims, bf16 = 144 registers) in the vector registers.  A workgroup owns up to 128 query
+// dims, 16-bit = 144 registers) in the vector registers.  The bf16 cache runs on bf16
+// operands; the NVFP4 cache, dequantised exactly to f16, on f16 operands (the query row
+// scaled by a power of two into f16, the weights in f16).  A workgroup owns up to 128 query
 // rows (query x head) of one request and one token range; wavefront w owns rows
 // 32w .. 32w+31 and does all of their arithmetic:
 //   scores   S^T[32 tok x 32 rows] = K . Q^T         36 MFMA 32x32x16, K from LDS
@@ -59,6 +61,8 @@ namespace mla {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(2))) int i32x2;
@@ -328,11 +332,13 @@ __device__ __forceinline__ void load_nvfp4_raw(const Src& S, int tb, const uint8
   if (wave < 2) scales(3 + wave);
 }
 
-// Raw NVFP4 staging -> bf16 tile.  Thread t writes chunk t % 8 of group m of row t / 8:
+// Raw NVFP4 staging -> f16 tile.  Thread t writes chunk t % 8 of group m of row t / 8:
 // eight codes (4 data bytes at 1024 m + 32 r + 4 (t % 8)) times their scale (group
-// (t % 8) / 2 + 4m of the row: byte (t % 8) / 2 of scale dword m).  The hardware
-// converts the codes exactly to f32 (unit scale); the products have at most 6
-// significant bits, so their high halves are the exact bf16 values.
+// (t % 8) / 2 + 4m of the row: byte (t % 8) / 2 of scale dword m).  With the scale
+// s = 2^E M (M in [1, 2), signed), the scaled FP4 conversion gives code x 2^E (it takes
+// only the exponent of its scale operand) as packed f16, and one packed f16 multiply by
+// M finishes the product.  Every product has at most 6 significant bits and lies in
+// [2^-10, 1536] (or is 0), so each step is exact in f16; a NaN scale gives NaN.
 // The work is cut into nine steps, one per 4 KiB group m of the bf16 tile, so that the
 // output phase can spread them between its MFMAs: read(m) fetches the step's code dword
 // and scale byte, put(m) converts and writes them.
@@ -352,13 +358,15 @@ struct NvDequant {
   }
   __device__ __forceinline__ void put(int m) {
     const float scale = __builtin_amdgcn_cvt_pk_f32_fp8((int)sc[m], false)[0];
-    const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[m], 1.0f, 0);
-    const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[m], 1.0f, 1);
-    const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[m], 1.0f, 2);
-    const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[m], 1.0f, 3);
+    const float mant = __uint_as_float((__float_as_uint(scale) & 0x807FFFFFu) | 0x3F800000u);  // +-M
+    const f16x2 m2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(mant, mant));  // exact: 4 bits
+    const f16x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[m], scale, 0) * m2;
+    const f16x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[m], scale, 1) * m2;
+    const f16x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[m], scale, 2) * m2;
+    const f16x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[m], scale, 3) * m2;
     *at<u32x4>(wr + kGroupBytes * m) =
-        u32x4{pack_hi16(f0[0] * scale, f0[1] * scale), pack_hi16(f1[0] * scale, f1[1] * scale),
-              pack_hi16(f2[0] * scale, f2[1] * scale), pack_hi16(f3[0] * scale, f3[1] * scale)};
+        u32x4{__builtin_bit_cast(unsigned, f0), __builtin_bit_cast(unsigned, f1), __builtin_bit_cast(unsigned, f2),
+              __builtin_bit_cast(unsigned, f3)};
   }
 };
 
@@ -376,6 +384,128 @@ __device__ __forceinline__ void dequant_nvfp4(uint32_t st, uint32_t tile, int ti
 // of lane l holds D[i = 8 (v / 4) + 4 (l / 32) + v % 4][j = l % 32].
 // ------------------------------------------------------------------------------------
 
+// The instruction block of qk_tile, for MF the MFMA 32x32x16 on bf16 or on f16 operands.
+#define MLA_QK_TILE_ASM(MF) \
+  asm volatile( \
+  "ds_read_b128 %[a0], %[b0] offset:0\n\t" \
+  "ds_read_b128 %[a1], %[b1] offset:0\n\t" \
+  "ds_read_b128 %[a2], %[b2] offset:0\n\t" \
+  "ds_read_b128 %[a3], %[b3] offset:0\n\t" \
+  "ds_read_b128 %[a4], %[b0] offset:4096\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a0], %[q0], 0\n\t" \
+  "ds_read_b128 %[a5], %[b1] offset:4096\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a1], %[q1], %[s]\n\t" \
+  "ds_read_b128 %[a6], %[b2] offset:4096\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a2], %[q2], %[s]\n\t" \
+  "ds_read_b128 %[a0], %[b3] offset:4096\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a3], %[q3], %[s]\n\t" \
+  "ds_read_b128 %[a1], %[b0] offset:8192\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a4], %[q4], %[s]\n\t" \
+  "ds_read_b128 %[a2], %[b1] offset:8192\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a5], %[q5], %[s]\n\t" \
+  "ds_read_b128 %[a3], %[b2] offset:8192\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a6], %[q6], %[s]\n\t" \
+  "ds_read_b128 %[a4], %[b3] offset:8192\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a0], %[q7], %[s]\n\t" \
+  "ds_read_b128 %[a5], %[b0] offset:12288\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a1], %[q8], %[s]\n\t" \
+  "ds_read_b128 %[a6], %[b1] offset:12288\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a2], %[q9], %[s]\n\t" \
+  "ds_read_b128 %[a0], %[b2] offset:12288\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a3], %[q10], %[s]\n\t" \
+  "ds_read_b128 %[a1], %[b3] offset:12288\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a4], %[q11], %[s]\n\t" \
+  "ds_read_b128 %[a2], %[b0] offset:16384\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a5], %[q12], %[s]\n\t" \
+  "ds_read_b128 %[a3], %[b1] offset:16384\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a6], %[q13], %[s]\n\t" \
+  "ds_read_b128 %[a4], %[b2] offset:16384\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a0], %[q14], %[s]\n\t" \
+  "ds_read_b128 %[a5], %[b3] offset:16384\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a1], %[q15], %[s]\n\t" \
+  "ds_read_b128 %[a6], %[b0] offset:20480\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a2], %[q16], %[s]\n\t" \
+  "ds_read_b128 %[a0], %[b1] offset:20480\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a3], %[q17], %[s]\n\t" \
+  "ds_read_b128 %[a1], %[b2] offset:20480\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a4], %[q18], %[s]\n\t" \
+  "ds_read_b128 %[a2], %[b3] offset:20480\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a5], %[q19], %[s]\n\t" \
+  "ds_read_b128 %[a3], %[b0] offset:24576\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a6], %[q20], %[s]\n\t" \
+  "ds_read_b128 %[a4], %[b1] offset:24576\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a0], %[q21], %[s]\n\t" \
+  "ds_read_b128 %[a5], %[b2] offset:24576\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a1], %[q22], %[s]\n\t" \
+  "ds_read_b128 %[a6], %[b3] offset:24576\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a2], %[q23], %[s]\n\t" \
+  "ds_read_b128 %[a0], %[b0] offset:28672\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a3], %[q24], %[s]\n\t" \
+  "ds_read_b128 %[a1], %[b1] offset:28672\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a4], %[q25], %[s]\n\t" \
+  "ds_read_b128 %[a2], %[b2] offset:28672\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a5], %[q26], %[s]\n\t" \
+  "ds_read_b128 %[a3], %[b3] offset:28672\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a6], %[q27], %[s]\n\t" \
+  "ds_read_b128 %[a4], %[b0] offset:32768\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a0], %[q28], %[s]\n\t" \
+  "ds_read_b128 %[a5], %[b1] offset:32768\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a1], %[q29], %[s]\n\t" \
+  "ds_read_b128 %[a6], %[b2] offset:32768\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a2], %[q30], %[s]\n\t" \
+  "ds_read_b128 %[a0], %[b3] offset:32768\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a3], %[q31], %[s]\n\t" \
+  "s_waitcnt lgkmcnt(3)\n\t" \
+  MF " %[s], %[a4], %[q32], %[s]\n\t" \
+  "s_waitcnt lgkmcnt(2)\n\t" \
+  MF " %[s], %[a5], %[q33], %[s]\n\t" \
+  "s_waitcnt lgkmcnt(1)\n\t" \
+  MF " %[s], %[a6], %[q34], %[s]\n\t" \
+  "s_waitcnt lgkmcnt(0)\n\t" \
+  MF " %[s], %[a0], %[q35], %[s]\n\t" \
+  "s_nop 7\n\ts_nop 7\n\ts_nop 7" \
+  : [s] "=&v"(s), [a0] "=&v"(a0), [a1] "=&v"(a1), [a2] "=&v"(a2), [a3] "=&v"(a3), [a4] "=&v"(a4), [a5] "=&v"(a5), [a6] "=&v"(a6) \
+  : [b0] "v"(b0), [b1] "v"(b1), [b2] "v"(b2), [b3] "v"(b3), \
+  [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]), [q5] "v"(q[5]), \
+  [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8]), [q9] "v"(q[9]), [q10] "v"(q[10]), [q11] "v"(q[11]), \
+  [q12] "v"(q[12]), [q13] "v"(q[13]), [q14] "v"(q[14]), [q15] "v"(q[15]), [q16] "v"(q[16]), [q17] "v"(q[17]), \
+  [q18] "v"(q[18]), [q19] "v"(q[19]), [q20] "v"(q[20]), [q21] "v"(q[21]), [q22] "v"(q[22]), [q23] "v"(q[23]), \
+  [q24] "v"(q[24]), [q25] "v"(q[25]), [q26] "v"(q[26]), [q27] "v"(q[27]), [q28] "v"(q[28]), [q29] "v"(q[29]), \
+  [q30] "v"(q[30]), [q31] "v"(q[31]), [q32] "v"(q[32]), [q33] "v"(q[33]), [q34] "v"(q[34]), [q35] "v"(q[35]) \
+  : "memory")
+
 // Scores of one tile: S^T[token][row], A = K (token l % 32, dims 16k + 8 (l / 32) ..),
 // B = Q^T (in registers).  K-step k reads chunk 2k + l/32 of the lane's token row: group
 // k / 4, swizzled position 2 (k % 4) + l/32, i.e. address ab[k % 4] + 4096 (k / 4) past
@@ -387,129 +517,15 @@ __device__ __forceinline__ void dequant_nvfp4(uint32_t st, uint32_t tile, int ti
 // back-to-back MFMAs accumulating into the same registers need no wait states.  The
 // closing s_nop run gives the wait states (more than the 18 required) before vector ALU
 // instructions may read the result.
+template <bool H = false>
 __device__ __forceinline__ f32x16 qk_tile(const bf16x8* q, uint32_t tile, const int* ab) {
   const uint32_t b0 = tile + ab[0], b1 = tile + ab[1], b2 = tile + ab[2], b3 = tile + ab[3];
   f32x16 s;
   bf16x8 a0, a1, a2, a3, a4, a5, a6;
-  asm volatile(
-      "ds_read_b128 %[a0], %[b0] offset:0\n\t"
-      "ds_read_b128 %[a1], %[b1] offset:0\n\t"
-      "ds_read_b128 %[a2], %[b2] offset:0\n\t"
-      "ds_read_b128 %[a3], %[b3] offset:0\n\t"
-      "ds_read_b128 %[a4], %[b0] offset:4096\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q0], 0\n\t"
-      "ds_read_b128 %[a5], %[b1] offset:4096\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q1], %[s]\n\t"
-      "ds_read_b128 %[a6], %[b2] offset:4096\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q2], %[s]\n\t"
-      "ds_read_b128 %[a0], %[b3] offset:4096\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q3], %[s]\n\t"
-      "ds_read_b128 %[a1], %[b0] offset:8192\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q4], %[s]\n\t"
-      "ds_read_b128 %[a2], %[b1] offset:8192\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q5], %[s]\n\t"
-      "ds_read_b128 %[a3], %[b2] offset:8192\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q6], %[s]\n\t"
-      "ds_read_b128 %[a4], %[b3] offset:8192\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q7], %[s]\n\t"
-      "ds_read_b128 %[a5], %[b0] offset:12288\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q8], %[s]\n\t"
-      "ds_read_b128 %[a6], %[b1] offset:12288\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q9], %[s]\n\t"
-      "ds_read_b128 %[a0], %[b2] offset:12288\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q10], %[s]\n\t"
-      "ds_read_b128 %[a1], %[b3] offset:12288\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q11], %[s]\n\t"
-      "ds_read_b128 %[a2], %[b0] offset:16384\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q12], %[s]\n\t"
-      "ds_read_b128 %[a3], %[b1] offset:16384\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q13], %[s]\n\t"
-      "ds_read_b128 %[a4], %[b2] offset:16384\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q14], %[s]\n\t"
-      "ds_read_b128 %[a5], %[b3] offset:16384\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q15], %[s]\n\t"
-      "ds_read_b128 %[a6], %[b0] offset:20480\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q16], %[s]\n\t"
-      "ds_read_b128 %[a0], %[b1] offset:20480\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q17], %[s]\n\t"
-      "ds_read_b128 %[a1], %[b2] offset:20480\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q18], %[s]\n\t"
-      "ds_read_b128 %[a2], %[b3] offset:20480\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q19], %[s]\n\t"
-      "ds_read_b128 %[a3], %[b0] offset:24576\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q20], %[s]\n\t"
-      "ds_read_b128 %[a4], %[b1] offset:24576\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q21], %[s]\n\t"
-      "ds_read_b128 %[a5], %[b2] offset:24576\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q22], %[s]\n\t"
-      "ds_read_b128 %[a6], %[b3] offset:24576\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q23], %[s]\n\t"
-      "ds_read_b128 %[a0], %[b0] offset:28672\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q24], %[s]\n\t"
-      "ds_read_b128 %[a1], %[b1] offset:28672\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q25], %[s]\n\t"
-      "ds_read_b128 %[a2], %[b2] offset:28672\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q26], %[s]\n\t"
-      "ds_read_b128 %[a3], %[b3] offset:28672\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q27], %[s]\n\t"
-      "ds_read_b128 %[a4], %[b0] offset:32768\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q28], %[s]\n\t"
-      "ds_read_b128 %[a5], %[b1] offset:32768\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q29], %[s]\n\t"
-      "ds_read_b128 %[a6], %[b2] offset:32768\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q30], %[s]\n\t"
-      "ds_read_b128 %[a0], %[b3] offset:32768\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q31], %[s]\n\t"
-      "s_waitcnt lgkmcnt(3)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q32], %[s]\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q33], %[s]\n\t"
-      "s_waitcnt lgkmcnt(1)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q34], %[s]\n\t"
-      "s_waitcnt lgkmcnt(0)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q35], %[s]\n\t"
-      "s_nop 7\n\ts_nop 7\n\ts_nop 7"
-      : [s] "=&v"(s), [a0] "=&v"(a0), [a1] "=&v"(a1), [a2] "=&v"(a2), [a3] "=&v"(a3), [a4] "=&v"(a4), [a5] "=&v"(a5), [a6] "=&v"(a6)
-      : [b0] "v"(b0), [b1] "v"(b1), [b2] "v"(b2), [b3] "v"(b3),
-        [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]), [q5] "v"(q[5]),
-        [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8]), [q9] "v"(q[9]), [q10] "v"(q[10]), [q11] "v"(q[11]),
-        [q12] "v"(q[12]), [q13] "v"(q[13]), [q14] "v"(q[14]), [q15] "v"(q[15]), [q16] "v"(q[16]), [q17] "v"(q[17]),
-        [q18] "v"(q[18]), [q19] "v"(q[19]), [q20] "v"(q[20]), [q21] "v"(q[21]), [q22] "v"(q[22]), [q23] "v"(q[23]),
-        [q24] "v"(q[24]), [q25] "v"(q[25]), [q26] "v"(q[26]), [q27] "v"(q[27]), [q28] "v"(q[28]), [q29] "v"(q[29]),
-        [q30] "v"(q[30]), [q31] "v"(q[31]), [q32] "v"(q[32]), [q33] "v"(q[33]), [q34] "v"(q[34]), [q35] "v"(q[35])
-      : "memory");
+  if constexpr (H)
+    MLA_QK_TILE_ASM("v_mfma_f32_32x32x16_f16");
+  else
+    MLA_QK_TILE_ASM("v_mfma_f32_32x32x16_bf16");
   return s;
 }
 
@@ -522,7 +538,17 @@ __device__ __forceinline__ f32x16 qk_tile(const bf16x8* q, uint32_t tile, const 
 // swizzle flipped, so the second K-step flips byte-offset bit 6 as well; vb[2e + 1] is
 // vb[2e] with that bit flipped).  pp holds P^T.  NB blocks from block db0 (even) into
 // o[0 .. NB): the wavefront's share of the 512 dims when several share one row block.
-template <int NB = kDimBlocks>
+// c += a . b on the 32x32x16 matrix core, operands bf16 or (H) f16, held as 16-byte vectors
+template <bool H>
+__device__ __forceinline__ f32x16 mfma16(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (H)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int NB = kDimBlocks, bool H = false>
 __device__ __forceinline__ void pv_tile(f32x16* o, uint32_t tile, const unsigned* pp, const int* vb, int db0 = 0) {
   uint32_t base[4];  // [e][db & 1]
 #pragma unroll
@@ -537,7 +563,7 @@ __device__ __forceinline__ void pv_tile(f32x16* o, uint32_t tile, const unsigned
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at<s16x4>(base[flip] + off));
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at<s16x4>(base[2 + flip] + off));
       const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[db], 0, 0, 0);
+      o[db] = mfma16<H>(va, pb, o[db]);
     }
   }
 }
@@ -582,6 +608,7 @@ struct Softmax {
 // log2 units.  Returns the factor for the row's accumulators before this tile's
 // product and P^T in the output product's B layout: pp[4 ks + ..] holds tokens
 // 16 ks + 8 (l / 32) .. + 8 of the row.
+template <bool H = false>
 __device__ __forceinline__ float softmax_tile(Softmax& S, float* x, float c, unsigned* pp) {
   float mt = x[0];
 #pragma unroll
@@ -604,12 +631,19 @@ __device__ __forceinline__ float softmax_tile(Softmax& S, float* x, float c, uns
   for (int v = 0; v < 16; ++v) acc += e[v];
   S.l_sum += acc;
   unsigned d[8];
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
   for (int v = 0; v < 8; ++v) {
-    const bf16x2 pr = {(__bf16)e[2 * v], (__bf16)e[2 * v + 1]};
-    S.l_rnd = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, S.l_rnd, false);
-    d[v] = __builtin_bit_cast(unsigned, pr);
+    if constexpr (H) {
+      const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+      const f16x2 pr = {(_Float16)e[2 * v], (_Float16)e[2 * v + 1]};
+      S.l_rnd = __builtin_amdgcn_fdot2(pr, ones, S.l_rnd, false);
+      d[v] = __builtin_bit_cast(unsigned, pr);
+    } else {
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      const bf16x2 pr = {(__bf16)e[2 * v], (__bf16)e[2 * v + 1]};
+      S.l_rnd = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, S.l_rnd, false);
+      d[v] = __builtin_bit_cast(unsigned, pr);
+    }
   }
   // d[4ks + 0..1]: tokens 16ks + 4 (l/32) + 0..3; d[4ks + 2..3]: tokens 16ks + 8 + 4 (l/32) + 0..3.
   // The low half needs tokens 16ks + 0..7 (its own d0 d1, then the high half's d0 d1), the
@@ -626,6 +660,228 @@ __device__ __forceinline__ float softmax_tile(Softmax& S, float* x, float c, uns
   return alpha;
 }
 
+// The instruction block of qk_softmax_tile, for bf16 or f16 operands: MF the MFMA
+// 32x32x16, CV the packing conversion of the weights, DT the dot product that adds a
+// packed pair of rounded weights to l_rnd (its second operand the pair (1, 1)).
+#define MLA_QK_SOFTMAX_ASM(MF, CV, DT) \
+  asm volatile( \
+  "ds_read_b128 %[a0], %[b0] offset:0\n\t" \
+  "ds_read_b128 %[a1], %[b1] offset:0\n\t" \
+  "ds_read_b128 %[a2], %[b2] offset:0\n\t" \
+  "ds_read_b128 %[a3], %[b3] offset:0\n\t" \
+  "ds_read_b128 %[a4], %[b0] offset:4096\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a0], %[q0], 0\n\t" \
+  "ds_read_b128 %[a5], %[b1] offset:4096\n\t" \
+  "v_max3_f32 %[t0], %[x0], %[x1], %[x2]\n\t" \
+  "v_max3_f32 %[t0], %[t0], %[x3], %[x4]\n\t" \
+  "v_max3_f32 %[t0], %[t0], %[x5], %[x6]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a1], %[q1], %[s]\n\t" \
+  "ds_read_b128 %[a6], %[b2] offset:4096\n\t" \
+  "v_max3_f32 %[t0], %[t0], %[x7], %[x8]\n\t" \
+  "v_max3_f32 %[t0], %[t0], %[x9], %[x10]\n\t" \
+  "v_max3_f32 %[t0], %[t0], %[x11], %[x12]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a2], %[q2], %[s]\n\t" \
+  "ds_read_b128 %[a0], %[b3] offset:4096\n\t" \
+  "v_max3_f32 %[t0], %[t0], %[x13], %[x14]\n\t" \
+  "v_max_f32 %[t0], %[t0], %[x15]\n\t" \
+  "v_mov_b32 %[t1], %[t0]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a3], %[q3], %[s]\n\t" \
+  "ds_read_b128 %[a1], %[b0] offset:8192\n\t" \
+  "v_permlane32_swap_b32 %[t0], %[t1]\n\t" \
+  "v_max_f32 %[t0], %[t0], %[t1]\n\t" \
+  "v_mul_f32 %[t0], %[c], %[t0]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a4], %[q4], %[s]\n\t" \
+  "ds_read_b128 %[a2], %[b1] offset:8192\n\t" \
+  "v_add_f32 %[t1], 0x41000000, %[m]\n\t" \
+  "v_cmp_gt_f32 vcc, %[t0], %[t1]\n\t" \
+  "v_cndmask_b32 %[t1], %[m], %[t0], vcc\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a5], %[q5], %[s]\n\t" \
+  "ds_read_b128 %[a3], %[b2] offset:8192\n\t" \
+  "v_sub_f32 %[t2], %[m], %[t1]\n\t" \
+  "v_exp_f32 %[t2], %[t2]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a6], %[q6], %[s]\n\t" \
+  "ds_read_b128 %[a4], %[b3] offset:8192\n\t" \
+  "v_cndmask_b32 %[al], 1.0, %[t2], vcc\n\t" \
+  "v_cmp_eq_f32 vcc, 0xff800000, %[m]\n\t" \
+  "v_cndmask_b32_e64 %[al], %[al], 1.0, vcc\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a0], %[q7], %[s]\n\t" \
+  "ds_read_b128 %[a5], %[b0] offset:12288\n\t" \
+  "v_mul_f32 %[ls], %[ls], %[al]\n\t" \
+  "v_mul_f32 %[lr], %[lr], %[al]\n\t" \
+  "v_mov_b32 %[m], %[t1]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a1], %[q8], %[s]\n\t" \
+  "ds_read_b128 %[a6], %[b1] offset:12288\n\t" \
+  "v_cmp_eq_f32 vcc, 0xff800000, %[t1]\n\t" \
+  "v_cndmask_b32_e64 %[t2], -%[t1], 0, vcc\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a2], %[q9], %[s]\n\t" \
+  "ds_read_b128 %[a0], %[b2] offset:12288\n\t" \
+  "v_fma_f32 %[x0], %[x0], %[c], %[t2]\n\t" \
+  "v_exp_f32 %[x0], %[x0]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a3], %[q10], %[s]\n\t" \
+  "ds_read_b128 %[a1], %[b3] offset:12288\n\t" \
+  "v_fma_f32 %[x1], %[x1], %[c], %[t2]\n\t" \
+  "v_exp_f32 %[x1], %[x1]\n\t" \
+  "v_add_f32 %[t0], 0, %[x0]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a4], %[q11], %[s]\n\t" \
+  "ds_read_b128 %[a2], %[b0] offset:16384\n\t" \
+  "v_fma_f32 %[x2], %[x2], %[c], %[t2]\n\t" \
+  "v_exp_f32 %[x2], %[x2]\n\t" \
+  "v_add_f32 %[t0], %[t0], %[x1]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a5], %[q12], %[s]\n\t" \
+  "ds_read_b128 %[a3], %[b1] offset:16384\n\t" \
+  "v_fma_f32 %[x3], %[x3], %[c], %[t2]\n\t" \
+  "v_exp_f32 %[x3], %[x3]\n\t" \
+  "v_add_f32 %[t0], %[t0], %[x2]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a6], %[q13], %[s]\n\t" \
+  "ds_read_b128 %[a4], %[b2] offset:16384\n\t" \
+  "v_fma_f32 %[x4], %[x4], %[c], %[t2]\n\t" \
+  "v_exp_f32 %[x4], %[x4]\n\t" \
+  "v_add_f32 %[t0], %[t0], %[x3]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a0], %[q14], %[s]\n\t" \
+  "ds_read_b128 %[a5], %[b3] offset:16384\n\t" \
+  "v_fma_f32 %[x5], %[x5], %[c], %[t2]\n\t" \
+  "v_exp_f32 %[x5], %[x5]\n\t" \
+  "v_add_f32 %[t0], %[t0], %[x4]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a1], %[q15], %[s]\n\t" \
+  "ds_read_b128 %[a6], %[b0] offset:20480\n\t" \
+  "v_fma_f32 %[x6], %[x6], %[c], %[t2]\n\t" \
+  "v_exp_f32 %[x6], %[x6]\n\t" \
+  "v_add_f32 %[t0], %[t0], %[x5]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a2], %[q16], %[s]\n\t" \
+  "ds_read_b128 %[a0], %[b1] offset:20480\n\t" \
+  "v_fma_f32 %[x7], %[x7], %[c], %[t2]\n\t" \
+  "v_exp_f32 %[x7], %[x7]\n\t" \
+  "v_add_f32 %[t0], %[t0], %[x6]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a3], %[q17], %[s]\n\t" \
+  "ds_read_b128 %[a1], %[b2] offset:20480\n\t" \
+  "v_fma_f32 %[x8], %[x8], %[c], %[t2]\n\t" \
+  "v_exp_f32 %[x8], %[x8]\n\t" \
+  "v_add_f32 %[t0], %[t0], %[x7]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a4], %[q18], %[s]\n\t" \
+  "ds_read_b128 %[a2], %[b3] offset:20480\n\t" \
+  "v_fma_f32 %[x9], %[x9], %[c], %[t2]\n\t" \
+  "v_exp_f32 %[x9], %[x9]\n\t" \
+  "v_add_f32 %[t0], %[t0], %[x8]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a5], %[q19], %[s]\n\t" \
+  "ds_read_b128 %[a3], %[b0] offset:24576\n\t" \
+  "v_fma_f32 %[x10], %[x10], %[c], %[t2]\n\t" \
+  "v_exp_f32 %[x10], %[x10]\n\t" \
+  "v_add_f32 %[t0], %[t0], %[x9]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a6], %[q20], %[s]\n\t" \
+  "ds_read_b128 %[a4], %[b1] offset:24576\n\t" \
+  "v_fma_f32 %[x11], %[x11], %[c], %[t2]\n\t" \
+  "v_exp_f32 %[x11], %[x11]\n\t" \
+  "v_add_f32 %[t0], %[t0], %[x10]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a0], %[q21], %[s]\n\t" \
+  "ds_read_b128 %[a5], %[b2] offset:24576\n\t" \
+  "v_fma_f32 %[x12], %[x12], %[c], %[t2]\n\t" \
+  "v_exp_f32 %[x12], %[x12]\n\t" \
+  "v_add_f32 %[t0], %[t0], %[x11]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a1], %[q22], %[s]\n\t" \
+  "ds_read_b128 %[a6], %[b3] offset:24576\n\t" \
+  "v_fma_f32 %[x13], %[x13], %[c], %[t2]\n\t" \
+  "v_exp_f32 %[x13], %[x13]\n\t" \
+  "v_add_f32 %[t0], %[t0], %[x12]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a2], %[q23], %[s]\n\t" \
+  "ds_read_b128 %[a0], %[b0] offset:28672\n\t" \
+  "v_fma_f32 %[x14], %[x14], %[c], %[t2]\n\t" \
+  "v_exp_f32 %[x14], %[x14]\n\t" \
+  "v_add_f32 %[t0], %[t0], %[x13]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a3], %[q24], %[s]\n\t" \
+  "ds_read_b128 %[a1], %[b1] offset:28672\n\t" \
+  "v_fma_f32 %[x15], %[x15], %[c], %[t2]\n\t" \
+  "v_exp_f32 %[x15], %[x15]\n\t" \
+  "v_add_f32 %[t0], %[t0], %[x14]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a4], %[q25], %[s]\n\t" \
+  "ds_read_b128 %[a2], %[b2] offset:28672\n\t" \
+  "v_add_f32 %[t0], %[t0], %[x15]\n\t" \
+  "v_add_f32 %[ls], %[ls], %[t0]\n\t" \
+  CV " %[x0], %[x0], %[x1]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a5], %[q26], %[s]\n\t" \
+  "ds_read_b128 %[a3], %[b3] offset:28672\n\t" \
+  DT " %[x0]\n\t" \
+  CV " %[x1], %[x2], %[x3]\n\t" \
+  DT " %[x1]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a6], %[q27], %[s]\n\t" \
+  "ds_read_b128 %[a4], %[b0] offset:32768\n\t" \
+  CV " %[x2], %[x4], %[x5]\n\t" \
+  DT " %[x2]\n\t" \
+  CV " %[x3], %[x6], %[x7]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a0], %[q28], %[s]\n\t" \
+  "ds_read_b128 %[a5], %[b1] offset:32768\n\t" \
+  DT " %[x3]\n\t" \
+  CV " %[x4], %[x8], %[x9]\n\t" \
+  DT " %[x4]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a1], %[q29], %[s]\n\t" \
+  "ds_read_b128 %[a6], %[b2] offset:32768\n\t" \
+  CV " %[x5], %[x10], %[x11]\n\t" \
+  DT " %[x5]\n\t" \
+  CV " %[x6], %[x12], %[x13]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a2], %[q30], %[s]\n\t" \
+  "ds_read_b128 %[a0], %[b3] offset:32768\n\t" \
+  DT " %[x6]\n\t" \
+  CV " %[x7], %[x14], %[x15]\n\t" \
+  DT " %[x7]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  MF " %[s], %[a3], %[q31], %[s]\n\t" \
+  "v_permlane32_swap_b32 %[x0], %[x2]\n\t" \
+  "v_permlane32_swap_b32 %[x1], %[x3]\n\t" \
+  "s_waitcnt lgkmcnt(3)\n\t" \
+  MF " %[s], %[a4], %[q32], %[s]\n\t" \
+  "v_permlane32_swap_b32 %[x4], %[x6]\n\t" \
+  "v_permlane32_swap_b32 %[x5], %[x7]\n\t" \
+  "s_waitcnt lgkmcnt(2)\n\t" \
+  MF " %[s], %[a5], %[q33], %[s]\n\t" \
+  "s_waitcnt lgkmcnt(1)\n\t" \
+  MF " %[s], %[a6], %[q34], %[s]\n\t" \
+  "s_waitcnt lgkmcnt(0)\n\t" \
+  MF " %[s], %[a0], %[q35], %[s]\n\t" \
+  "s_nop 7\n\ts_nop 7\n\ts_nop 7" \
+  : [s] "=&v"(s), [a0] "=&v"(a0), [a1] "=&v"(a1), [a2] "=&v"(a2), [a3] "=&v"(a3), [a4] "=&v"(a4), [a5] "=&v"(a5), \
+  [a6] "=&v"(a6), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [al] "=&v"(alpha), [x0] "+v"(x[0]), [x1] "+v"(x[1]), [x2] "+v"(x[2]), \
+  [x3] "+v"(x[3]), [x4] "+v"(x[4]), [x5] "+v"(x[5]), [x6] "+v"(x[6]), [x7] "+v"(x[7]), [x8] "+v"(x[8]), \
+  [x9] "+v"(x[9]), [x10] "+v"(x[10]), [x11] "+v"(x[11]), [x12] "+v"(x[12]), [x13] "+v"(x[13]), \
+  [x14] "+v"(x[14]), [x15] "+v"(x[15]), [m] "+v"(S.m_used), [ls] "+v"(S.l_sum), [lr] "+v"(S.l_rnd) \
+  : [b0] "v"(b0), [b1] "v"(b1), [b2] "v"(b2), [b3] "v"(b3), [c] "v"(c), \
+  [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]), [q5] "v"(q[5]), \
+  [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8]), [q9] "v"(q[9]), [q10] "v"(q[10]), [q11] "v"(q[11]), \
+  [q12] "v"(q[12]), [q13] "v"(q[13]), [q14] "v"(q[14]), [q15] "v"(q[15]), [q16] "v"(q[16]), [q17] "v"(q[17]), \
+  [q18] "v"(q[18]), [q19] "v"(q[19]), [q20] "v"(q[20]), [q21] "v"(q[21]), [q22] "v"(q[22]), [q23] "v"(q[23]), \
+  [q24] "v"(q[24]), [q25] "v"(q[25]), [q26] "v"(q[26]), [q27] "v"(q[27]), [q28] "v"(q[28]), [q29] "v"(q[29]), \
+  [q30] "v"(q[30]), [q31] "v"(q[31]), [q32] "v"(q[32]), [q33] "v"(q[33]), [q34] "v"(q[34]), [q35] "v"(q[35]) \
+  : "vcc", "memory")
+
 // Scores of tile i as in qk_tile, with the online softmax of tile i-1 (the same steps
 // as softmax_tile) spread over the MFMA chain: vector ALU work on registers the chain
 // does not touch, which issues while the matrix core is busy.  x: the raw scores of
@@ -635,229 +891,17 @@ __device__ __forceinline__ float softmax_tile(Softmax& S, float* x, float c, uns
 // result is read three or more instructions later, a cross-half swap reads registers
 // written two or more instructions earlier, and vcc is written and read only by these
 // steps.
+template <bool H = false>
 __device__ __forceinline__ f32x16 qk_softmax_tile(const bf16x8* q, uint32_t tile, const int* ab, float* x,
                                                   Softmax& S, float c, unsigned* pp, float& alpha) {
   const uint32_t b0 = tile + ab[0], b1 = tile + ab[1], b2 = tile + ab[2], b3 = tile + ab[3];
   f32x16 s;
   bf16x8 a0, a1, a2, a3, a4, a5, a6;
   float t0, t1, t2;
-  asm volatile(
-      "ds_read_b128 %[a0], %[b0] offset:0\n\t"
-      "ds_read_b128 %[a1], %[b1] offset:0\n\t"
-      "ds_read_b128 %[a2], %[b2] offset:0\n\t"
-      "ds_read_b128 %[a3], %[b3] offset:0\n\t"
-      "ds_read_b128 %[a4], %[b0] offset:4096\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q0], 0\n\t"
-      "ds_read_b128 %[a5], %[b1] offset:4096\n\t"
-      "v_max3_f32 %[t0], %[x0], %[x1], %[x2]\n\t"
-      "v_max3_f32 %[t0], %[t0], %[x3], %[x4]\n\t"
-      "v_max3_f32 %[t0], %[t0], %[x5], %[x6]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q1], %[s]\n\t"
-      "ds_read_b128 %[a6], %[b2] offset:4096\n\t"
-      "v_max3_f32 %[t0], %[t0], %[x7], %[x8]\n\t"
-      "v_max3_f32 %[t0], %[t0], %[x9], %[x10]\n\t"
-      "v_max3_f32 %[t0], %[t0], %[x11], %[x12]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q2], %[s]\n\t"
-      "ds_read_b128 %[a0], %[b3] offset:4096\n\t"
-      "v_max3_f32 %[t0], %[t0], %[x13], %[x14]\n\t"
-      "v_max_f32 %[t0], %[t0], %[x15]\n\t"
-      "v_mov_b32 %[t1], %[t0]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q3], %[s]\n\t"
-      "ds_read_b128 %[a1], %[b0] offset:8192\n\t"
-      "v_permlane32_swap_b32 %[t0], %[t1]\n\t"
-      "v_max_f32 %[t0], %[t0], %[t1]\n\t"
-      "v_mul_f32 %[t0], %[c], %[t0]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q4], %[s]\n\t"
-      "ds_read_b128 %[a2], %[b1] offset:8192\n\t"
-      "v_add_f32 %[t1], 0x41000000, %[m]\n\t"
-      "v_cmp_gt_f32 vcc, %[t0], %[t1]\n\t"
-      "v_cndmask_b32 %[t1], %[m], %[t0], vcc\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q5], %[s]\n\t"
-      "ds_read_b128 %[a3], %[b2] offset:8192\n\t"
-      "v_sub_f32 %[t2], %[m], %[t1]\n\t"
-      "v_exp_f32 %[t2], %[t2]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q6], %[s]\n\t"
-      "ds_read_b128 %[a4], %[b3] offset:8192\n\t"
-      "v_cndmask_b32 %[al], 1.0, %[t2], vcc\n\t"
-      "v_cmp_eq_f32 vcc, 0xff800000, %[m]\n\t"
-      "v_cndmask_b32_e64 %[al], %[al], 1.0, vcc\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q7], %[s]\n\t"
-      "ds_read_b128 %[a5], %[b0] offset:12288\n\t"
-      "v_mul_f32 %[ls], %[ls], %[al]\n\t"
-      "v_mul_f32 %[lr], %[lr], %[al]\n\t"
-      "v_mov_b32 %[m], %[t1]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q8], %[s]\n\t"
-      "ds_read_b128 %[a6], %[b1] offset:12288\n\t"
-      "v_cmp_eq_f32 vcc, 0xff800000, %[t1]\n\t"
-      "v_cndmask_b32_e64 %[t2], -%[t1], 0, vcc\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q9], %[s]\n\t"
-      "ds_read_b128 %[a0], %[b2] offset:12288\n\t"
-      "v_fma_f32 %[x0], %[x0], %[c], %[t2]\n\t"
-      "v_exp_f32 %[x0], %[x0]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q10], %[s]\n\t"
-      "ds_read_b128 %[a1], %[b3] offset:12288\n\t"
-      "v_fma_f32 %[x1], %[x1], %[c], %[t2]\n\t"
-      "v_exp_f32 %[x1], %[x1]\n\t"
-      "v_add_f32 %[t0], 0, %[x0]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q11], %[s]\n\t"
-      "ds_read_b128 %[a2], %[b0] offset:16384\n\t"
-      "v_fma_f32 %[x2], %[x2], %[c], %[t2]\n\t"
-      "v_exp_f32 %[x2], %[x2]\n\t"
-      "v_add_f32 %[t0], %[t0], %[x1]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q12], %[s]\n\t"
-      "ds_read_b128 %[a3], %[b1] offset:16384\n\t"
-      "v_fma_f32 %[x3], %[x3], %[c], %[t2]\n\t"
-      "v_exp_f32 %[x3], %[x3]\n\t"
-      "v_add_f32 %[t0], %[t0], %[x2]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q13], %[s]\n\t"
-      "ds_read_b128 %[a4], %[b2] offset:16384\n\t"
-      "v_fma_f32 %[x4], %[x4], %[c], %[t2]\n\t"
-      "v_exp_f32 %[x4], %[x4]\n\t"
-      "v_add_f32 %[t0], %[t0], %[x3]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q14], %[s]\n\t"
-      "ds_read_b128 %[a5], %[b3] offset:16384\n\t"
-      "v_fma_f32 %[x5], %[x5], %[c], %[t2]\n\t"
-      "v_exp_f32 %[x5], %[x5]\n\t"
-      "v_add_f32 %[t0], %[t0], %[x4]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q15], %[s]\n\t"
-      "ds_read_b128 %[a6], %[b0] offset:20480\n\t"
-      "v_fma_f32 %[x6], %[x6], %[c], %[t2]\n\t"
-      "v_exp_f32 %[x6], %[x6]\n\t"
-      "v_add_f32 %[t0], %[t0], %[x5]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q16], %[s]\n\t"
-      "ds_read_b128 %[a0], %[b1] offset:20480\n\t"
-      "v_fma_f32 %[x7], %[x7], %[c], %[t2]\n\t"
-      "v_exp_f32 %[x7], %[x7]\n\t"
-      "v_add_f32 %[t0], %[t0], %[x6]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q17], %[s]\n\t"
-      "ds_read_b128 %[a1], %[b2] offset:20480\n\t"
-      "v_fma_f32 %[x8], %[x8], %[c], %[t2]\n\t"
-      "v_exp_f32 %[x8], %[x8]\n\t"
-      "v_add_f32 %[t0], %[t0], %[x7]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q18], %[s]\n\t"
-      "ds_read_b128 %[a2], %[b3] offset:20480\n\t"
-      "v_fma_f32 %[x9], %[x9], %[c], %[t2]\n\t"
-      "v_exp_f32 %[x9], %[x9]\n\t"
-      "v_add_f32 %[t0], %[t0], %[x8]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q19], %[s]\n\t"
-      "ds_read_b128 %[a3], %[b0] offset:24576\n\t"
-      "v_fma_f32 %[x10], %[x10], %[c], %[t2]\n\t"
-      "v_exp_f32 %[x10], %[x10]\n\t"
-      "v_add_f32 %[t0], %[t0], %[x9]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q20], %[s]\n\t"
-      "ds_read_b128 %[a4], %[b1] offset:24576\n\t"
-      "v_fma_f32 %[x11], %[x11], %[c], %[t2]\n\t"
-      "v_exp_f32 %[x11], %[x11]\n\t"
-      "v_add_f32 %[t0], %[t0], %[x10]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q21], %[s]\n\t"
-      "ds_read_b128 %[a5], %[b2] offset:24576\n\t"
-      "v_fma_f32 %[x12], %[x12], %[c], %[t2]\n\t"
-      "v_exp_f32 %[x12], %[x12]\n\t"
-      "v_add_f32 %[t0], %[t0], %[x11]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q22], %[s]\n\t"
-      "ds_read_b128 %[a6], %[b3] offset:24576\n\t"
-      "v_fma_f32 %[x13], %[x13], %[c], %[t2]\n\t"
-      "v_exp_f32 %[x13], %[x13]\n\t"
-      "v_add_f32 %[t0], %[t0], %[x12]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q23], %[s]\n\t"
-      "ds_read_b128 %[a0], %[b0] offset:28672\n\t"
-      "v_fma_f32 %[x14], %[x14], %[c], %[t2]\n\t"
-      "v_exp_f32 %[x14], %[x14]\n\t"
-      "v_add_f32 %[t0], %[t0], %[x13]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q24], %[s]\n\t"
-      "ds_read_b128 %[a1], %[b1] offset:28672\n\t"
-      "v_fma_f32 %[x15], %[x15], %[c], %[t2]\n\t"
-      "v_exp_f32 %[x15], %[x15]\n\t"
-      "v_add_f32 %[t0], %[t0], %[x14]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q25], %[s]\n\t"
-      "ds_read_b128 %[a2], %[b2] offset:28672\n\t"
-      "v_add_f32 %[t0], %[t0], %[x15]\n\t"
-      "v_add_f32 %[ls], %[ls], %[t0]\n\t"
-      "v_cvt_pk_bf16_f32 %[x0], %[x0], %[x1]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q26], %[s]\n\t"
-      "ds_read_b128 %[a3], %[b3] offset:28672\n\t"
-      "v_dot2c_f32_bf16 %[lr], 0x3f803f80, %[x0]\n\t"
-      "v_cvt_pk_bf16_f32 %[x1], %[x2], %[x3]\n\t"
-      "v_dot2c_f32_bf16 %[lr], 0x3f803f80, %[x1]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q27], %[s]\n\t"
-      "ds_read_b128 %[a4], %[b0] offset:32768\n\t"
-      "v_cvt_pk_bf16_f32 %[x2], %[x4], %[x5]\n\t"
-      "v_dot2c_f32_bf16 %[lr], 0x3f803f80, %[x2]\n\t"
-      "v_cvt_pk_bf16_f32 %[x3], %[x6], %[x7]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q28], %[s]\n\t"
-      "ds_read_b128 %[a5], %[b1] offset:32768\n\t"
-      "v_dot2c_f32_bf16 %[lr], 0x3f803f80, %[x3]\n\t"
-      "v_cvt_pk_bf16_f32 %[x4], %[x8], %[x9]\n\t"
-      "v_dot2c_f32_bf16 %[lr], 0x3f803f80, %[x4]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a1], %[q29], %[s]\n\t"
-      "ds_read_b128 %[a6], %[b2] offset:32768\n\t"
-      "v_cvt_pk_bf16_f32 %[x5], %[x10], %[x11]\n\t"
-      "v_dot2c_f32_bf16 %[lr], 0x3f803f80, %[x5]\n\t"
-      "v_cvt_pk_bf16_f32 %[x6], %[x12], %[x13]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a2], %[q30], %[s]\n\t"
-      "ds_read_b128 %[a0], %[b3] offset:32768\n\t"
-      "v_dot2c_f32_bf16 %[lr], 0x3f803f80, %[x6]\n\t"
-      "v_cvt_pk_bf16_f32 %[x7], %[x14], %[x15]\n\t"
-      "v_dot2c_f32_bf16 %[lr], 0x3f803f80, %[x7]\n\t"
-      "s_waitcnt lgkmcnt(4)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a3], %[q31], %[s]\n\t"
-      "v_permlane32_swap_b32 %[x0], %[x2]\n\t"
-      "v_permlane32_swap_b32 %[x1], %[x3]\n\t"
-      "s_waitcnt lgkmcnt(3)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a4], %[q32], %[s]\n\t"
-      "v_permlane32_swap_b32 %[x4], %[x6]\n\t"
-      "v_permlane32_swap_b32 %[x5], %[x7]\n\t"
-      "s_waitcnt lgkmcnt(2)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a5], %[q33], %[s]\n\t"
-      "s_waitcnt lgkmcnt(1)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a6], %[q34], %[s]\n\t"
-      "s_waitcnt lgkmcnt(0)\n\t"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[a0], %[q35], %[s]\n\t"
-      "s_nop 7\n\ts_nop 7\n\ts_nop 7"
-      : [s] "=&v"(s), [a0] "=&v"(a0), [a1] "=&v"(a1), [a2] "=&v"(a2), [a3] "=&v"(a3), [a4] "=&v"(a4), [a5] "=&v"(a5),
-        [a6] "=&v"(a6), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [al] "=&v"(alpha), [x0] "+v"(x[0]), [x1] "+v"(x[1]), [x2] "+v"(x[2]),
-        [x3] "+v"(x[3]), [x4] "+v"(x[4]), [x5] "+v"(x[5]), [x6] "+v"(x[6]), [x7] "+v"(x[7]), [x8] "+v"(x[8]),
-        [x9] "+v"(x[9]), [x10] "+v"(x[10]), [x11] "+v"(x[11]), [x12] "+v"(x[12]), [x13] "+v"(x[13]),
-        [x14] "+v"(x[14]), [x15] "+v"(x[15]), [m] "+v"(S.m_used), [ls] "+v"(S.l_sum), [lr] "+v"(S.l_rnd)
-      : [b0] "v"(b0), [b1] "v"(b1), [b2] "v"(b2), [b3] "v"(b3), [c] "v"(c),
-        [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]), [q5] "v"(q[5]),
-        [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8]), [q9] "v"(q[9]), [q10] "v"(q[10]), [q11] "v"(q[11]),
-        [q12] "v"(q[12]), [q13] "v"(q[13]), [q14] "v"(q[14]), [q15] "v"(q[15]), [q16] "v"(q[16]), [q17] "v"(q[17]),
-        [q18] "v"(q[18]), [q19] "v"(q[19]), [q20] "v"(q[20]), [q21] "v"(q[21]), [q22] "v"(q[22]), [q23] "v"(q[23]),
-        [q24] "v"(q[24]), [q25] "v"(q[25]), [q26] "v"(q[26]), [q27] "v"(q[27]), [q28] "v"(q[28]), [q29] "v"(q[29]),
-        [q30] "v"(q[30]), [q31] "v"(q[31]), [q32] "v"(q[32]), [q33] "v"(q[33]), [q34] "v"(q[34]), [q35] "v"(q[35])
-      : "vcc", "memory");
+  if constexpr (H)
+    MLA_QK_SOFTMAX_ASM("v_mfma_f32_32x32x16_f16", "v_cvt_pk_f16_f32", "v_dot2c_f32_f16 %[lr], 0x3c003c00,");
+  else
+    MLA_QK_SOFTMAX_ASM("v_mfma_f32_32x32x16_bf16", "v_cvt_pk_bf16_f32", "v_dot2c_f32_bf16 %[lr], 0x3f803f80,");
 #pragma unroll
   for (int j = 0; j < 8; ++j) pp[j] = __float_as_uint(x[j]);  // P^T went into x[0..7]
   return s;
@@ -868,7 +912,7 @@ __device__ __forceinline__ f32x16 qk_softmax_tile(const bf16x8* q, uint32_t tile
 // softmax ran in the score block).  nv: the NVFP4 dequantisation of the next tile, spread
 // over the MFMAs (step m after MFMA 3m + 2, its reads two steps earlier); null for the
 // other formats, and only with all 16 blocks.
-template <int NB = kDimBlocks>
+template <int NB = kDimBlocks, bool H = false>
 __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const unsigned* pp, const int* vb,
                                              NvDequant* nv = nullptr, int db0 = 0) {
   constexpr int kAhead = 4;
@@ -894,7 +938,7 @@ __device__ __forceinline__ void output_phase(f32x16* o, uint32_t vtile, const un
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int k = 0; k < 2 * NB; ++k) {
-    o[k % NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k], (k < NB) ? pb0 : pb1, o[k % NB], 0, 0, 0);
+    o[k % NB] = mfma16<H>(va[k], (k < NB) ? pb0 : pb1, o[k % NB]);
     if (k + kAhead < 2 * NB) va[k + kAhead] = tr(k + kAhead);
     if (NB == kDimBlocks && nv && k % 3 == 2 && k / 3 < 9) {
       nv->put(k / 3);
@@ -977,7 +1021,7 @@ __device__ __forceinline__ int q_split(const uint16_t* qrow, const uint16_t* pro
     amax = max(r[0], r[1]);
   }
   // 2^sh * amax in [128, 256) (bounded so that 2^sh and 2^-sh stay normal floats)
-  const int sh = amax ? min(max(7 - ((int)(amax >> 7) - 127), -100), 100) : 0;
+  const int sh = amax ? min(max(7 - ((int)(amax >> 7) - 127), -126), 126) : 0;
   const float sc = __uint_as_float((unsigned)(sh + 127) << 23);
 #pragma unroll
   for (int k = 0; k < 9; ++k) {
@@ -1449,6 +1493,41 @@ __device__ __forceinline__ void pv64(f32x16* o, uint32_t raw, const unsigned* ph
 // (the scores and the softmax are the same in all D, so they run in each).
 // ------------------------------------------------------------------------------------
 
+// The query row (the 36 Q^T operands of this lane, bf16) as f16 operands for the NVFP4
+// path: every value times 2^sh, with sh chosen so that the row's largest magnitude (over
+// lanes l and l ^ 32, which hold the row's two halves) lands in [2^14, 2^15).  The f16
+// values are then exact for every element of at least 2^-17 after scaling, i.e. 2^-31
+// of the row's largest (f16 keeps 11 bits down to 2^-14 and 8 bits down to 2^-17).
+// Returns the row's score scale in log2 units with 2^-sh taken out (kept positive:
+// sm_scale = 0 gives the plain mean).
+__device__ __forceinline__ float q_to_f16(bf16x8* q, float score_scale) {
+  unsigned amax = 0;  // largest |bf16| bit pattern (ordered like the magnitudes)
+#pragma unroll
+  for (int k = 0; k < kKSteps; ++k) {
+    const u32x4 w = __builtin_bit_cast(u32x4, q[k]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) amax = max(amax, max(w[e] & 0x7FFFu, (w[e] >> 16) & 0x7FFFu));
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(amax, amax, false, false);
+    amax = max(r[0], r[1]);
+  }
+  const int sh = amax ? min(max(14 - ((int)(amax >> 7) - 127), -126), 126) : 0;
+  const float sc = __uint_as_float((unsigned)(sh + 127) << 23);
+#pragma unroll
+  for (int k = 0; k < kKSteps; ++k) {
+    const u32x4 w = __builtin_bit_cast(u32x4, q[k]);
+    u32x4 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f16x2 v = {(_Float16)(__uint_as_float(w[e] << 16) * sc), (_Float16)(__uint_as_float(w[e] & 0xFFFF0000u) * sc)};
+      h[e] = __builtin_bit_cast(unsigned, v);
+    }
+    q[k] = __builtin_bit_cast(bf16x8, h);
+  }
+  return fmaxf(score_scale * __uint_as_float((unsigned)(127 - sh) << 23), 1e-37f);
+}
+
 template <int FMT, bool PAGED, int D = 1>
 __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, int b, int n, int rg, int lt0,
                                           int lt1, int64_t slot) {
@@ -1466,8 +1545,11 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
   const int rows_here = min(kGroupRows, p.rows - row0);
   const int my_row = kWaveRows * rblk + lr;               // this lane's row (in the group)
   const int rc = min(row0 + my_row, p.rows - 1);          // rows past the end repeat the last row
-  const float c = fmaxf(p.score_scale, 1e-30f);           // sm_scale = 0 gives the plain mean
+  float c = p.score_scale > 0.f ? p.score_scale : 1e-30f;  // sm_scale = 0 gives the plain mean
   const int nt = lt1 - lt0;
+  // the NVFP4 cache runs on f16 operands (its dequantised values are exact in f16 and
+  // the weights keep 11 bits); the bf16 cache on bf16 operands
+  constexpr bool H = FMT == kFmtNvfp4;
 
   // Q^T operand, row rc: dims 16k + 8 (l / 32) .. + 8
   bf16x8 q[kKSteps];
@@ -1481,6 +1563,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
       q[k] = *reinterpret_cast<const bf16x8*>(src);
     }
   }
+  if constexpr (H) c = q_to_f16(q, p.score_scale);
   // query i of a request sees tokens lo .. vis - 1: vis = n - q_len + i + 1, and lo = 0, or
   // vis - window with a sliding window
   const int vis = max(n - p.q_len + rc / p.H + 1, 0);
@@ -1563,11 +1646,11 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
     }
     f32x16 s;
     if (first) {
-      s = qk_tile(q, tile_buf(i), ab);
+      s = qk_tile<H>(q, tile_buf(i), ab);
     } else {
       // scores of tile i, softmax of tile i-1 (x) -> P^T in pp and its factor
       float alpha;
-      s = qk_softmax_tile(q, tile_buf(i), ab, x, S, c, pp, alpha);
+      s = qk_softmax_tile<H>(q, tile_buf(i), ab, x, S, c, pp, alpha);
       if (__any(alpha != 1.f)) rescale<NB>(o, alpha);
     }
 #pragma unroll
@@ -1588,7 +1671,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
       if (FMT == kFmtNvfp4) dequant(i + 1);
     } else if constexpr (FMT == kFmtNvfp4) {
       NvDequant nv(raw_buf(i + 1), tile_buf(i + 1), tid);
-      output_phase(o, tile_buf(i - 1), pp, vb, &nv);
+      output_phase<kDimBlocks, true>(o, tile_buf(i - 1), pp, vb, &nv);
     } else {
       output_phase<NB>(o, tile_buf(i - 1), pp, vb, nullptr, db0);
     }
@@ -1612,9 +1695,9 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
     }
     body(0, std::true_type{});
     for (int i = 1; i < nt; ++i) body(i, std::false_type{});
-    const float alpha = softmax_tile(S, x, c, pp);  // the last tile's softmax
+    const float alpha = softmax_tile<H>(S, x, c, pp);  // the last tile's softmax
     if (__any(alpha != 1.f)) rescale<NB>(o, alpha);
-    pv_tile<NB>(o, tile_buf(nt - 1), pp, vb, db0);
+    pv_tile<NB, H>(o, tile_buf(nt - 1), pp, vb, db0);
   }
 
   // ---- epilogue: normalised partial O and its lse ----
@@ -1774,7 +1857,7 @@ __device__ __forceinline__ void run_range_fp8(const DecodeParams& p, uint32_t sm
   const uint16_t* prow = p.qpe + ((int64_t)b * p.rows + rc) * kRope;
   if constexpr (kQ8) {
     q_round_e4m3(qrow, prow, lh, qh);
-    c = fmaxf(p.score_scale, 1e-30f);  // sm_scale = 0 gives the plain mean
+    c = p.score_scale > 0.f ? p.score_scale : 1e-30f;  // sm_scale = 0 gives the plain mean
   } else {
     const int sh = q_split(qrow, prow, lh, qh, ql);
     // score scale of this row in log2 units, with the query's 2^sh taken out; kept positive
@@ -1836,7 +1919,7 @@ __device__ __forceinline__ void run_split_tiles_parallel(const DecodeParams& p, 
   const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
   const int rows = p.rows;  // at most 32: one block, shared by the four wavefronts
   const int rc = min(lr, rows - 1);
-  const float c = fmaxf(p.score_scale, 1e-30f);
+  const float c = p.score_scale > 0.f ? p.score_scale : 1e-30f;  // sm_scale = 0 gives the plain mean
   const int nt = lt1 - lt0;  // 1 .. 4
 
   bf16x8 q[kKSteps];

@@ -25,11 +25,11 @@ def test_stream_read_touches_every_word(nbytes, blocks):
     assert got == np.bitwise_xor.reduce(host)
 
 
-@pytest.mark.parametrize("kind", [ceiling.MFMA_BF16, ceiling.MFMA_FP8])
+@pytest.mark.parametrize("kind", [ceiling.MFMA_BF16, ceiling.MFMA_FP8, ceiling.MFMA_F16])
 def test_mfma_loop_runs(kind):
     say(f"ceiling mfma kind {kind}")
     out = torch.full((8 * 4,), float("nan"), dtype=torch.float32, device="cuda:0")
     flops = ceiling.mfma(kind, 10, out, 8)
     torch.cuda.synchronize()
-    assert flops == 8 * 4 * 10 * 4 * (32768 if kind == ceiling.MFMA_BF16 else 131072)
+    assert flops == 8 * 4 * 10 * 4 * (131072 if kind == ceiling.MFMA_FP8 else 32768)
     assert torch.isfinite(out).all()

@@ -344,15 +344,17 @@ def _scale_bf16(bits, k):
     return gen.to_bf16_bits(gen.bf16_bits_to_f32(bits) * np.float32(2.0 ** k))
 
 
-@pytest.mark.parametrize("qexp,scale_exp", [(12, -12), (-24, 24), (2, 0), (0, 0)])
-def test_paged_fp8_query_magnitudes_and_peaked_rows(qexp, scale_exp):
+@pytest.mark.parametrize("fmt", [gen.FMT_FP8, gen.FMT_NVFP4, gen.FMT_BF16])
+@pytest.mark.parametrize("qexp,scale_exp", [(12, -12), (-24, 24), (110, -110), (2, 0), (0, 0)])
+def test_paged_query_magnitudes_and_peaked_rows(fmt, qexp, scale_exp):
     """The FP8 cache path splits each query row into two E4M3 operands after a power-of-two
-    row scale, and the softmax weights likewise: query rows far from unit magnitude (the
-    score scale compensates, so the scores are unchanged), all-zero rows, and strongly
-    peaked rows (query x 4: most weights fall below E4M3's subnormal range) stay within
-    the FP8 tolerance of the oracle."""
-    say(f"paged fp8 query x 2^{qexp}, sm_scale x 2^{scale_exp}")
-    w = gen.make_paged(B=3, H=128, q_len=1, lo=200, hi=900, page_size=64, fmt=gen.FMT_FP8, seed=65)
+    row scale, and the softmax weights likewise; the NVFP4 path scales each query row by a
+    power of two into f16: query rows far from unit magnitude (the score scale compensates,
+    so the scores are unchanged; 2^110 is near the top of the bf16 range), all-zero rows,
+    and strongly peaked rows (query x 4: most weights fall below E4M3's subnormal range)
+    stay within the tolerance of the oracle, as they do on the bf16 cache."""
+    say(f"paged {gen.FMT_NAMES[fmt]} query x 2^{qexp}, sm_scale x 2^{scale_exp}")
+    w = gen.make_paged(B=3, H=128, q_len=1, lo=200, hi=900, page_size=64, fmt=fmt, seed=65)
     w.q = _scale_bf16(w.q, qexp)
     w.qpe = _scale_bf16(w.qpe, qexp)
     w.q[:, :, :16] = 0
@@ -360,7 +362,7 @@ def test_paged_fp8_query_magnitudes_and_peaked_rows(qexp, scale_exp):
     w.sm_scale = w.sm_scale * 2.0 ** scale_exp
     ro, rl = _paged_ref(w)
     o, lse = _paged_run(w)
-    check_o("o", o, ro, TOL_O_QUANT)
+    check_o("o", o, ro, _tol_o(fmt))
     check("lse", lse, rl, TOL_LSE)
 
 
