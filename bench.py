@@ -223,13 +223,28 @@ def settle(step, torch, ms: float):
 
 
 def timed_steps(torch, steps, decode, combine, flush_buf=None):
-    """K steps with events around each launch; returns (wall_s, decode_ms[], combine_ms[])."""
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    """K steps with events around each launch; returns (wall_s, decode_ms[], combine_ms[]).
+    Without a flush, consecutive steps share their boundary event (two event records per
+    step: each record between two launches adds a few microseconds to the stream); with
+    one, each step has its own three, so the flush stays outside the timed launches."""
+    E = lambda: torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    if flush_buf is None:
+        ev = [E() for _ in range(2 * steps + 1)]
+        ev[0].record()
+        for k in range(steps):
+            decode()
+            ev[2 * k + 1].record()
+            combine()
+            ev[2 * k + 2].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return (wall, [ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(steps)],
+                [ev[2 * k + 1].elapsed_time(ev[2 * k + 2]) for k in range(steps)])
+    ev = [[E() for _ in range(3)] for _ in range(steps)]
     for k in range(steps):
-        if flush_buf is not None:
-            flush_buf[1].copy_(flush_buf[0].max())  # reads the whole buffer
+        flush_buf[1].copy_(flush_buf[0].max())  # reads the whole buffer
         ev[k][0].record()
         decode()
         ev[k][1].record()
