@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI host code (mla_api.cpp) and the gfx950 kernels
-// (mla_kernels.hip: decode and combine; mla_append.hip: cache append).  Not installed; the public interface is include/mla_decode.h.
+// (mla_kernels.hip: decode and combine; mla_append.hip: cache append).  Not installed;
+// the public interface is include/mla_decode.h.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -23,8 +23,8 @@
 // the scores of tile i, with the softmax of tile i-1 (whose scores stayed in registers)
 // spread between the score MFMAs, so the vector work issues while the matrix core is
 // busy; then the output product of tile i-1, with NVFP4's dequantisation of tile i+1
-// spread between its MFMAs in nine steps; then one barrier.  The first tile's softmax and the last tile's output product come
-// after the loop.
+// spread between its MFMAs in nine steps; then one barrier.  The first tile's softmax
+// and the last tile's output product come after the loop.
 //
 // FP8 cache (run_range_fp8): 64-token tiles, none converted to bf16.  The bf16 query of
 // each row is split exactly into two E4M3 operands (hi + lo, after a power-of-two row
@@ -1520,7 +1520,8 @@ __device__ __forceinline__ float q_to_f16(bf16x8* q, float score_scale) {
     u32x4 h;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const f16x2 v = {(_Float16)(__uint_as_float(w[e] << 16) * sc), (_Float16)(__uint_as_float(w[e] & 0xFFFF0000u) * sc)};
+      const f16x2 v = {(_Float16)(__uint_as_float(w[e] << 16) * sc),
+                       (_Float16)(__uint_as_float(w[e] & 0xFFFF0000u) * sc)};
       h[e] = __builtin_bit_cast(unsigned, v);
     }
     q[k] = __builtin_bit_cast(bf16x8, h);
