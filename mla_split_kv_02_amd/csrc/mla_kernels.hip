@@ -203,6 +203,15 @@ __device__ __forceinline__ LDS_AS T* at(uint32_t a) { return (LDS_AS T*)(uintptr
 __device__ __forceinline__ void dma16_s(const uint8_t* base, uint32_t voff, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
 }
+// dma16_s of base + OFF: the instruction's immediate offset moves the LDS destination by
+// the same amount as the global source, so M0 takes lds - OFF.  Loads that share one base
+// then need no 64-bit address arithmetic of their own.
+template <int OFF>
+__device__ __forceinline__ void dma16_o(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  static_assert(OFF >= 0 && OFF < 4096, "immediate offset range");
+  asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2" ::"v"(voff), "s"(base), "i"(OFF), "{m0}"(lds - OFF)
+               : "memory");
+}
 __device__ __forceinline__ void dma4_s(const uint8_t* base, uint32_t voff, uint32_t lds) {
   asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
 }
@@ -266,14 +275,28 @@ __device__ __forceinline__ void load_bf16_tile(const Src& S, int tb, const uint8
   if (PAGED) {
     const int rip = tb & (p.page_size - 1);
     const uint32_t voff = (uint32_t)((rip + tok - tb) * (2 * kRow) + cpos);
-#pragma unroll
-    for (int m = 0; m < 9; ++m) dma16_s(pg + 128 * m, voff, lds + kGroupBytes * m);
+    dma16_o<0>(pg, voff, lds);
+    dma16_o<128>(pg, voff, lds + kGroupBytes);
+    dma16_o<256>(pg, voff, lds + kGroupBytes * 2);
+    dma16_o<384>(pg, voff, lds + kGroupBytes * 3);
+    dma16_o<512>(pg, voff, lds + kGroupBytes * 4);
+    dma16_o<640>(pg, voff, lds + kGroupBytes * 5);
+    dma16_o<768>(pg, voff, lds + kGroupBytes * 6);
+    dma16_o<896>(pg, voff, lds + kGroupBytes * 7);
+    dma16_o<1024>(pg, voff, lds + kGroupBytes * 8);
   } else {
     const int64_t t0 = (int64_t)S.b * p.S + tb;
     const uint8_t* kv = reinterpret_cast<const uint8_t*>(p.kv + t0 * kLatent);
     const uint8_t* kpe = reinterpret_cast<const uint8_t*>(p.kpe + t0 * kRope);
-#pragma unroll
-    for (int m = 0; m < 8; ++m) dma16_s(kv + 128 * m, (uint32_t)((tok - tb) * (2 * kLatent) + cpos), lds + kGroupBytes * m);
+    const uint32_t kvoff = (uint32_t)((tok - tb) * (2 * kLatent) + cpos);
+    dma16_o<0>(kv, kvoff, lds);
+    dma16_o<128>(kv, kvoff, lds + kGroupBytes);
+    dma16_o<256>(kv, kvoff, lds + kGroupBytes * 2);
+    dma16_o<384>(kv, kvoff, lds + kGroupBytes * 3);
+    dma16_o<512>(kv, kvoff, lds + kGroupBytes * 4);
+    dma16_o<640>(kv, kvoff, lds + kGroupBytes * 5);
+    dma16_o<768>(kv, kvoff, lds + kGroupBytes * 6);
+    dma16_o<896>(kv, kvoff, lds + kGroupBytes * 7);
     dma16_s(kpe, (uint32_t)((tok - tb) * (2 * kRope) + cpos), lds + kGroupBytes * 8);
   }
 }
@@ -300,9 +323,11 @@ __device__ __forceinline__ void load_fp8_raw(const Src& S, int tb, const uint8_t
   // 18 instructions: four from every wavefront, a fifth from wavefronts 0 and 1 (a
   // wavefront-uniform branch, so the condition stays in scalar registers)
   static_assert(kFp8Loads > 16 && kFp8Loads <= 20, "four or five loads per wavefront");
-#pragma unroll
-  for (int m = 0; m < 4; ++m) dma16_s(pg + 128 * m, voff, st + 1024 * (4 * m + wave));
-  if (wave < kFp8Loads - 16) dma16_s(pg + 512, voff, st + 1024 * (16 + wave));
+  dma16_o<0>(pg, voff, st + 1024 * wave);
+  dma16_o<128>(pg, voff, st + 1024 * (4 + wave));
+  dma16_o<256>(pg, voff, st + 1024 * (8 + wave));
+  dma16_o<384>(pg, voff, st + 1024 * (12 + wave));
+  if (wave < kFp8Loads - 16) dma16_o<512>(pg, voff, st + 1024 * (16 + wave));
 }
 
 // NVFP4 rows, raw.  Data: chunk c (32 codes) of row r at 1024 (c / 2) + 32 r + 16 (c % 2);
@@ -325,9 +350,9 @@ __device__ __forceinline__ void load_nvfp4_raw(const Src& S, int tb, const uint8
   // stay in scalar registers): m = 0, 1 data; m = 2 data 8 (wavefront 0) or scales 0..2;
   // m = 3 scales 3, 4 (wavefronts 0, 1)
   static_assert(kNvDataLoads == 9 && kNvScaleLoads == 5, "load split below");
-#pragma unroll
-  for (int m = 0; m < 2; ++m) dma16_s(pg + 32 * (4 * m + wave), dvoff, st + 1024 * (4 * m + wave));
-  if (wave == 0) dma16_s(pg + 32 * 8, dvoff, st + 1024 * 8);
+  dma16_o<0>(pg + 32 * wave, dvoff, st + 1024 * wave);
+  dma16_o<128>(pg + 32 * wave, dvoff, st + 1024 * (4 + wave));
+  if (wave == 0) dma16_o<256>(pg, dvoff, st + 1024 * 8);
   else scales(wave - 1);
   if (wave < 2) scales(3 + wave);
 }
