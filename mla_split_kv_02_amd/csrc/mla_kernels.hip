@@ -93,10 +93,10 @@ constexpr int kNvRawBytes = kNvRawData + 256 * kNvScaleLoads;     // 10496
 constexpr float kTau = 8.0f;   // lazy rescale threshold (log2 units)
 constexpr float kLn2 = 0.69314718055994531f;
 
-// Buffers and load distance per cache format.  Tile i sits in bf16 buffer i % kTiles
-// (kStride bytes apart); raw tile i (FP8 / NVFP4) in staging buffer i % kRaw.  In
-// iteration i the loads of tile i + kAhead are issued.  The FP8 formats (split loop) have
-// no bf16 tiles at all.
+// Buffers and load distance per cache format.  Tile i sits in 16-bit buffer i % kTiles
+// (kStride bytes apart; bf16, or f16 dequantised from NVFP4); raw tile i (FP8 / NVFP4)
+// in staging buffer i % kRaw.  In iteration i the loads of tile i + kAhead are issued.
+// The FP8 formats (split loop) have no 16-bit tiles at all.
 template <int FMT> struct Pipe;
 template <> struct Pipe<kFmtBf16> {
   static constexpr int kTiles = 4, kStride = kTileBytes, kRaw = 0, kRawBytes = 0, kAhead = 2, kLoads = kBf16Loads;
@@ -121,7 +121,7 @@ static_assert(smem_bytes<kFmtBf16>() <= 160 * 1024 && smem_bytes<kFmtFp8>() <= 1
                   smem_bytes<kFmtNvfp4>() <= 160 * 1024 && smem_bytes<kFmtFp8Q>() <= 160 * 1024,
               "LDS budget");
 
-// Byte offset of 16-byte chunk c (0..71) of token row r in a bf16 tile.  The tile is
+// Byte offset of 16-byte chunk c (0..71) of token row r in a 16-bit tile.  The tile is
 // nine 4 KiB groups, one per 8 chunks (128 bytes) of every row: group c / 8 holds
 // [32 rows][8 chunks], and inside a row the chunk position is XOR-swizzled with swz(r).
 // Every global->LDS load instruction then fills one kilobyte of one group (8 rows), so
@@ -364,7 +364,7 @@ __device__ __forceinline__ void load_nvfp4_raw(const Src& S, int tb, const uint8
 // only the exponent of its scale operand) as packed f16, and one packed f16 multiply by
 // M finishes the product.  Every product has at most 6 significant bits and lies in
 // [2^-10, 1536] (or is 0), so each step is exact in f16; a NaN scale gives NaN.
-// The work is cut into nine steps, one per 4 KiB group m of the bf16 tile, so that the
+// The work is cut into nine steps, one per 4 KiB group m of the f16 tile, so that the
 // output phase can spread them between its MFMAs: read(m) fetches the step's code dword
 // and scale byte, put(m) converts and writes them.
 struct NvDequant {
@@ -1651,7 +1651,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, uint32_t smem, 
     else load_nvfp4_raw(src, tb, pg, raw_buf(i), wave, lane);
   };
   int e_next = 0;  // block-table entry of tile i + kAhead, read one tile early
-  auto dequant = [&](int i) {  // raw tile i -> its bf16 buffer
+  auto dequant = [&](int i) {  // raw tile i -> its f16 buffer
     if (FMT == kFmtNvfp4) dequant_nvfp4(raw_buf(i), tile_buf(i), tid);
   };
 
@@ -2112,7 +2112,7 @@ void decode_contig_kernel(const DecodeParams p) {
 // time against tiles and segments over the 256 ranges of the B=64, H=128 FP8 workload):
 // about 50700 cycles (24-26 us) per segment against about 6550 cycles per 64-token tile,
 // i.e. 8 tiles; the 32-token figure (17 us against 1.6 us per tile) is from the
-// bf16-dequantising loop.
+// 32-token loop with NVFP4 dequantisation.
 // An empty range can only sit where one request ends and the next begins, so every
 // range between seg_first[b] and seg_last[b] holds tiles of b exactly when its cost
 // interval is not empty (the combine relies on this).
