@@ -327,6 +327,32 @@ def test_paged_nvfp4_every_code_and_scale():
     check("lse", lse, rl, TOL_LSE)
 
 
+def test_paged_nvfp4_large_scales():
+    """Every E2M1 code under scales drawn from every finite E4M3 code of either sign, up to
+    448 (values up to 2688, the top of the NVFP4 range, dequantised exactly to f16), with a
+    query scaled by 2^-8 so that the scores stay moderate."""
+    say("paged nvfp4 large scales")
+    w = gen.make_paged(B=2, H=32, q_len=1, lo=300, hi=300, page_size=64, fmt=gen.FMT_NVFP4, seed=66)
+    rng = np.random.default_rng(3)
+    pages = w.cache.reshape(w.num_pages, w.page_stride)
+    sc = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)  # no NaN codes
+    for pg in range(w.num_pages - 1):  # the last page is the poison page
+        pages[pg, :64 * 288] = rng.integers(0, 256, 64 * 288, dtype=np.uint8)
+        pages[pg, 64 * 288:64 * 324] = rng.choice(sc, 64 * 36)
+    w.q = _scale_bf16(w.q, -8)
+    w.qpe = _scale_bf16(w.qpe, -8)
+    ro, rl = _paged_ref(w)
+    o, lse = _paged_run(w)
+    # O's error scales with the latent values: compare in units of the largest one
+    vmax = max(float(np.abs(oracle.gather_request(w.cache, w.fmt, w.kv_scale, w.page_size, w.page_stride,
+                                                  w.block_tables[b], int(w.seq_lens[b]))[:, :512]).max())
+               for b in range(w.B))
+    say(f"  largest latent value {vmax:g}")
+    assert vmax > 1000
+    check_o("o / max|latent|", o / vmax, ro / vmax, TOL_O_QUANT)
+    check("lse", lse, rl, TOL_LSE)
+
+
 def test_paged_fp8_b64_h128_full_size():
     """The benchmark workload at full size and in its benchmark launch configuration:
     every one of its 64 requests against the oracle."""
