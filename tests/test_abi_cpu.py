@@ -46,9 +46,11 @@ def test_ceiling_library_exports_its_header():
     for name in decl:
         assert hasattr(L, name), name
     assert L.mla_ceiling_mfma_flops(0) == 32768.0 and L.mla_ceiling_mfma_flops(1) == 131072.0
+    assert L.mla_ceiling_mfma_flops(2) == 32768.0 and L.mla_ceiling_mfma_flops(3) == 0.0
     # invalid arguments are refused before any launch
     assert L.mla_ceiling_stream_read(None, 16, None, 1, None) == -1
     assert L.mla_ceiling_mfma(7, 1, ctypes.c_void_p(F), 1, None) == -1
+    assert L.mla_ceiling_mfma(3, 1, ctypes.c_void_p(F), 1, None) == -1
 
 
 def test_status_strings():
