@@ -52,7 +52,6 @@
 // log-sum-exp reduce (TileGym page, forward: splitk_reduce), plus the row's sink logit
 // when there is one.
 
-#include "mla_fp8.h"
 #include "mla_internal.h"
 
 #include <math.h>
@@ -1072,22 +1071,27 @@ __device__ __forceinline__ int q_split(const uint16_t* qrow, const uint16_t* pro
 }
 
 // FP8 query (cache format 3): the query row rounded to E4M3 once per segment, in the
-// operand layout of qk_tile_f8 (K-step k: dims 64k + 32h .. + 31 as bytes 0..31), with the
-// same encoder as the cache append (nearest, ties to even, saturating).
+// operand layout of qk_tile_f8 (K-step k: dims 64k + 32h .. + 31 as bytes 0..31): each
+// value saturated at +-448 (a NaN to 448 with its sign), then the hardware conversion
+// (nearest, ties to even).  For every bf16 input this gives the codes of the cache
+// append's encoder (e4m3_code): a probe compared all 65536 patterns.
 __device__ __forceinline__ void q_round_e4m3(const uint16_t* qrow, const uint16_t* prow, int lh, i32x8* q8) {
+  auto sat = [](float x) { return copysignf(fminf(fabsf(x), 448.0f), x); };
 #pragma unroll
   for (int k = 0; k < 9; ++k) {
     const int d = 64 * k + 32 * lh;
     const u32x4* src = reinterpret_cast<const u32x4*>((d < kLatent) ? qrow + d : prow + (d - kLatent));
-    i32x8 v = {};
+    i32x8 v;
 #pragma unroll
     for (int w4 = 0; w4 < 4; ++w4) {
       const u32x4 raw = src[w4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {  // dims 8 w4 + 2e, 8 w4 + 2e + 1
-        const unsigned lo = e4m3_code(__uint_as_float(raw[e] << 16));
-        const unsigned hi = e4m3_code(__uint_as_float(raw[e] & 0xFFFF0000u));
-        v[2 * w4 + (e >> 1)] |= (int)((lo | (hi << 8)) << (16 * (e & 1)));
+      for (int e = 0; e < 4; e += 2) {  // dims 8 w4 + 2e .. + 3 -> dword 2 w4 + e / 2
+        unsigned c = e4m3_pair<false>(0u, sat(__uint_as_float(raw[e] << 16)),
+                                      sat(__uint_as_float(raw[e] & 0xFFFF0000u)));
+        c = e4m3_pair<true>(c, sat(__uint_as_float(raw[e + 1] << 16)),
+                            sat(__uint_as_float(raw[e + 1] & 0xFFFF0000u)));
+        v[2 * w4 + e / 2] = (int)c;
       }
     }
     q8[k] = v;
