@@ -85,10 +85,11 @@ def algorithmic_counts(w):
     return flops, kv + qbytes + obytes + tbytes, kv
 
 
-def traffic_from_profiles(workload: str, src_hash: str, kernel: str = "decode_paged"):
+def traffic_from_profiles(workload: str, src_hash: str, kernel: str = "decode_paged", variant: str | None = None):
     """HBM bytes per decode launch (FETCH_SIZE and WRITE_SIZE, each scaled by what the
     counter reads for a copy kernel of known size) from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
+    summary, if it was taken on the current kernel source; else None.  variant: the name
+    of another decode kernel the same profiled runs launched (the benchmark's variants)."""
     path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.counters.json")
     if not os.path.exists(path):
         return None
@@ -96,6 +97,8 @@ def traffic_from_profiles(workload: str, src_hash: str, kernel: str = "decode_pa
         d = json.load(f)
     if d.get("kernel_source_sha") != src_hash:
         return None
+    if variant is not None:
+        return d.get("variant_hbm_bytes_per_launch", {}).get(variant)
     return d.get("hbm_bytes_per_launch")
 
 
@@ -381,7 +384,10 @@ def time_fp8_query_variant(mla, torch, np, w, q, qpe, cache, bt, sl, G, args, fl
     log(f"[bench] fp8-query variant: {ms_step:.4f} ms/step, decode {dec:.4f} ms")
     return {"kv_format": "fp8_e4m3, query rounded to e4m3", "arithmetic": ARITHMETIC[3],
             "ms_per_step": round(ms_step, 5), "value": round(flops / (ms_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
-            "decode_ms": round(dec, 5), "roofline": roofline(flops, nbytes, dec, "fp8", ceilings, None)}
+            "decode_ms": round(dec, 5),
+            "roofline": roofline(flops, nbytes, dec, "fp8", ceilings,
+                                 traffic_from_profiles(args.workload, kernel_source_hash(), "decode_paged",
+                                                       f"decode_paged_kernel<{mla.MLA_KV_FP8_E4M3_QFP8}>"))}
 
 
 def time_fixed_splits(mla, torch, np, w, q, qpe, cache, bt, sl, args, flops, nbytes, ceilings, flush_buf):

@@ -65,3 +65,17 @@ def test_traffic_only_for_the_profiled_sources():
         assert t is None
     assert b.traffic_from_profiles("paged_fp8_b64_h128_s1k_32k", "0" * 16) is None
     assert b.traffic_from_profiles("no_such_workload", sha) is None
+
+
+def test_variant_traffic_from_the_same_profile():
+    """The benchmark's variants (FP8-query decode) take their traffic from the same
+    profiled runs, by kernel name, under the same source check."""
+    b = _bench()
+    path = os.path.join(ROOT, "profiles", "decode_paged.paged_fp8_b64_h128_s1k_32k.counters.json")
+    d = json.load(open(path))
+    sha = d["kernel_source_sha"]
+    t = b.traffic_from_profiles("paged_fp8_b64_h128_s1k_32k", sha, "decode_paged", "decode_paged_kernel<3>")
+    assert t == d["variant_hbm_bytes_per_launch"]["decode_paged_kernel<3>"] and t > 0
+    assert b.traffic_from_profiles("paged_fp8_b64_h128_s1k_32k", sha, "decode_paged", "no_such_kernel") is None
+    assert b.traffic_from_profiles("paged_fp8_b64_h128_s1k_32k", "0" * 16, "decode_paged",
+                                   "decode_paged_kernel<3>") is None
